@@ -1,0 +1,434 @@
+"""Seeded synthetic decode batches and the host-side block bookkeeping.
+
+This module builds inputs only: block tables popped from a shuffled free
+list, context lengths, query / cache contents and the new token's K/V with
+its slot. It holds none of the attention arithmetic, so the HIP path and the
+CPU oracle can both be fed from it.
+
+Host bookkeeping follows the pages:
+
+* Free-list allocator: the free list starts as the (shuffled) block ids;
+  allocation pops from the front, freeing appends to the back, and a request
+  that needs more blocks than are free raises an out-of-memory error
+  ("vLLM PagedAttention深度解析与工程实践" §3.2 Block Manager 的核心流程).
+* Per-sequence table growth: a new token takes a fresh block exactly when
+  the token count is a multiple of the block size (lqnn.cn/news/170268
+  §2.2, BlockTable.append_token).
+* Shared prefix blocks are referenced by several tables at once and carry a
+  reference count (lqnn.cn/news/170268 §3.2; "vLLM 核心：PagedAttention 与
+  Continuous Batching" §3 Prefix Caching).
+
+Randomness: context lengths and the free-list shuffle come from
+numpy.random.default_rng(seed) (PCG64), in that order. Element data q, K, V
+and the new token's K/V ~ N(0, 1) are drawn in float32 from independent PCG64
+streams keyed SeedSequence(seed, spawn_key=(stream, chunk)) - one stream per
+tensor, one chunk per 256 cache blocks in allocation order - so generation
+can run on several threads and still give the same bits; values are rounded
+to nearest-even into fp16 / bf16. bf16 arrays are carried as uint16 bit
+patterns.
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+import math
+import os
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Named workloads
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str            # "f16" or "bf16"
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    lens: str             # length-distribution recipe, see draw_context_lens
+    partition_size: int = 512
+    shared_prefix_tokens: int = 0
+    long_seqs: int = 0        # extra sequences of long_len tokens
+    long_len: int = 0
+    description: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", 4, 8, 8, 64, "f16", 16, 64, 8, "uniform:1:128",
+        description="4 seqs, 8 MHA heads, head_dim 64, fp16, block 16, "
+                    "64 permuted physical blocks, context U[1,128]"),
+    "llama13b": Workload(
+        "llama13b", 32, 40, 40, 128, "f16", 16, 8192, 128, "uniform:32:2048",
+        description="LLaMA-13B-like decode: 32 seqs, 40 heads, head_dim 128, "
+                    "fp16, block 16, 8192-block shuffled free list, "
+                    "context U[32,2048]"),
+    "llama7b": Workload(
+        "llama7b", 64, 32, 32, 128, "bf16", 16, 16384, 256,
+        "lognormal:512:1.0:16:4096",
+        description="LLaMA-7B-like decode: 64 seqs, 32 heads, head_dim 128, "
+                    "bf16, block 16, context lognormal(median 512, sigma 1) "
+                    "clipped to [16,4096], new K/V scattered by slot"),
+    "gqa_long": Workload(
+        "gqa_long", 128, 64, 8, 128, "bf16", 16, 65536, 512,
+        "uniform:1024:8192", partition_size=512,
+        description="GQA long context: 128 seqs, 64 q / 8 kv heads, head_dim "
+                    "128, bf16, block 16, context U[1024,8192], split-K 512"),
+    "shared_prefix": Workload(
+        "shared_prefix", 256, 32, 32, 128, "f16", 32, 16384, 1024,
+        "uniform:1:1024", shared_prefix_tokens=2048, long_seqs=4,
+        long_len=32768,
+        description="shared prefix: 256 seqs share a 2048-token prefix "
+                    "(same physical blocks) then private suffixes U[1,1024]; "
+                    "plus 4 seqs of 32768 tokens; 32 heads, head_dim 128, "
+                    "fp16, block 32"),
+}
+
+WORKLOAD_ORDER = ["tiny", "llama13b", "llama7b", "gqa_long", "shared_prefix"]
+
+# ---------------------------------------------------------------------------
+# Block bookkeeping
+# ---------------------------------------------------------------------------
+
+
+class OutOfBlocks(RuntimeError):
+    """The free list cannot satisfy an allocation (preemption territory)."""
+
+
+class BlockManager:
+    """Free-list allocator: pop from the front, return to the back."""
+
+    def __init__(self, free_blocks, block_size):
+        self.free_blocks = list(int(b) for b in free_blocks)
+        self.block_size = int(block_size)
+        self.allocated = {}   # seq id -> list of physical blocks
+        self.refcount = {}    # physical block -> number of tables using it
+
+    def _pop(self):
+        if not self.free_blocks:
+            raise OutOfBlocks("no free KV block left")
+        b = self.free_blocks.pop(0)
+        self.refcount[b] = 1
+        return b
+
+    def allocate(self, seq_id, num_tokens):
+        """Grow seq_id's table until it holds num_tokens tokens."""
+        have = len(self.allocated.get(seq_id, [])) * self.block_size
+        if have >= num_tokens:
+            return
+        need = -(-(num_tokens - have) // self.block_size)
+        if len(self.free_blocks) < need:
+            raise OutOfBlocks("need %d blocks, %d free" % (need, len(self.free_blocks)))
+        for _ in range(need):
+            self.allocated.setdefault(seq_id, []).append(self._pop())
+
+    def share(self, seq_id, blocks):
+        """Point seq_id's table at existing blocks (shared, read-only)."""
+        for b in blocks:
+            self.refcount[b] = self.refcount.get(b, 0) + 1
+            self.allocated.setdefault(seq_id, []).append(int(b))
+
+    def free(self, seq_id):
+        for b in self.allocated.pop(seq_id, []):
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                del self.refcount[b]
+                self.free_blocks.append(b)
+
+
+class SequenceTable:
+    """One sequence's table that grows by one token at a time."""
+
+    def __init__(self, block_size):
+        self.block_size = int(block_size)
+        self.physical_blocks = []
+        self.num_tokens = 0
+
+    def append_token(self, allocate_block):
+        """Take a new block when the current ones are full; return the slot."""
+        if self.num_tokens % self.block_size == 0:
+            self.physical_blocks.append(int(allocate_block()))
+        blk = self.physical_blocks[self.num_tokens // self.block_size]
+        slot = blk * self.block_size + self.num_tokens % self.block_size
+        self.num_tokens += 1
+        return slot
+
+
+def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype_bytes):
+    """K and V bytes one token occupies: 2 · layers · kv_heads · head_dim · bytes."""
+    return 2 * num_layers * num_kv_heads * head_dim * dtype_bytes
+
+
+def reservation_utilisation(used_tokens, reserved_per_request):
+    """Fraction of a max-length contiguous reservation that holds tokens."""
+    return sum(used_tokens) / float(reserved_per_request * len(used_tokens))
+
+
+# ---------------------------------------------------------------------------
+# Element encodings
+# ---------------------------------------------------------------------------
+
+F16_NAN = np.uint16(0x7E00)
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x):
+    """Round-to-nearest-even fp32 -> bf16, returned as uint16 bits (finite x)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def encode(x, dtype):
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def element_numpy_dtype(dtype):
+    return {"f16": np.float16, "bf16": np.uint16}[dtype]
+
+
+def nan_bits(dtype):
+    return {"f16": F16_NAN, "bf16": BF16_NAN}[dtype]
+
+
+# ---------------------------------------------------------------------------
+# Batch construction
+# ---------------------------------------------------------------------------
+
+
+def draw_context_lens(rng, recipe, n):
+    kind, *args = recipe.split(":")
+    if kind == "uniform":
+        lo, hi = int(args[0]), int(args[1])
+        return rng.integers(lo, hi, endpoint=True, size=n).astype(np.int64)
+    if kind == "lognormal":
+        median, sigma, lo, hi = float(args[0]), float(args[1]), int(args[2]), int(args[3])
+        z = rng.standard_normal(n)
+        return np.clip(np.floor(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
+    if kind == "fixed":
+        return np.full(n, int(args[0]), dtype=np.int64)
+    raise ValueError(recipe)
+
+
+@dataclass
+class Batch:
+    """One decode step's inputs. Caches hold the history (positions < L-1);
+    the new token (position L-1) arrives as new_key/new_value + slot_mapping."""
+    workload: Workload
+    query: np.ndarray          # [B, Hq, D]
+    key_cache: np.ndarray      # [NB, BS, Hkv, D]
+    value_cache: np.ndarray    # [NB, BS, Hkv, D]
+    block_tables: np.ndarray   # int32 [B, MB], -1 past each table's end
+    context_lens: np.ndarray   # int32 [B]
+    new_key: np.ndarray        # [B, Hkv, D]
+    new_value: np.ndarray      # [B, Hkv, D]
+    slot_mapping: np.ndarray   # int64 [B]
+    scale: float
+    allocated_blocks: np.ndarray  # int64, every block some table uses (unique)
+    shared_blocks: np.ndarray     # int64, blocks referenced by several tables
+    refcount: dict = field(default_factory=dict)
+
+    @property
+    def dtype(self):
+        return self.workload.dtype
+
+
+def _bits(a):
+    return a.view(np.uint16)
+
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_NEW_K, STREAM_NEW_V = range(5)
+BLOCKS_PER_CHUNK = 256
+
+
+def _normal(seed, stream, chunk, shape):
+    ss = np.random.SeedSequence(seed, spawn_key=(stream, chunk))
+    return np.random.Generator(np.random.PCG64(ss)).standard_normal(shape, dtype=np.float32)
+
+
+def _workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _fill_blocks(seed, stream, cache_bits, blocks, dtype):
+    """Draw N(0,1) contents for whole blocks, chunk by chunk in parallel."""
+    shape = cache_bits.shape[1:]
+    starts = list(range(0, len(blocks), BLOCKS_PER_CHUNK))
+
+    def one(c):
+        ids = blocks[starts[c]:starts[c] + BLOCKS_PER_CHUNK]
+        vals = _normal(seed, stream, c, (len(ids),) + shape)
+        cache_bits[ids] = _bits(encode(vals, dtype))
+
+    if len(starts) <= 1:
+        for c in range(len(starts)):
+            one(c)
+        return
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(starts))))
+
+
+def make_batch(workload, seed=0, lens=None, poison="nan", unallocated="zero"):
+    """Build the seeded batch for a Workload.
+
+    lens overrides the drawn context lengths (shared-prefix workloads take
+    suffix lengths here). poison fills the new token's slot and the idle tail
+    of each last block ("nan" or "zero"); unallocated blocks are "zero" or
+    "nan".
+    """
+    w = workload
+    rng = np.random.default_rng(seed)
+    B = w.num_seqs + w.long_seqs
+    BS = w.block_size
+    # -- context lengths (each includes the new token) ---------------------
+    if lens is None:
+        drawn = draw_context_lens(rng, w.lens, w.num_seqs)
+    else:
+        drawn = np.asarray(lens, dtype=np.int64)
+        if len(drawn) != w.num_seqs:
+            raise ValueError("expected %d lengths" % w.num_seqs)
+    if w.shared_prefix_tokens:
+        ctx = np.concatenate([w.shared_prefix_tokens + drawn,
+                              np.full(w.long_seqs, w.long_len, dtype=np.int64)])
+    else:
+        ctx = np.concatenate([drawn, np.full(w.long_seqs, w.long_len, dtype=np.int64)])
+    if ctx.max(initial=0) > w.max_blocks_per_seq * BS:
+        raise ValueError("context longer than max_blocks_per_seq * block_size")
+    # -- block tables --------------------------------------------------------
+    free = rng.permutation(w.num_blocks)
+    mgr = BlockManager(free, BS)
+    shared = []
+    if w.shared_prefix_tokens:
+        if w.shared_prefix_tokens % BS:
+            raise ValueError("shared prefix must be whole blocks")
+        mgr.allocate("prefix", w.shared_prefix_tokens)
+        shared = list(mgr.allocated["prefix"])
+    tables = []
+    for i in range(B):
+        t = SequenceTable(BS)
+        hist = int(ctx[i]) - 1 if ctx[i] > 0 else 0
+        if shared:
+            mgr.share(i, shared)
+            t.physical_blocks = list(shared)
+            t.num_tokens = w.shared_prefix_tokens
+        mgr.allocate(i, hist)
+        t.physical_blocks = list(mgr.allocated.get(i, []))
+        t.num_tokens = hist
+        tables.append(t)
+    if shared:
+        mgr.free("prefix")  # the prefix stays alive through the sequences' references
+    slots = np.full(B, -1, dtype=np.int64)
+    for i in range(B):
+        if ctx[i] > 0:
+            slots[i] = tables[i].append_token(lambda i=i: _grow(mgr, i))
+    bt = np.full((B, w.max_blocks_per_seq), -1, dtype=np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t.physical_blocks)] = t.physical_blocks
+    # -- element data (built as uint16 bit patterns) -------------------------
+    D, Hq, Hkv = w.head_dim, w.num_heads, w.num_kv_heads
+    q = _bits(encode(_normal(seed, STREAM_Q, 0, (B, Hq, D)), w.dtype))
+    pool = (w.num_blocks, BS, Hkv, D)
+    if unallocated == "nan":
+        key_cache = np.full(pool, nan_bits(w.dtype), dtype=np.uint16)
+        value_cache = np.full(pool, nan_bits(w.dtype), dtype=np.uint16)
+    else:
+        key_cache = np.zeros(pool, dtype=np.uint16)
+        value_cache = np.zeros(pool, dtype=np.uint16)
+    order = []
+    seen = set()
+    for t in tables:
+        for b in t.physical_blocks:
+            if b not in seen:
+                seen.add(b)
+                order.append(b)
+    order = np.asarray(order, dtype=np.int64)
+    _fill_blocks(seed, STREAM_K, key_cache, order, w.dtype)
+    _fill_blocks(seed, STREAM_V, value_cache, order, w.dtype)
+    new_key = _bits(encode(_normal(seed, STREAM_NEW_K, 0, (B, Hkv, D)), w.dtype))
+    new_value = _bits(encode(_normal(seed, STREAM_NEW_V, 0, (B, Hkv, D)), w.dtype))
+    # -- poison the new token's slot and every idle tail slot ----------------
+    if poison is not None:
+        pv = nan_bits(w.dtype) if poison == "nan" else np.uint16(0)
+        for i in range(B):
+            L = int(ctx[i])
+            if L <= 0:
+                continue
+            last = tables[i].physical_blocks[(L - 1) // BS]
+            off = (L - 1) % BS
+            key_cache[last, off:] = pv
+            value_cache[last, off:] = pv
+    edt = element_numpy_dtype(w.dtype)
+    q, key_cache, value_cache, new_key, new_value = (
+        a.view(edt) for a in (q, key_cache, value_cache, new_key, new_value))
+    scale = 1.0 / math.sqrt(D)
+    return Batch(w, q, key_cache, value_cache, bt, ctx.astype(np.int32), new_key,
+                 new_value, slots, scale, order, np.asarray(shared, dtype=np.int64),
+                 dict(mgr.refcount))
+
+
+def _grow(mgr, seq_id):
+    """Take one block from the free list for seq_id's table."""
+    b = mgr._pop()
+    mgr.allocated.setdefault(seq_id, []).append(b)
+    return b
+
+
+def custom_workload(name="custom", **kw):
+    base = dict(num_seqs=2, num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16",
+                block_size=16, num_blocks=64, max_blocks_per_seq=8,
+                lens="uniform:1:128")
+    base.update(kw)
+    return Workload(name, **base)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting for the measurement
+# ---------------------------------------------------------------------------
+
+
+def element_bytes(dtype):
+    return {"f16": 2, "bf16": 2, "f32": 4}[dtype]
+
+
+def step_bytes(batch, out_dtype=None):
+    """Algorithmic bytes of one decode step (attention part).
+
+    Σ L_i · 2·Hkv·D·e for K and V, plus q, the output, the block-table entries
+    actually used and the context lengths. Returns (unique, logical): unique
+    counts each shared physical block once.
+    """
+    w = batch.workload
+    e = element_bytes(w.dtype)
+    eo = element_bytes(out_dtype or w.dtype)
+    B = len(batch.context_lens)
+    per_tok = 2 * w.num_kv_heads * w.head_dim * e
+    L = batch.context_lens.astype(np.int64)
+    logical_tokens = int(L.sum())
+    shared_tokens = len(batch.shared_blocks) * w.block_size
+    n_sharing = int((L > shared_tokens).sum()) if shared_tokens else 0
+    unique_tokens = logical_tokens - max(n_sharing - 1, 0) * shared_tokens if shared_tokens else logical_tokens
+    nblk = int(sum(-(-int(x) // w.block_size) for x in L))
+    fixed = B * w.num_heads * w.head_dim * (e + eo) + 4 * nblk + 4 * B
+    return unique_tokens * per_tok + fixed, logical_tokens * per_tok + fixed
+
+
+def cache_write_bytes(batch):
+    """reshape_and_cache bytes: new K/V read + written, plus 8-byte slots."""
+    w = batch.workload
+    e = element_bytes(w.dtype)
+    T = len(batch.slot_mapping)
+    return 2 * (2 * T * w.num_kv_heads * w.head_dim * e) + 8 * T

@@ -1,0 +1,425 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it follows. None of them re-types the oracle's
+own formula: they use printed worked examples, a library attention routine on
+unpaged data, closed forms, invariances the pages state, and brute force.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.paging_helpers import paginate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Block arithmetic and printed tables
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("case", _load("block_arithmetic.json")["cases"])
+def test_block_counts_match_printed_examples(case):
+    assert oracle.blocks_needed(case["tokens"], case["block_size"]) == case["blocks"]
+    assert oracle.unused_slots(case["tokens"], case["block_size"]) == case["unused"]
+
+
+def test_idle_slots_never_reach_a_block():
+    # "only the last block wastes, at most block_size - 1 slots"
+    for bs in (1, 4, 16, 32, 128):
+        for n in range(0, 4 * bs + 3):
+            u = oracle.unused_slots(n, bs)
+            assert 0 <= u <= bs - 1
+            assert oracle.blocks_needed(n, bs) * bs >= n
+
+
+@pytest.mark.parametrize("ex", _load("printed_block_tables.json")["examples"])
+def test_printed_tables_gather_in_logical_order(ex):
+    """A cache whose every slot stores its own (block, offset) coordinates is
+    gathered through the printed table; the gathered sequence must visit the
+    physical blocks and offsets in the printed order."""
+    bs = ex["block_size"]
+    phys = ex["physical"]
+    fill = ex["fill"] or [bs] * len(phys)
+    L = sum(fill)
+    nb_pool = max(phys) + 1
+    cache = np.zeros((nb_pool, bs, 1, 2), dtype=np.float32)
+    for b in range(nb_pool):
+        for o in range(bs):
+            cache[b, o, 0] = (b, o)
+    seq = oracle.gather_sequence(cache, np.array(phys), L, bs)
+    assert seq.shape == (L, 1, 2)
+    t = 0
+    for j, (p, f) in enumerate(zip(phys, fill)):
+        for o in range(f):
+            assert tuple(seq[t, 0]) == (p, o), (t, p, o)
+            t += 1
+    if "tokens_by_physical_block" in ex:
+        for p, toks in ex["tokens_by_physical_block"].items():
+            for o, tok in enumerate(toks):
+                assert oracle.slot_of_token(phys, tok, bs) == int(p) * bs + o
+
+
+def test_reshape_and_cache_places_tokens_as_printed():
+    """Write K0..K9 of the diagram's sequence A through its slots; the
+    physical blocks must then hold exactly the printed tokens, and the
+    sentinel elsewhere stays untouched."""
+    ex = _load("printed_block_tables.json")["examples"][1]
+    bs = ex["block_size"]
+    phys = ex["physical"]
+    sentinel = np.uint16(0xBEEF)
+    kc = np.full((16, bs, 2, 3), sentinel, dtype=np.uint16)
+    vc = np.full((16, bs, 2, 3), sentinel, dtype=np.uint16)
+    T = 10
+    key = np.arange(T * 6, dtype=np.uint16).reshape(T, 2, 3)
+    value = (1000 + np.arange(T * 6)).astype(np.uint16).reshape(T, 2, 3)
+    slots = np.array([oracle.slot_of_token(phys, t, bs) for t in range(T)], dtype=np.int64)
+    kc2, vc2 = oracle.reshape_and_cache(key, value, kc, vc, slots)
+    written = np.zeros(kc.shape[:2], dtype=bool)
+    for p, toks in ex["tokens_by_physical_block"].items():
+        for o, tok in enumerate(toks):
+            assert np.array_equal(kc2[int(p), o], key[tok])
+            assert np.array_equal(vc2[int(p), o], value[tok])
+            written[int(p), o] = True
+    assert np.all(kc2[~written] == sentinel) and np.all(vc2[~written] == sentinel)
+    # the inputs are not modified in place
+    assert np.all(kc == sentinel)
+
+
+def test_reshape_and_cache_skips_negative_slots_and_rejects_out_of_range():
+    kc = np.zeros((2, 4, 1, 1), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    key = np.array([[[7]], [[9]]], dtype=np.uint16)
+    kc2, _ = oracle.reshape_and_cache(key, key, kc, vc, np.array([-1, 5]))
+    assert kc2[1, 1, 0, 0] == 9 and int(kc2.sum()) == 9
+    with pytest.raises(IndexError):
+        oracle.reshape_and_cache(key, key, kc, vc, np.array([0, 8]))
+
+
+# ---------------------------------------------------------------------------
+# Attention: library routine on unpaged data, closed forms, invariances
+# ---------------------------------------------------------------------------
+
+
+def _random_logical(rng, lens, hkv, d, dtype=np.float16):
+    ks = [rng.standard_normal((L, hkv, d)).astype(dtype) for L in lens]
+    vs = [rng.standard_normal((L, hkv, d)).astype(dtype) for L in lens]
+    return ks, vs
+
+
+def _sdpa_reference(q, ks, vs, scale, group):
+    """torch's scaled_dot_product_attention in float64 on the contiguous,
+    unpaged sequences (kv heads repeated for grouped queries)."""
+    out = np.zeros(q.shape, dtype=np.float64)
+    for i, (k, v) in enumerate(zip(ks, vs)):
+        if k.shape[0] == 0:
+            continue
+        qt = torch.from_numpy(q[i].astype(np.float64))[:, None, :]          # [Hq,1,D]
+        kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2)        # [Hkv,L,D]
+        vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2)
+        kt = kt.repeat_interleave(group, dim=0).contiguous()
+        vt = vt.repeat_interleave(group, dim=0).contiguous()
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+        out[i] = o[:, 0, :].numpy()
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(4, 4, 16), (8, 2, 4), (6, 1, 32)])
+def test_decode_matches_library_attention_on_unpaged_data(hq, hkv, bs):
+    rng = np.random.default_rng(11)
+    d = 16
+    lens = [1, 5, bs, bs + 1, 3 * bs - 1, 70]
+    ks, vs = _random_logical(rng, lens, hkv, d)
+    q = rng.standard_normal((len(lens), hq, d)).astype(np.float16)
+    kc, bt = paginate(ks, bs, 64, rng, fill=np.float16(np.nan))
+    vc, _ = paginate(vs, bs, 64, np.random.default_rng(11 + 1000), fill=np.float16(np.nan))
+    # both caches must use the same tables: rebuild V with K's tables
+    vc = np.full_like(kc, np.float16(np.nan))
+    for i, v in enumerate(vs):
+        nb = -(-v.shape[0] // bs)
+        pad = np.full((nb * bs, hkv, d), np.float16(np.nan), dtype=np.float16)
+        pad[:v.shape[0]] = v
+        vc[bt[i, :nb]] = pad.reshape(nb, bs, hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    got = oracle.decode(q, kc, vc, bt, np.array(lens), scale, "f16")
+    ref = _sdpa_reference(q, ks, vs, scale, hq // hkv)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_bf16_inputs_are_read_exactly():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(1000).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)      # truncation: exact bf16 values
+    back = oracle.upcast(bits, "bf16")
+    # torch's own bfloat16 decoding of the same bits
+    expect = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(back, expect)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -7)
+    assert oracle.upcast(np.array([0x3F80], dtype=np.uint16), "bf16")[0] == 1.0
+    assert oracle.upcast(np.array([0xC000], dtype=np.uint16), "bf16")[0] == -2.0
+
+
+def test_single_token_context_returns_its_value_row():
+    rng = np.random.default_rng(3)
+    ks, vs = _random_logical(rng, [1, 1], 2, 8)
+    q = rng.standard_normal((2, 2, 8)).astype(np.float16)
+    kc, bt = paginate(ks, 16, 8, np.random.default_rng(1))
+    vc, _ = paginate(vs, 16, 8, np.random.default_rng(1))
+    out = oracle.decode(q, kc, vc, bt, np.array([1, 1]), 0.25, "f16")
+    for i in range(2):
+        assert np.array_equal(out[i], vs[i][0].astype(np.float64))
+
+
+def test_zero_query_averages_the_values():
+    rng = np.random.default_rng(4)
+    ks, vs = _random_logical(rng, [37], 1, 8)
+    q = np.zeros((1, 3, 8), dtype=np.float16)
+    kc, bt = paginate(ks, 16, 8, np.random.default_rng(2))
+    vc, _ = paginate(vs, 16, 8, np.random.default_rng(2))
+    out = oracle.decode(q, kc, vc, bt, np.array([37]), 1.0, "f16")
+    mean = vs[0][:, 0, :].astype(np.float64).mean(axis=0)
+    for h in range(3):
+        np.testing.assert_allclose(out[0, h], mean, rtol=0, atol=1e-15)
+
+
+def test_dominant_token_selects_its_value_row():
+    """One logical token's scaled logit is +1448 and every other one -1448,
+    so its softmax weight is 1 in float64 and the output is that value row
+    (and exp of the raw logit would overflow, so the max must be removed)."""
+    L, d = 40, 8
+    q = np.zeros((1, 1, d), dtype=np.float16)
+    q[0, 0, :4] = 64.0
+    k = np.zeros((L, 1, d), dtype=np.float16)
+    k[:, 0, :4] = -64.0
+    j = 27
+    k[j, 0, :4] = 64.0
+    v = np.arange(L * d, dtype=np.float16).reshape(L, 1, d) + 1
+    kc, bt = paginate([k], 16, 8, np.random.default_rng(9))
+    vc, _ = paginate([v], 16, 8, np.random.default_rng(9))
+    out = oracle.decode(q, kc, vc, bt, np.array([L]), 1.0 / math.sqrt(128), "f16")
+    assert np.array_equal(out[0, 0], v[j, 0].astype(np.float64))
+
+
+def test_zero_context_gives_zero_output():
+    q = np.ones((2, 2, 4), dtype=np.float16)
+    kc = np.full((4, 4, 2, 4), np.float16(np.nan))
+    bt = np.full((2, 2), -1, dtype=np.int32)
+    bt[1, 0] = 2
+    kc[2] = 1.0
+    out = oracle.decode(q, kc, kc, bt, np.array([0, 3]), 0.5, "f16")
+    assert np.all(out[0] == 0.0)
+    assert np.all(out[1] == 1.0)
+
+
+def test_physical_placement_does_not_change_the_result():
+    """Same logical K/V under two random physical layouts: identical bits."""
+    rng = np.random.default_rng(21)
+    lens = [3, 17, 64, 100]
+    ks, vs = _random_logical(rng, lens, 2, 8)
+    q = rng.standard_normal((4, 4, 8)).astype(np.float16)
+    outs = []
+    for seed in (100, 200):
+        kc, bt = paginate(ks, 16, 40, np.random.default_rng(seed))
+        vc, _ = paginate(vs, 16, 40, np.random.default_rng(seed))
+        outs.append(oracle.decode(q, kc, vc, bt, np.array(lens), 0.3, "f16"))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_shared_prefix_blocks_equal_private_copies():
+    """Sequences whose tables point at the same prefix blocks give the same
+    result as with private copies of those blocks."""
+    rng = np.random.default_rng(8)
+    bs, hkv, d = 8, 2, 8
+    prefix_k = rng.standard_normal((3 * bs, hkv, d)).astype(np.float16)
+    prefix_v = rng.standard_normal((3 * bs, hkv, d)).astype(np.float16)
+    suf = [5, 9, 1]
+    ks = [np.concatenate([prefix_k, rng.standard_normal((s, hkv, d)).astype(np.float16)]) for s in suf]
+    vs = [np.concatenate([prefix_v, rng.standard_normal((s, hkv, d)).astype(np.float16)]) for s in suf]
+    q = rng.standard_normal((3, 4, d)).astype(np.float16)
+    lens = np.array([k.shape[0] for k in ks])
+    kc_priv, bt_priv = paginate(ks, bs, 32, np.random.default_rng(1))
+    vc_priv, _ = paginate(vs, bs, 32, np.random.default_rng(1))
+    # shared layout: prefix in blocks 0..2, suffixes after
+    kc = np.full((32, bs, hkv, d), np.float16(np.nan))
+    vc = np.full_like(kc, np.float16(np.nan))
+    kc[0:3] = prefix_k.reshape(3, bs, hkv, d)
+    vc[0:3] = prefix_v.reshape(3, bs, hkv, d)
+    bt = np.full((3, 8), -1, dtype=np.int32)
+    nxt = 10
+    for i, s in enumerate(suf):
+        nb = -(-s // bs)
+        bt[i, :3] = [0, 1, 2]
+        for j in range(nb):
+            rows = ks[i][3 * bs + j * bs: 3 * bs + (j + 1) * bs]
+            rv = vs[i][3 * bs + j * bs: 3 * bs + (j + 1) * bs]
+            kc[nxt, :rows.shape[0]] = rows
+            vc[nxt, :rv.shape[0]] = rv
+            bt[i, 3 + j] = nxt
+            nxt += 1
+    shared = oracle.decode(q, kc, vc, bt, lens, 0.35, "f16")
+    private = oracle.decode(q, kc_priv, vc_priv, bt_priv, lens, 0.35, "f16")
+    assert np.array_equal(shared, private)
+
+
+def test_unfilled_slots_are_ignored_even_when_nan():
+    rng = np.random.default_rng(12)
+    lens = [1, 15, 16, 17, 33]
+    ks, vs = _random_logical(rng, lens, 2, 8)
+    q = rng.standard_normal((5, 2, 8)).astype(np.float16)
+    clean_k, bt = paginate(ks, 16, 20, np.random.default_rng(3), fill=0.0)
+    clean_v, _ = paginate(vs, 16, 20, np.random.default_rng(3), fill=0.0)
+    dirty_k, _ = paginate(ks, 16, 20, np.random.default_rng(3), fill=np.float16(np.nan))
+    dirty_v, _ = paginate(vs, 16, 20, np.random.default_rng(3), fill=np.float16(np.nan))
+    bt_dirty = bt.copy()
+    bt_dirty[bt_dirty < 0] = 999  # padding entries must never be used
+    a = oracle.decode(q, clean_k, clean_v, bt, np.array(lens), 0.4, "f16")
+    b = oracle.decode(q, dirty_k, dirty_v, bt_dirty, np.array(lens), 0.4, "f16")
+    assert np.isfinite(b).all()
+    assert np.array_equal(a, b)
+
+
+def test_grouped_query_heads_equal_mha_with_repeated_kv():
+    rng = np.random.default_rng(14)
+    lens = [20, 33]
+    g = 4
+    ks, vs = _random_logical(rng, lens, 2, 8)
+    q = rng.standard_normal((2, 8, 8)).astype(np.float16)
+    kc, bt = paginate(ks, 16, 16, np.random.default_rng(4))
+    vc, _ = paginate(vs, 16, 16, np.random.default_rng(4))
+    gqa = oracle.decode(q, kc, vc, bt, np.array(lens), 0.3, "f16")
+    kc_rep = np.repeat(kc, g, axis=2)
+    vc_rep = np.repeat(vc, g, axis=2)
+    mha = oracle.decode(q, kc_rep, vc_rep, bt, np.array(lens), 0.3, "f16")
+    assert np.array_equal(gqa, mha)
+
+
+@pytest.mark.parametrize("part", [16, 32, 48, 256, 512])
+def test_partitions_merged_by_lse_equal_single_pass(part):
+    rng = np.random.default_rng(30)
+    lens = [0, 1, 16, 47, 300, 600]
+    ks, vs = _random_logical(rng, lens[1:], 2, 8)
+    ks = [np.zeros((0, 2, 8), np.float16)] + ks
+    vs = [np.zeros((0, 2, 8), np.float16)] + vs
+    q = rng.standard_normal((6, 4, 8)).astype(np.float16)
+    kc, bt = paginate([k if k.shape[0] else np.zeros((1, 2, 8), np.float16) for k in ks],
+                      16, 80, np.random.default_rng(5))
+    vc, _ = paginate([v if v.shape[0] else np.zeros((1, 2, 8), np.float16) for v in vs],
+                     16, 80, np.random.default_rng(5))
+    direct = oracle.decode(q, kc, vc, bt, np.array(lens), 0.3, "f16")
+    split = oracle.decode_split(q, kc, vc, bt, np.array(lens), 0.3, "f16", part)
+    np.testing.assert_allclose(split, direct, rtol=0, atol=1e-12)
+    m, l, o = oracle.decode_partitions(q, kc, vc, bt, np.array(lens), 0.3, "f16", part)
+    # empty partitions carry -inf / 0 / 0
+    assert np.all(np.isneginf(m[0])) and np.all(l[0] == 0) and np.all(o[0] == 0)
+    for i, L in enumerate(lens):
+        n = oracle.blocks_needed(L, part)
+        assert np.all(np.isfinite(m[i, :, :n]))
+        assert np.all(np.isneginf(m[i, :, n:]))
+        assert np.all(l[i, :, :n] >= 1.0)   # the max term contributes exp(0) = 1
+
+
+def test_brute_force_scalar_loops_on_tiny_inputs():
+    """Dense, unpaged attention with math.exp in plain Python loops."""
+    rng = np.random.default_rng(2)
+    lens = [1, 7, 18]
+    hkv, g, d, bs = 2, 2, 4, 4
+    ks, vs = _random_logical(rng, lens, hkv, d)
+    q = rng.standard_normal((3, hkv * g, d)).astype(np.float16)
+    kc, bt = paginate(ks, bs, 16, np.random.default_rng(6))
+    vc, _ = paginate(vs, bs, 16, np.random.default_rng(6))
+    scale = 0.7
+    got = oracle.decode(q, kc, vc, bt, np.array(lens), scale, "f16")
+    for i, L in enumerate(lens):
+        for h in range(hkv * g):
+            kv = h // g
+            logits = []
+            for t in range(L):
+                acc = 0.0
+                for c in range(d):
+                    acc += float(q[i, h, c]) * float(ks[i][t, kv, c])
+                logits.append(acc * scale)
+            top = max(logits)
+            ws = [math.exp(x - top) for x in logits]
+            tot = math.fsum(ws)
+            for c in range(d):
+                val = math.fsum(ws[t] * float(vs[i][t, kv, c]) for t in range(L)) / tot
+                assert abs(got[i, h, c] - val) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each plausible slip in the oracle fails a pin above
+# ---------------------------------------------------------------------------
+
+
+def _mutant_cases():
+    def drop_scale(q, kc, vc, bt, lens, scale, dt):
+        return ORIG_DECODE(q, kc, vc, bt, lens, 1.0, dt)
+
+    def wrong_group_map(q, kc, vc, bt, lens, scale, dt):
+        # h % Hkv instead of h // G
+        hq, hkv = q.shape[1], kc.shape[2]
+        perm = [(h % hkv) * (hq // hkv) + h // hkv for h in range(hq)]
+        out = ORIG_DECODE(q[:, perm], kc, vc, bt, lens, scale, dt)
+        inv = np.argsort(perm)
+        return out[:, inv]
+
+    def no_max_subtraction(q, kc, vc, bt, lens, scale, dt):
+        out = np.zeros(q.shape)
+        for i in range(q.shape[0]):
+            K = oracle.upcast(oracle.gather_sequence(kc, bt[i], lens[i], kc.shape[1]), dt)
+            V = oracle.upcast(oracle.gather_sequence(vc, bt[i], lens[i], kc.shape[1]), dt)
+            for h in range(q.shape[1]):
+                s = scale * (K[:, h * kc.shape[2] // q.shape[1]] @ oracle.upcast(q[i, h], dt))
+                p = np.exp(s)
+                out[i, h] = (p / p.sum()) @ V[:, h * kc.shape[2] // q.shape[1]]
+        return out
+
+    return {"drop_scale": drop_scale, "wrong_group_map": wrong_group_map,
+            "no_max_subtraction": no_max_subtraction}
+
+
+ORIG_DECODE = oracle.decode
+
+
+@pytest.mark.parametrize("name", ["drop_scale", "wrong_group_map", "no_max_subtraction"])
+def test_planted_oracle_mistakes_are_caught(name, monkeypatch):
+    mutant = _mutant_cases()[name]
+    monkeypatch.setattr(oracle, "decode", mutant)
+    failed = False
+    try:
+        if name == "no_max_subtraction":
+            test_dominant_token_selects_its_value_row()
+        else:
+            test_decode_matches_library_attention_on_unpaged_data(8, 2, 4)
+    except AssertionError:
+        failed = True
+    except FloatingPointError:
+        failed = True
+    assert failed, "pin did not catch planted mistake %s" % name
+
+
+def test_planted_gather_mistake_is_caught(monkeypatch):
+    orig = oracle.gather_sequence
+
+    def off_by_one(cache, row, L, bs):   # keeps the idle tail instead of the head
+        seq = orig(cache, row, L, bs)
+        nb = oracle.blocks_needed(L, bs)
+        full = np.concatenate([cache[int(row[j])] for j in range(nb)], axis=0) if nb else seq
+        return full[nb * bs - L:] if nb else seq
+
+    import oracle.paged_attention as pa
+    monkeypatch.setattr(pa, "gather_sequence", off_by_one)
+    with pytest.raises(AssertionError):
+        test_unfilled_slots_are_ignored_even_when_nan()
