@@ -1,0 +1,204 @@
+"""Benchmark one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one seeded synthetic batch: the new
+tokens' K/V are scattered into their slots (pa_reshape_and_cache), then
+every sequence's query attends over its paged context (pa_decode, or
+pa_decode_split for the long-context workloads). Inputs are resident in HBM
+before timing starts; the timed loop cycles through copies of the batch whose
+blocks sit at different physical places, so no step re-reads the previous
+step's blocks out of the 256 MB last-level cache.
+
+Prints one JSON line. `value` is KV GB/s: the step's algorithmic bytes
+(Σ context_len · 2·Hkv·D·e for K and V, plus q, the output, the block-table
+entries used, the context lengths and the cache write) over the measured
+step time.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama13b]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama13b")
+    ap.add_argument("--path", choices=["auto", "decode", "split"], default="auto")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--out-dtype", choices=["native", "f32"], default="native")
+    ap.add_argument("--rotations", type=int, default=0, help="batch copies cycled (0 = auto)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    return ap.parse_args()
+
+
+def default_path(workload):
+    # long contexts (tens of partitions per sequence) go through the split path
+    return "split" if workload.name in ("gqa_long", "shared_prefix") else "decode"
+
+
+def cpu_baseline(batch, target_s):
+    """Time the fp64 CPU oracle on a bounded sample of the same step."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_138_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    w = batch.workload
+    B = len(batch.context_lens)
+    order = list(range(B))
+    bytes_per_tok = 2 * w.num_kv_heads * w.head_dim * W.element_bytes(w.dtype)
+    done_seqs = 0
+    done_bytes = 0
+    t0 = time.perf_counter()
+    kc, vc = oracle.reshape_and_cache(batch.new_key, batch.new_value, batch.key_cache,
+                                      batch.value_cache, batch.slot_mapping) if B <= 64 else (None, None)
+    t_write = time.perf_counter() - t0
+    elapsed = 0.0
+    i = 0
+    while elapsed < target_s and i < 4 * B:
+        s = order[i % B]
+        sl = slice(s, s + 1)
+        if kc is None:
+            kc1, vc1 = oracle.reshape_and_cache(batch.new_key[sl], batch.new_value[sl], batch.key_cache,
+                                                batch.value_cache, batch.slot_mapping[sl])
+        else:
+            kc1, vc1 = kc, vc
+        t1 = time.perf_counter()
+        oracle.decode(batch.query[sl], kc1, vc1, batch.block_tables[sl], batch.context_lens[sl],
+                      batch.scale, w.dtype)
+        elapsed += time.perf_counter() - t1
+        done_bytes += int(batch.context_lens[s]) * bytes_per_tok
+        done_seqs += 1
+        i += 1
+    if limiter is not None:
+        limiter.unregister()
+    gbs = done_bytes / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d sequence-steps of the %s batch (all %d heads; KV bytes %d) in %.1f s of "
+                      "oracle decode, 1 BLAS thread; cache-write oracle %.2f s not counted"
+                      % (done_seqs, w.name, w.num_heads, done_bytes, elapsed, t_write),
+            "seq_tokens_per_s": round(done_seqs / elapsed, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from paged_kv_cache_138_amd import lib as palib
+    from paged_kv_cache_138_amd import workloads as W
+    from paged_kv_cache_138_amd.pipeline import DeviceBatch, RotatedBatch
+
+    palib.load()  # fails loudly if libpa.so is missing
+    w = W.WORKLOADS[args.workload]
+    path = default_path(w) if args.path == "auto" else args.path
+    t_gen = time.perf_counter()
+    batch = W.make_batch(w, seed=args.seed)
+    t_gen = time.perf_counter() - t_gen
+    out_dtype = torch.float32 if args.out_dtype == "f32" else None
+    base = DeviceBatch(batch, out_dtype=out_dtype, split=(path == "split"),
+                       partition_size=args.partition_size)
+    unique_bytes, logical_bytes = W.step_bytes(batch, None if out_dtype is None else "f32")
+    write_bytes = W.cache_write_bytes(batch)
+    # rotation copies: enough that the cycle's footprint is >= 8x the LLC
+    kv_block = 2 * base.key_cache[0].numel() * base.key_cache.element_size()
+    footprint = kv_block * len(batch.allocated_blocks)
+    R = args.rotations or max(2, min(16, -(-8 * LLC_BYTES // max(footprint, 1))))
+    copies = [RotatedBatch(base, seed=1000 + r) for r in range(R)]
+    del base
+    torch.cuda.synchronize()
+
+    for k in range(args.warmup):
+        copies[k % R].step()
+    torch.cuda.synchronize()
+    # all copies must agree bit for bit (same logical data, different placement)
+    ref = copies[0].out.clone()
+    for c in copies[1:]:
+        c.step()
+    torch.cuda.synchronize()
+    for c in copies[1:]:
+        assert torch.equal(c.out.view(torch.int16) if c.out.dtype != torch.float32 else c.out,
+                           ref.view(torch.int16) if ref.dtype != torch.float32 else ref), \
+            "rotated copies disagree"
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        c = copies[k % R]
+        c.write_cache()
+        ev[k][0].record()
+        c.attend()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg_ms = float(np.mean(attn_ms))
+    step_bytes = unique_bytes + write_bytes
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    attn_gbs = unique_bytes / (attn_avg_ms * 1e-3) / 1e9
+    B = len(batch.context_lens)
+    res = {
+        "metric": "paged decode attn: KV GB/s (% HBM peak) + seq-tokens/s, LLaMA-13B shape",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "num_seqs": B,
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "sum_context_lens": int(batch.context_lens.sum()),
+                   "path": path, "partition_size": base_partition(path, args, w),
+                   "out_dtype": args.out_dtype, "rotations": R, "seed": args.seed},
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "seq_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "context_tokens_per_s": round(int(batch.context_lens.sum()) / (ms_per_step * 1e-3), 1),
+        "step_bytes": {"attention_unique": unique_bytes, "attention_logical": logical_bytes,
+                       "cache_write": write_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attention (%s), HIP events around each launch; avg %.2f us, "
+                               "min %.2f us" % (path, attn_avg_ms * 1e3, min(attn_ms) * 1e3)},
+        "host_data_generation_s": round(t_gen, 2),
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def base_partition(path, args, w):
+    if path != "split":
+        return None
+    return args.partition_size or w.partition_size
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * pa.h - C ABI of libpa: paged decode attention and the KV-cache scatter on
+ * MI355X (gfx950).
+ *
+ * The operations follow the pages' statement of the problem:
+ *   - KV cache per layer laid out [num_blocks, block_size, num_kv_heads,
+ *     head_dim]; physical blocks are not contiguous per sequence and are
+ *     found through a per-sequence block table ("vLLM PagedAttention深度解析
+ *     与工程实践" §3.1 Block Table and §4.1 注意力计算的修改;
+ *     lqnn.cn/news/170268 §2.2).
+ *   - Each decode step appends the new token's K/V into a free slot of the
+ *     sequence's current block or of a newly taken block (same pages, §二
+ *     and §2.2): pa_reshape_and_cache.
+ *   - Decode attention walks the block table, scores the query against every
+ *     cached token, weights V by softmax(q·Kᵀ·scale) and writes the output
+ *     ("vLLM PagedAttention深度解析与工程实践" §二 formula;
+ *     lqnn.cn/news/170268 §2.3 three steps): pa_decode.
+ *   - The long-context variant accumulates per context partition and then
+ *     merges ("vLLM PagedAttention深度解析与工程实践" §4.1, the v2 kernel):
+ *     pa_decode_split, with the merge exported as pa_lse_merge.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE memory owned by the caller; tensors are
+ *     dense and row-major in the layouts stated below, 16-byte aligned.
+ *     The library allocates nothing and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the default
+ *     stream); nothing is synchronised. Calls that write the same buffers
+ *     race if they overlap on different streams.
+ *   - Host-side validation happens before any launch. A non-zero status
+ *     means nothing was launched and nothing was written; pa_last_error()
+ *     gives the detail (thread-local, valid until the next call on the
+ *     same thread). No C++ exception crosses this boundary.
+ *   - Device data the host cannot see without a synchronisation (block ids,
+ *     context lengths, slots) are the caller's contract; the kernels still
+ *     never touch memory outside the buffers: a block id outside
+ *     [0, num_blocks) makes its tokens count as absent, a context length is
+ *     clamped to [0, max_blocks_per_seq * block_size], a slot outside
+ *     [0, num_blocks * block_size) is skipped.
+ *   - Element types: KV cache, query and new K/V share `dtype`
+ *     (PA_F16 or PA_BF16). Outputs may be that type (rounded to nearest
+ *     even from fp32) or PA_F32. All accumulation is fp32
+ *     (lqnn.cn/news/170268 §6: half-precision accumulation of the scores
+ *     degrades long sequences).
+ *   - Supported shapes: head_dim in {64, 128}; block_size in {16, 32};
+ *     num_heads a multiple of num_kv_heads (query head h reads kv head
+ *     h / (num_heads / num_kv_heads)).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,         /* a required pointer is NULL */
+    PA_ERR_SHAPE = 2,        /* sizes out of range or inconsistent */
+    PA_ERR_DTYPE = 3,        /* element type not accepted here */
+    PA_ERR_UNSUPPORTED = 4,  /* valid request without a compiled instance */
+    PA_ERR_WORKSPACE = 5,    /* workspace NULL, too small or misaligned */
+    PA_ERR_LAUNCH = 6,       /* the HIP runtime refused the launch */
+    PA_ERR_ALIGNMENT = 7     /* a data pointer is not 16-byte aligned */
+} pa_status;
+
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_F32 = 2 } pa_dtype;
+
+/*
+ * pa_reshape_and_cache - store each new token's K and V in its cache slot.
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_dim] of `dtype`; token n
+ *                     starts at key + n * key_token_stride elements (use
+ *                     num_kv_heads * head_dim for a dense tensor; larger
+ *                     strides let K/V be read straight out of a fused QKV
+ *                     projection). Heads and dims of one token are dense.
+ *   key_cache,
+ *   value_cache       [num_blocks, block_size, num_kv_heads, head_dim], written
+ *                     in place.
+ *   slot_mapping      int64 [num_tokens]; slot s means block s / block_size,
+ *                     row s % block_size. s < 0 marks padding: the token is
+ *                     skipped. Slots must be distinct (else the result for
+ *                     the duplicated slot is one of the writers, unspecified).
+ *
+ * Bit-exact copy; no arithmetic on the elements. num_tokens == 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value,
+                               void* key_cache, void* value_cache,
+                               const int64_t* slot_mapping, int num_tokens,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               int num_kv_heads, int head_dim, int num_blocks,
+                               int block_size, pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode - one query token per sequence attends over its paged context,
+ * in a single launch (no workspace).
+ *
+ *   out               [num_seqs, num_heads, head_dim] of `out_dtype`
+ *                     (PA_F32 or the cache's dtype).
+ *   query             [num_seqs, num_heads, head_dim] of `kv_dtype`.
+ *   key_cache,
+ *   value_cache       [num_blocks, block_size, num_kv_heads, head_dim].
+ *   block_tables      int32 [num_seqs, max_blocks_per_seq]; entry j of row i
+ *                     is the physical block of sequence i's logical block j.
+ *                     Only the first ceil(L_i / block_size) entries are read.
+ *   context_lens      int32 [num_seqs]; L_i counts every cached token of
+ *                     sequence i, the one written this step included.
+ *   scale             multiplies q·k before the softmax (1/sqrt(head_dim) in
+ *                     the usual attention).
+ *
+ * out[i, h, :] = Σ_t softmax_t(scale · q_ih · K_i[t]) · V_i[t] over t < L_i;
+ * a sequence with L_i == 0 gets zeros. Slots at or past L_i in the last
+ * block are never read, whatever they hold.
+ */
+pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
+                    const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                    int block_size, int max_blocks_per_seq, int num_blocks,
+                    float scale, pa_dtype kv_dtype, void* stream);
+
+/*
+ * Workspace of pa_decode_split, in bytes, for these sizes. With
+ * NP = ceil(max_blocks_per_seq * block_size / partition_size) it holds, each
+ * region starting on a 256-byte boundary in this order:
+ *   part_max  float [num_seqs, num_heads, NP]
+ *   part_sum  float [num_seqs, num_heads, NP]
+ *   part_out  float [num_seqs, num_heads, NP, head_dim]
+ * Returns 0 for invalid sizes.
+ */
+size_t pa_decode_split_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                       int max_blocks_per_seq, int block_size,
+                                       int partition_size);
+
+/*
+ * pa_decode_split - pa_decode computed as context partitions and a merge.
+ *
+ * Same arguments and result as pa_decode, plus:
+ *   partition_size    tokens per partition, a positive multiple of
+ *                     block_size; partition p of sequence i covers logical
+ *                     tokens [p*P, min((p+1)*P, L_i)).
+ *   workspace         device buffer of at least
+ *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
+ *                     aligned, owned by the caller; its contents on entry are
+ *                     ignored and on exit unspecified.
+ *
+ * Two launches on `stream`: the partition kernel writes each partition's
+ * (max logit, Σ exp, normalised partial output) for sequences with more than
+ * one partition - sequences with a single partition get their final output
+ * directly - then the merge combines the partitions by log-sum-exp.
+ */
+pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
+                          const void* key_cache, const void* value_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                          int block_size, int max_blocks_per_seq, int num_blocks,
+                          float scale, pa_dtype kv_dtype, int partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_lse_merge - combine per-partition results (the second launch of
+ * pa_decode_split, exported so it can be checked on its own).
+ *
+ *   part_max  float [num_seqs, num_heads, max_partitions]: m_p, the largest
+ *             scaled logit scale·q·k of partition p (natural-log units).
+ *   part_sum  float [num_seqs, num_heads, max_partitions]: l_p = Σ exp(s - m_p).
+ *   part_out  float [num_seqs, num_heads, max_partitions, head_dim]:
+ *             o_p = Σ exp(s - m_p) v / l_p.
+ *   context_lens  int32 [num_seqs]; sequence i uses partitions
+ *             p < ceil(L_i / partition_size).
+ *
+ * With M = max_p m_p and w_p = l_p exp(m_p - M):
+ * out = Σ_p w_p o_p / Σ_p w_p. Sequences with at most one partition are NOT
+ * written (pa_decode_split writes those directly).
+ */
+pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,
+                       const float* part_max, const float* part_sum,
+                       const int32_t* context_lens, int num_seqs, int num_heads,
+                       int head_dim, int max_partitions, int partition_size,
+                       void* stream);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Detail of the last failure on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

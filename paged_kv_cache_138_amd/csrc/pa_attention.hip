@@ -1,0 +1,543 @@
+// Paged decode attention: pa_decode, pa_decode_split and pa_lse_merge.
+//
+// What is computed ("vLLM PagedAttention深度解析与工程实践" §二 formula and
+// §4.1; lqnn.cn/news/170268 §2.3 and §6): for sequence i and query head h,
+// out = softmax(scale · K_i q_ih) · V_i over the sequence's first L_i logical
+// tokens, whose rows sit in physical blocks named by the block table. Slots
+// at or past L_i in the last block are never read.
+//
+// Work decomposition (MI355X, 64-lane wavefronts):
+//   * one workgroup = one (sequence, query head, context partition) with NW
+//     wavefronts; the waves take 64-token chunks of the partition in turn and
+//     their softmax states are merged in LDS at the end. The single-pass
+//     pa_decode is the same kernel with one partition covering the context.
+//   * inside a chunk, one 16-byte load per lane brings 8 elements of a K (or
+//     V) row: head_dim/8 lanes cover a row, 64 lanes cover 64*8/head_dim
+//     rows of one physical block per load instruction, so each load is a
+//     set of dense head_dim*2-byte row segments and the block's base address
+//     is uniform across the wavefront.
+//   * q·k: fp32 dot2 of packed fp16/bf16 pairs, then a transpose-reduce over
+//     the lanes of a row that leaves lane c of each row group holding the
+//     full score of that group's c-th load; softmax max/sum by wavefront
+//     shuffles; exp2 with log2(e) folded into the scale.
+//   * p·V: each lane scales its 8 V elements by the broadcast weight of its
+//     row; the rows are summed at the end of the partition.
+#include "pa_device.h"
+#include "pa_host.h"
+
+#include <math.h>
+
+namespace pa {
+namespace {
+
+struct AttnArgs {
+    void* out;
+    const uint16_t* query;
+    const uint16_t* key_cache;
+    const uint16_t* value_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* part_max;
+    float* part_sum;
+    float* part_out;
+    int num_seqs;
+    int num_heads;
+    int num_kv_heads;
+    int max_blocks_per_seq;
+    int num_blocks;
+    int partition_size;
+    int max_partitions;
+    float scale_log2;  // scale * log2(e)
+};
+
+constexpr int kWaves = 4;
+
+template <class KV, class OUT, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
+    constexpr int LPR = D / 8;          // lanes per cache row
+    constexpr int RPI = 64 / LPR;       // rows per load instruction
+    constexpr int IPB = BS / RPI;       // load instructions per block
+    constexpr int NI = LPR;             // load instructions per chunk
+    constexpr int CHUNK = RPI * NI;     // tokens per chunk (64)
+    constexpr int BPC = CHUNK / BS;     // blocks per chunk
+    constexpr int DPL = D / 64;         // output elements per lane in the epilogue
+    static_assert(CHUNK == 64, "one score per lane per chunk");
+    static_assert(BS % RPI == 0 && CHUNK % BS == 0, "block must tile the chunk");
+
+    __shared__ float sm_m[NW];
+    __shared__ float sm_l[NW];
+    __shared__ float sm_acc[NW][D];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane / LPR;  // row within a load instruction
+    const int c = lane % LPR;  // 8-element slice of the row
+
+    const int Hq = a.num_heads;
+    int bid = blockIdx.x;
+    const int head = bid % Hq;
+    bid /= Hq;
+    const int seq = bid % a.num_seqs;
+    const int part = bid / a.num_seqs;
+
+    const int Lmax = a.max_blocks_per_seq * BS;
+    int L = a.context_lens[seq];
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int P = a.partition_size;
+    const int nparts = (L + P - 1) / P;
+    if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+    const int start = part * P;
+    const int end = min(start + P, L);
+    const int nb = (L + BS - 1) / BS;
+
+    const int kvh = head / (Hq / a.num_kv_heads);
+    const size_t row_stride = (size_t)a.num_kv_heads * D;  // elements
+    const size_t block_stride = row_stride * BS;
+    const uint16_t* kc = a.key_cache + (size_t)kvh * D + c * 8;
+    const uint16_t* vc = a.value_cache + (size_t)kvh * D + c * 8;
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+
+    const u32x4 q = *(const u32x4*)(a.query + ((size_t)seq * Hq + head) * D + c * 8);
+
+    float m = -INFINITY;  // running max of scores (log2 units)
+    float lsum = 0.f;     // this lane's share of Σ exp2(s - m)
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+
+    for (int cs = start + wave * CHUNK; cs < end; cs += NW * CHUNK) {
+        const int lb0 = cs / BS;
+        int phys[BPC];
+        bool pok[BPC];
+#pragma unroll
+        for (int b = 0; b < BPC; ++b) {
+            const int lb = lb0 + b;
+            const int pid = lb < nb ? bt[lb] : -1;
+            pok[b] = pid >= 0 && pid < a.num_blocks;
+            phys[b] = pok[b] ? pid : 0;
+        }
+        // ---- K rows of the chunk ------------------------------------------
+        u32x4 kr[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int b = i / IPB;
+            const int row = (i % IPB) * RPI + r;
+            const bool ok = pok[b] && (cs + b * BS + row) < end;
+            const size_t off = (size_t)phys[b] * block_stride + (size_t)row * row_stride;
+            kr[i] = ok ? *(const u32x4*)(kc + off) : u32x4{0u, 0u, 0u, 0u};
+        }
+        // ---- V rows (issued early, used after the softmax update) --------
+        u32x4 vr[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int b = i / IPB;
+            const int row = (i % IPB) * RPI + r;
+            const bool ok = pok[b] && (cs + b * BS + row) < end;
+            const size_t off = (size_t)phys[b] * block_stride + (size_t)row * row_stride;
+            vr[i] = ok ? *(const u32x4*)(vc + off) : u32x4{0u, 0u, 0u, 0u};
+        }
+        // ---- partial dots over this lane's 8 elements ---------------------
+        float pd[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float t = KV::dot2(kr[i].x, q.x, 0.f);
+            t = KV::dot2(kr[i].y, q.y, t);
+            t = KV::dot2(kr[i].z, q.z, t);
+            pd[i] = KV::dot2(kr[i].w, q.w, t);
+        }
+        // ---- transpose-reduce across the LPR lanes of each row group -------
+        // after the step with mask `half`, a lane keeps the half of its list
+        // selected by bit `half` of c; at the end lane c owns load c.
+#pragma unroll
+        for (int half = NI / 2; half >= 1; half >>= 1) {
+            const bool upper = (c & half) != 0;
+#pragma unroll
+            for (int k = 0; k < half; ++k) {
+                const float send = upper ? pd[k] : pd[k + half];
+                const float keep = upper ? pd[k + half] : pd[k];
+                pd[k] = keep + __shfl_xor(send, half, 64);
+            }
+        }
+        const int myb = c / IPB;
+        const int mytok = cs + myb * BS + (c % IPB) * RPI + r;
+        bool mok = pok[0];
+#pragma unroll
+        for (int b = 1; b < BPC; ++b)
+            if (myb == b) mok = pok[b];
+        mok = mok && mytok < end;
+        const float s = mok ? pd[0] * a.scale_log2 : -INFINITY;
+        // ---- online softmax update ----------------------------------------
+        const float mn = fmaxf(m, wave_max(s));
+        float alpha, pr;
+        if (mn == -INFINITY) {  // no valid token yet (uniform)
+            alpha = 1.f;
+            pr = 0.f;
+        } else {
+            alpha = fast_exp2(m - mn);
+            pr = fast_exp2(s - mn);
+        }
+        m = mn;
+        lsum = lsum * alpha + pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+        // ---- p·V ------------------------------------------------------------
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float pb = __shfl(pr, (lane & ~(LPR - 1)) | i, 64);
+            acc[0] += pb * KV::lo(vr[i].x);
+            acc[1] += pb * KV::hi(vr[i].x);
+            acc[2] += pb * KV::lo(vr[i].y);
+            acc[3] += pb * KV::hi(vr[i].y);
+            acc[4] += pb * KV::lo(vr[i].z);
+            acc[5] += pb * KV::hi(vr[i].z);
+            acc[6] += pb * KV::lo(vr[i].w);
+            acc[7] += pb * KV::hi(vr[i].w);
+        }
+    }
+
+    // ---- fold the wavefront's rows, then the workgroup's waves -------------
+    lsum = wave_sum(lsum);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int msk = LPR; msk < 64; msk <<= 1) acc[e] += __shfl_xor(acc[e], msk, 64);
+    }
+    if (lane == 0) {
+        sm_m[wave] = m;
+        sm_l[wave] = lsum;
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_acc[wave][c * 8 + e] = acc[e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w]);
+    float wt[NW];
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        wt[w] = sm_m[w] == -INFINITY ? 0.f : fast_exp2(sm_m[w] - M);
+        tot += wt[w] * sm_l[w];
+    }
+    float o[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += wt[w] * sm_acc[w][lane * DPL + k];
+        o[k] = tot > 0.f ? t / tot : 0.f;
+    }
+    const size_t sh = (size_t)seq * Hq + head;
+    if (nparts <= 1) {
+        const size_t base = sh * D + (size_t)lane * DPL;
+        if constexpr (DPL == 2) {
+            OUT::store2(a.out, base, o[0], o[1]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) OUT::store(a.out, base + k, o[k]);
+        }
+    } else {
+        const size_t pidx = sh * a.max_partitions + part;
+        float* po = a.part_out + pidx * D + (size_t)lane * DPL;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) po[k] = o[k];
+        if (lane == 0) {
+            a.part_max[pidx] = M * kLn2;  // natural-log units
+            a.part_sum[pidx] = tot;
+        }
+    }
+}
+
+struct MergeArgs {
+    void* out;
+    const float* part_out;
+    const float* part_max;
+    const float* part_sum;
+    const int32_t* context_lens;
+    int num_seqs;
+    int num_heads;
+    int max_partitions;
+    int partition_size;
+};
+
+// One wavefront per (sequence, head): combine that head's partitions.
+template <class OUT, int D>
+__global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
+    constexpr int DPL = D / 64;
+    const int lane = threadIdx.x;
+    const int sh = blockIdx.x;
+    const int seq = sh / a.num_heads;
+    int L = a.context_lens[seq];
+    if (L < 0) L = 0;
+    int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
+    if (np > a.max_partitions) np = a.max_partitions;
+    if (np <= 1) return;
+    const float* pm = a.part_max + (size_t)sh * a.max_partitions;
+    const float* ps = a.part_sum + (size_t)sh * a.max_partitions;
+    const float* po = a.part_out + (size_t)sh * a.max_partitions * D + (size_t)lane * DPL;
+    float M = -INFINITY;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, pm[p]);
+    float tot = 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+    for (int p = 0; p < np; ++p) {
+        const float mp = pm[p];
+        const float w = mp == -INFINITY ? 0.f : ps[p] * fast_exp2((mp - M) * kLog2e);
+        tot += w;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[k] += w * po[(size_t)p * D + k];
+    }
+    const size_t base = (size_t)sh * D + (size_t)lane * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) OUT::store(a.out, base + k, tot > 0.f ? o[k] / tot : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Host dispatch
+// ---------------------------------------------------------------------------
+
+typedef void (*attn_fn)(AttnArgs);
+typedef void (*merge_fn)(MergeArgs);
+
+template <class KV, class OUT, int D>
+attn_fn pick_attn_bs(int bs) {
+    switch (bs) {
+        case 16: return attn_partition_kernel<KV, OUT, D, 16, kWaves>;
+        case 32: return attn_partition_kernel<KV, OUT, D, 32, kWaves>;
+    }
+    return nullptr;
+}
+
+template <class KV, class OUT>
+attn_fn pick_attn_d(int d, int bs) {
+    switch (d) {
+        case 64: return pick_attn_bs<KV, OUT, 64>(bs);
+        case 128: return pick_attn_bs<KV, OUT, 128>(bs);
+    }
+    return nullptr;
+}
+
+template <class KV>
+attn_fn pick_attn_out(pa_dtype out, pa_dtype kv, int d, int bs) {
+    if (out == PA_F32) return pick_attn_d<KV, OutF32>(d, bs);
+    if (out != kv) return nullptr;
+    if (kv == PA_F16) return pick_attn_d<KV, OutF16>(d, bs);
+    return pick_attn_d<KV, OutBF16>(d, bs);
+}
+
+attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs) {
+    if (kv == PA_F16) return pick_attn_out<KvF16>(out, kv, d, bs);
+    if (kv == PA_BF16) return pick_attn_out<KvBF16>(out, kv, d, bs);
+    return nullptr;
+}
+
+template <class OUT>
+merge_fn pick_merge_d(int d) {
+    switch (d) {
+        case 64: return lse_merge_kernel<OUT, 64>;
+        case 128: return lse_merge_kernel<OUT, 128>;
+    }
+    return nullptr;
+}
+
+merge_fn pick_merge(pa_dtype out, int d) {
+    switch (out) {
+        case PA_F32: return pick_merge_d<OutF32>(d);
+        case PA_F16: return pick_merge_d<OutF16>(d);
+        case PA_BF16: return pick_merge_d<OutBF16>(d);
+    }
+    return nullptr;
+}
+
+struct DecodeShape {
+    int num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        num_blocks;
+};
+
+pa_status validate_decode(void* out, pa_dtype out_dtype, const void* query, const void* kc,
+                          const void* vc, const int32_t* bt, const int32_t* cl,
+                          const DecodeShape& s, float scale, pa_dtype kv_dtype) {
+    PA_REQUIRE(s.num_seqs >= 0, PA_ERR_SHAPE, "num_seqs %d < 0", s.num_seqs);
+    PA_REQUIRE(s.num_heads > 0 && s.num_kv_heads > 0, PA_ERR_SHAPE,
+               "num_heads and num_kv_heads must be > 0");
+    PA_REQUIRE(s.num_heads % s.num_kv_heads == 0, PA_ERR_SHAPE,
+               "num_heads %d is not a multiple of num_kv_heads %d", s.num_heads,
+               s.num_kv_heads);
+    PA_REQUIRE(s.block_size > 0 && s.max_blocks_per_seq > 0 && s.num_blocks > 0,
+               PA_ERR_SHAPE, "block_size, max_blocks_per_seq, num_blocks must be > 0");
+    PA_REQUIRE((int64_t)s.max_blocks_per_seq * s.block_size <= (int64_t)1 << 30, PA_ERR_SHAPE,
+               "max_blocks_per_seq * block_size too large");
+    PA_REQUIRE(kv_dtype == PA_F16 || kv_dtype == PA_BF16, PA_ERR_DTYPE,
+               "kv dtype must be PA_F16 or PA_BF16");
+    PA_REQUIRE(out_dtype == PA_F32 || out_dtype == kv_dtype, PA_ERR_DTYPE,
+               "out dtype must be PA_F32 or the kv dtype");
+    PA_REQUIRE(isfinite(scale), PA_ERR_SHAPE, "scale must be finite");
+    PA_REQUIRE(s.head_dim == 64 || s.head_dim == 128, PA_ERR_UNSUPPORTED,
+               "head_dim %d not in {64, 128}", s.head_dim);
+    PA_REQUIRE(s.block_size == 16 || s.block_size == 32, PA_ERR_UNSUPPORTED,
+               "block_size %d not in {16, 32}", s.block_size);
+    if (s.num_seqs == 0) return PA_OK;
+    PA_REQUIRE(out && query && kc && vc && bt && cl, PA_ERR_NULL, "null pointer argument");
+    PA_REQUIRE(aligned16(out) && aligned16(query) && aligned16(kc) && aligned16(vc),
+               PA_ERR_ALIGNMENT, "out, query and caches must be 16-byte aligned");
+    return PA_OK;
+}
+
+AttnArgs make_args(void* out, const void* query, const void* kc, const void* vc,
+                   const int32_t* bt, const int32_t* cl, const DecodeShape& s, float scale) {
+    AttnArgs a{};
+    a.out = out;
+    a.query = (const uint16_t*)query;
+    a.key_cache = (const uint16_t*)kc;
+    a.value_cache = (const uint16_t*)vc;
+    a.block_tables = bt;
+    a.context_lens = cl;
+    a.num_seqs = s.num_seqs;
+    a.num_heads = s.num_heads;
+    a.num_kv_heads = s.num_kv_heads;
+    a.max_blocks_per_seq = s.max_blocks_per_seq;
+    a.num_blocks = s.num_blocks;
+    a.scale_log2 = scale * kLog2e;
+    return a;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SplitLayout {
+    int np;
+    size_t off_max, off_sum, off_out, total;
+};
+
+bool split_layout(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
+                  int block_size, int partition_size, SplitLayout* lay) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+        block_size <= 0 || partition_size <= 0)
+        return false;
+    const int64_t lmax = (int64_t)max_blocks_per_seq * block_size;
+    const int np = (int)((lmax + partition_size - 1) / partition_size);
+    const size_t rows = (size_t)num_seqs * num_heads * np;
+    lay->np = np;
+    lay->off_max = 0;
+    lay->off_sum = align256(rows * sizeof(float));
+    lay->off_out = lay->off_sum + align256(rows * sizeof(float));
+    lay->total = lay->off_out + align256(rows * head_dim * sizeof(float));
+    return true;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
+                               const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               float scale, pa_dtype kv_dtype, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                   context_lens, s, scale, kv_dtype);
+    if (st != PA_OK || num_seqs == 0) return st;
+    attn_fn fn = pick_attn(kv_dtype, out_dtype, head_dim, block_size);
+    PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
+                           scale);
+    a.partition_size = max_blocks_per_seq * block_size;  // one partition per sequence
+    a.max_partitions = 1;
+    const int64_t grid = (int64_t)num_seqs * num_heads;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+    return check_launch("pa_decode");
+}
+
+extern "C" size_t pa_decode_split_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                                  int max_blocks_per_seq, int block_size,
+                                                  int partition_size) {
+    SplitLayout lay;
+    if (!split_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
+                      partition_size, &lay))
+        return 0;
+    return lay.total;
+}
+
+extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
+                                     const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int max_blocks_per_seq, int num_blocks,
+                                     float scale, pa_dtype kv_dtype, int partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                   context_lens, s, scale, kv_dtype);
+    if (st != PA_OK) return st;
+    PA_REQUIRE(partition_size > 0 && partition_size % block_size == 0, PA_ERR_SHAPE,
+               "partition_size %d must be a positive multiple of block_size %d",
+               partition_size, block_size);
+    if (num_seqs == 0) return PA_OK;
+    SplitLayout lay;
+    split_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
+                 &lay);
+    PA_REQUIRE(workspace, PA_ERR_WORKSPACE, "workspace is NULL");
+    PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PA_ERR_WORKSPACE,
+               "workspace must be 256-byte aligned");
+    PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
+               "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+    attn_fn fn = pick_attn(kv_dtype, out_dtype, head_dim, block_size);
+    merge_fn mfn = pick_merge(out_dtype, head_dim);
+    PA_REQUIRE(fn && mfn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    char* ws = (char*)workspace;
+    AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
+                           scale);
+    a.part_max = (float*)(ws + lay.off_max);
+    a.part_sum = (float*)(ws + lay.off_sum);
+    a.part_out = (float*)(ws + lay.off_out);
+    a.partition_size = partition_size;
+    a.max_partitions = lay.np;
+    const int64_t grid = (int64_t)num_seqs * num_heads * lay.np;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+    st = check_launch("pa_decode_split (partitions)");
+    if (st != PA_OK) return st;
+    MergeArgs m{out, a.part_out, a.part_max, a.part_sum, context_lens,
+                num_seqs, num_heads, lay.np, partition_size};
+    hipLaunchKernelGGL(mfn, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
+                       (hipStream_t)stream, m);
+    return check_launch("pa_decode_split (merge)");
+}
+
+extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,
+                                  const float* part_max, const float* part_sum,
+                                  const int32_t* context_lens, int num_seqs, int num_heads,
+                                  int head_dim, int max_partitions, int partition_size,
+                                  void* stream) {
+    clear_error();
+    PA_REQUIRE(num_seqs >= 0 && num_heads > 0 && max_partitions > 0 && partition_size > 0,
+               PA_ERR_SHAPE, "invalid sizes");
+    PA_REQUIRE(head_dim == 64 || head_dim == 128, PA_ERR_UNSUPPORTED,
+               "head_dim %d not in {64, 128}", head_dim);
+    PA_REQUIRE(out_dtype == PA_F32 || out_dtype == PA_F16 || out_dtype == PA_BF16,
+               PA_ERR_DTYPE, "invalid out dtype");
+    if (num_seqs == 0) return PA_OK;
+    PA_REQUIRE(out && part_out && part_max && part_sum && context_lens, PA_ERR_NULL,
+               "null pointer argument");
+    PA_REQUIRE(aligned16(out) && aligned16(part_out), PA_ERR_ALIGNMENT,
+               "out and part_out must be 16-byte aligned");
+    merge_fn mfn = pick_merge(out_dtype, head_dim);
+    PA_REQUIRE(mfn, PA_ERR_UNSUPPORTED, "no merge instance");
+    MergeArgs m{out, part_out, part_max, part_sum, context_lens,
+                num_seqs, num_heads, max_partitions, partition_size};
+    hipLaunchKernelGGL(mfn, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
+                       (hipStream_t)stream, m);
+    return check_launch("pa_lse_merge");
+}

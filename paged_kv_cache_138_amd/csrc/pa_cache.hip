@@ -1,0 +1,77 @@
+// pa_reshape_and_cache: scatter each new token's K/V rows into its cache
+// slot ("vLLM PagedAttention深度解析与工程实践" §二, per-step KV append;
+// lqnn.cn/news/170268 §2.2, write into the current block's free slot).
+//
+// One work item moves one 16-byte piece (8 elements) of one token's K row
+// and the matching piece of its V row; consecutive work items cover
+// consecutive pieces of the same token, so both the reads of key/value and
+// the writes into the slot's [num_kv_heads, head_dim] row are coalesced.
+#include "pa_device.h"
+#include "pa_host.h"
+
+namespace pa {
+namespace {
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int64_t key_stride,
+    int64_t value_stride, int pieces_per_token, int64_t num_slots) {
+    const int64_t total = (int64_t)num_tokens * pieces_per_token;
+    const int64_t row_elems = (int64_t)pieces_per_token * 8;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tok = idx / pieces_per_token;
+        const int64_t piece = idx - tok * pieces_per_token;
+        const int64_t slot = slot_mapping[tok];
+        if (slot < 0 || slot >= num_slots) continue;  // padding, or outside the cache
+        // slot = block * block_size + row, and rows are dense inside a block,
+        // so the destination row is simply `slot` rows into the cache
+        const int64_t dst = slot * row_elems + piece * 8;
+        const u32x4 k = *(const u32x4*)(key + tok * key_stride + piece * 8);
+        const u32x4 v = *(const u32x4*)(value + tok * value_stride + piece * 8);
+        *(u32x4*)(key_cache + dst) = k;
+        *(u32x4*)(value_cache + dst) = v;
+    }
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                          void* value_cache, const int64_t* slot_mapping,
+                                          int num_tokens, int64_t key_token_stride,
+                                          int64_t value_token_stride, int num_kv_heads,
+                                          int head_dim, int num_blocks, int block_size,
+                                          pa_dtype dtype, void* stream) {
+    using namespace pa;
+    clear_error();
+    PA_REQUIRE(num_tokens >= 0, PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+    PA_REQUIRE(num_kv_heads > 0 && head_dim > 0 && num_blocks > 0 && block_size > 0,
+               PA_ERR_SHAPE, "num_kv_heads, head_dim, num_blocks, block_size must be > 0");
+    PA_REQUIRE(dtype == PA_F16 || dtype == PA_BF16, PA_ERR_DTYPE,
+               "cache dtype must be PA_F16 or PA_BF16");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    PA_REQUIRE(row % 8 == 0, PA_ERR_UNSUPPORTED,
+               "num_kv_heads * head_dim must be a multiple of 8");
+    PA_REQUIRE(key_token_stride >= row && value_token_stride >= row, PA_ERR_SHAPE,
+               "token strides must be >= num_kv_heads * head_dim");
+    PA_REQUIRE(key_token_stride % 8 == 0 && value_token_stride % 8 == 0, PA_ERR_ALIGNMENT,
+               "token strides must be multiples of 8 elements");
+    if (num_tokens == 0) return PA_OK;
+    PA_REQUIRE(key && value && key_cache && value_cache && slot_mapping, PA_ERR_NULL,
+               "null pointer argument");
+    PA_REQUIRE(aligned16(key) && aligned16(value) && aligned16(key_cache) &&
+                   aligned16(value_cache),
+               PA_ERR_ALIGNMENT, "K/V and cache pointers must be 16-byte aligned");
+    const int pieces = (int)(row / 8);
+    const int64_t total = (int64_t)num_tokens * pieces;
+    int64_t grid = (total + 255) / 256;
+    if (grid > 1 << 20) grid = 1 << 20;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, (const uint16_t*)key, (const uint16_t*)value,
+                       (uint16_t*)key_cache, (uint16_t*)value_cache, slot_mapping, num_tokens,
+                       key_token_stride, value_token_stride, pieces,
+                       (int64_t)num_blocks * block_size);
+    return check_launch("pa_reshape_and_cache");
+}

@@ -1,0 +1,122 @@
+"""One decode step on the GPU, as the benchmark times it.
+
+A step appends the new token's K/V into its slot (pa_reshape_and_cache),
+then runs paged decode attention over every sequence's context, the new
+token included (append first, then attend: "vLLM PagedAttention深度解析与
+工程实践" §二). Attention uses the split path (partitions + log-sum-exp
+merge) with the workload's partition size, or the single-launch path when
+`split` is False.
+"""
+
+import numpy as np
+import torch
+
+from . import lib as palib
+
+_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_device_tensor(arr, dtype, device):
+    """Host array (fp16, or bf16 as uint16 bits) -> GPU tensor of `dtype`."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device)
+
+
+def to_host_bits(t):
+    """GPU fp16/bf16 tensor -> host uint16 bit patterns."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def to_host_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class DeviceBatch:
+    """GPU copies of a workloads.Batch plus the step's output buffers."""
+
+    def __init__(self, batch, device="cuda", out_dtype=None, split=True, partition_size=None):
+        w = batch.workload
+        self.batch = batch
+        self.device = device
+        dt = w.dtype
+        self.query = to_device_tensor(batch.query, dt, device)
+        self.key_cache = to_device_tensor(batch.key_cache, dt, device)
+        self.value_cache = to_device_tensor(batch.value_cache, dt, device)
+        self.new_key = to_device_tensor(batch.new_key, dt, device)
+        self.new_value = to_device_tensor(batch.new_value, dt, device)
+        self.block_tables = torch.from_numpy(batch.block_tables).to(device)
+        self.context_lens = torch.from_numpy(batch.context_lens).to(device)
+        self.slot_mapping = torch.from_numpy(batch.slot_mapping).to(device)
+        self.scale = batch.scale
+        self.split = split
+        self.partition_size = partition_size or w.partition_size
+        B, Hq, D = self.query.shape
+        od = out_dtype if out_dtype is not None else self.query.dtype
+        self.out = torch.empty((B, Hq, D), dtype=od, device=device)
+        self.workspace = None
+        if split:
+            self.workspace = palib.make_workspace(B, Hq, D, self.block_tables.shape[1],
+                                                  w.block_size, self.partition_size, device)
+
+    def write_cache(self):
+        palib.reshape_and_cache(self.new_key, self.new_value, self.key_cache, self.value_cache,
+                                self.slot_mapping)
+
+    def attend(self):
+        if self.split:
+            palib.decode_split(self.query, self.key_cache, self.value_cache, self.block_tables,
+                               self.context_lens, self.scale, self.partition_size,
+                               workspace=self.workspace, out=self.out)
+        else:
+            palib.decode(self.query, self.key_cache, self.value_cache, self.block_tables,
+                         self.context_lens, self.scale, out=self.out)
+        return self.out
+
+    def step(self):
+        self.write_cache()
+        return self.attend()
+
+
+class RotatedBatch(DeviceBatch):
+    """A copy of a DeviceBatch whose allocated blocks are moved, in a new
+    random physical order, into a compact pool of their own.
+
+    The logical content of every sequence is unchanged, so the outputs are
+    bit-identical to the source batch's; timing loops cycle through several
+    such copies so that no step finds the previous step's cache blocks in
+    the GPU's last-level cache.
+    """
+
+    def __init__(self, src, seed):  # noqa: D401 - no DeviceBatch.__init__
+        self.batch = src.batch
+        self.device = src.device
+        self.query, self.new_key, self.new_value = src.query, src.new_key, src.new_value
+        self.context_lens = src.context_lens
+        self.scale = src.scale
+        self.split = src.split
+        self.partition_size = src.partition_size
+        bt = src.block_tables
+        used = torch.unique(bt[bt >= 0])
+        n = int(used.numel())
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        perm = torch.randperm(n, generator=g).to(src.device)
+        remap = torch.full((src.key_cache.shape[0],), -1, dtype=torch.int64, device=src.device)
+        remap[used] = perm
+        shape = (n,) + tuple(src.key_cache.shape[1:])
+        self.key_cache = torch.empty(shape, dtype=src.key_cache.dtype, device=src.device)
+        self.value_cache = torch.empty_like(self.key_cache)
+        self.key_cache[perm] = src.key_cache[used]
+        self.value_cache[perm] = src.value_cache[used]
+        self.block_tables = torch.where(bt >= 0, remap[bt.clamp(min=0).long()],
+                                        torch.full_like(bt, -1, dtype=torch.int64)).to(torch.int32)
+        BS = self.key_cache.shape[1]
+        sm = src.slot_mapping
+        blk = torch.div(sm.clamp(min=0), BS, rounding_mode="floor")
+        self.slot_mapping = torch.where(sm >= 0, remap[blk] * BS + sm.clamp(min=0) % BS, sm)
+        self.out = torch.empty_like(src.out)
+        self.workspace = None if src.workspace is None else torch.empty_like(src.workspace)

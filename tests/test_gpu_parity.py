@@ -1,0 +1,302 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: the cache scatter and block-table indexing are bit-exact; attention
+outputs are within 2e-3 max-abs of the oracle with fp32 outputs, and within
+2e-3 plus one unit in the last place of the output type for fp16 / bf16
+outputs (a correctly rounded bf16 value already differs from the exact one by
+up to half an ulp, 3.9e-3 in [1, 2)).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_138_amd import lib as palib
+from paged_kv_cache_138_amd import workloads as W
+from paged_kv_cache_138_amd.pipeline import DeviceBatch, to_device_tensor, to_host_bits, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_present():
+    assert os.path.exists(palib.LIB_PATH), "libpa.so must be built before the GPU tests"
+    palib.load()
+
+
+def _ulp(x, dtype):
+    a = np.maximum(np.abs(x), 2.0 ** -14)
+    mant = {"f16": 10, "bf16": 7}[dtype]
+    return 2.0 ** (np.floor(np.log2(a)) - mant)
+
+
+def _assert_close(got, ref, out_dtype, what=""):
+    assert np.isfinite(got).all(), "non-finite output " + what
+    err = np.abs(got - ref)
+    if out_dtype == "f32":
+        bound = ATOL
+    else:
+        bound = ATOL + _ulp(ref, out_dtype)
+    bad = err > bound
+    assert not bad.any(), "%s: max err %.3g at %s (bound %s)" % (
+        what, err.max(), np.unravel_index(np.argmax(err), err.shape), out_dtype)
+
+
+def _oracle_step(b, partition=None):
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    return kc, vc, oracle.decode(b.query, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype)
+
+
+def _small(name="s", **kw):
+    return W.custom_workload(name, **kw)
+
+
+SMALL_CASES = [
+    dict(num_seqs=5, num_heads=8, num_kv_heads=8, head_dim=64, dtype="f16", block_size=16,
+         num_blocks=96, max_blocks_per_seq=16, lens="uniform:1:256"),
+    dict(num_seqs=5, num_heads=4, num_kv_heads=4, head_dim=128, dtype="bf16", block_size=16,
+         num_blocks=160, max_blocks_per_seq=32, lens="uniform:1:500"),
+    dict(num_seqs=4, num_heads=8, num_kv_heads=2, head_dim=128, dtype="f16", block_size=32,
+         num_blocks=96, max_blocks_per_seq=24, lens="uniform:1:700"),
+    dict(num_seqs=3, num_heads=16, num_kv_heads=2, head_dim=128, dtype="bf16", block_size=16,
+         num_blocks=200, max_blocks_per_seq=64, lens="uniform:200:1000"),
+    dict(num_seqs=6, num_heads=4, num_kv_heads=1, head_dim=64, dtype="bf16", block_size=32,
+         num_blocks=64, max_blocks_per_seq=8, lens="uniform:1:256"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("out_kind", ["f32", "native"])
+def test_decode_step_matches_oracle_small(case, split, out_kind):
+    w = _small("small%d" % case, **SMALL_CASES[case])
+    b = W.make_batch(w, seed=100 + case, unallocated="nan")
+    out_dtype = torch.float32 if out_kind == "f32" else None
+    db = DeviceBatch(b, out_dtype=out_dtype, split=split, partition_size=64 if split else None)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    # the scatter is bit-exact over the whole cache
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, "f32" if out_kind == "f32" else w.dtype,
+                  "case %d split=%s" % (case, split))
+
+
+def test_tiny_workload_in_full():
+    b = W.make_batch(W.WORKLOADS["tiny"], seed=0, unallocated="nan")
+    for split in (False, True):
+        for od in (torch.float32, None):
+            db = DeviceBatch(b, out_dtype=od, split=split)
+            out = db.step()
+            torch.cuda.synchronize()
+            kc, vc, ref = _oracle_step(b)
+            assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+            _assert_close(to_host_f64(out), ref, "f32" if od is not None else "f16", "tiny")
+
+
+@pytest.mark.parametrize("part", [16, 32, 48, 64, 256, 512, 1024])
+def test_split_partition_sizes(part):
+    w = _small("sp", num_seqs=4, num_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16",
+               block_size=16, num_blocks=300, max_blocks_per_seq=80, lens="uniform:1:1280")
+    b = W.make_batch(w, seed=7, lens=[1, 17, 600, 1280])
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=part)
+    out = db.step()
+    torch.cuda.synchronize()
+    _, _, ref = _oracle_step(b)
+    _assert_close(to_host_f64(out), ref, "f32", "partition %d" % part)
+
+
+def test_edge_lengths_and_zero_context():
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 511, 512, 513]
+    w = _small("edge", num_seqs=len(lens), num_heads=2, num_kv_heads=2, head_dim=128, dtype="f16",
+               block_size=16, num_blocks=300, max_blocks_per_seq=40, lens="fixed:1")
+    b = W.make_batch(w, seed=9, lens=lens, unallocated="nan")
+    for split in (False, True):
+        db = DeviceBatch(b, out_dtype=torch.float32, split=split, partition_size=128)
+        out = db.step()
+        torch.cuda.synchronize()
+        _, _, ref = _oracle_step(b)
+        got = to_host_f64(out)
+        assert np.all(got[0] == 0.0)
+        _assert_close(got, ref, "f32", "edge split=%s" % split)
+
+
+def test_single_token_returns_value_row_exactly():
+    w = _small("one", num_seqs=3, num_heads=4, num_kv_heads=2, head_dim=64, dtype="bf16",
+               block_size=16, num_blocks=8, max_blocks_per_seq=2, lens="fixed:1")
+    b = W.make_batch(w, seed=3)
+    for split in (False, True):
+        for od in (torch.float32, torch.bfloat16):
+            db = DeviceBatch(b, out_dtype=od, split=split)
+            out = db.step()
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy()
+            v = oracle.upcast(b.new_value, "bf16")
+            for i in range(3):
+                for h in range(4):
+                    assert np.array_equal(got[i, h], v[i, h // 2].astype(np.float32))
+
+
+def _selector_batch(dtype, D, BS, lens, G=1, seed=5):
+    """q and K built from exactly representable values so that one logical
+    token j per sequence wins by a scaled logit gap > 700: exp of every other
+    score underflows to 0 in fp32 and the output equals V_j bit-exactly.
+    V rows hold distinct non-zero integers (seq, token, dim)."""
+    Hkv = 2
+    Hq = Hkv * G
+    w = _small("sel", num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=D, dtype=dtype,
+               block_size=BS, num_blocks=256, max_blocks_per_seq=64, lens="fixed:1")
+    b = W.make_batch(w, seed=seed, lens=lens)
+    rng = np.random.default_rng(seed)
+    enc = lambda x: W.encode(np.asarray(x, np.float32), dtype)
+    q = np.zeros((len(lens), Hq, D), np.float32)
+    q[:, :, :4] = 64.0
+    b.query[...] = enc(q)
+    winners = []
+    for i, L in enumerate(lens):
+        j = int(rng.integers(0, L))
+        winners.append(j)
+        for t in range(L):
+            s = oracle.slot_of_token(b.block_tables[i], t, BS)
+            blk, off = divmod(s, BS)
+            krow = np.zeros((Hkv, D), np.float32)
+            krow[:, :4] = 64.0 if t == j else -64.0
+            vrow = (np.arange(D, dtype=np.float32)[None, :] % 50 + 1 + (t % 50) * 0.5 + i) * (1 + np.arange(Hkv)[:, None])
+            if t == L - 1:
+                b.new_key[i] = enc(krow)
+                b.new_value[i] = enc(vrow)
+            else:
+                b.key_cache[blk, off] = enc(krow)
+                b.value_cache[blk, off] = enc(vrow)
+    return b, winners
+
+
+@pytest.mark.parametrize("dtype,D,BS,G", [("f16", 128, 16, 1), ("bf16", 64, 32, 1),
+                                          ("bf16", 128, 16, 8), ("f16", 64, 16, 4)])
+def test_selector_pins_block_table_indexing_bit_exactly(dtype, D, BS, G):
+    lens = [1, 5, BS, BS + 3, 100, 257, 700]
+    b, winners = _selector_batch(dtype, D, BS, lens, G)
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    for split in (False, True):
+        db = DeviceBatch(b, out_dtype=torch.float32, split=split, partition_size=64)
+        out = db.step()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i, j in enumerate(winners):
+            s = oracle.slot_of_token(b.block_tables[i], j, b.workload.block_size)
+            blk, off = divmod(s, b.workload.block_size)
+            vj = oracle.upcast(vc[blk, off], dtype)
+            for h in range(b.query.shape[1]):
+                assert np.array_equal(got[i, h], vj[h // G].astype(np.float32)), (i, h, split)
+
+
+def test_physical_permutation_gives_identical_bits():
+    w = _small("perm", num_seqs=6, num_heads=8, num_kv_heads=4, head_dim=128, dtype="f16",
+               block_size=16, num_blocks=400, max_blocks_per_seq=40, lens="uniform:1:640")
+    b = W.make_batch(w, seed=21)
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    # permute physical blocks: block p moves to perm[p]
+    perm = np.random.default_rng(1).permutation(w.num_blocks)
+    kc2 = np.empty_like(kc)
+    vc2 = np.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    bt2 = np.where(b.block_tables >= 0, perm[np.maximum(b.block_tables, 0)], -1).astype(np.int32)
+    outs = []
+    for (K, V, BT) in ((kc, vc, b.block_tables), (kc2, vc2, bt2)):
+        for split in (False, True):
+            o = palib.decode_split if split else palib.decode
+            args = (to_device_tensor(b.query, "f16", "cuda"), to_device_tensor(K, "f16", "cuda"),
+                    to_device_tensor(V, "f16", "cuda"), torch.from_numpy(BT).cuda(),
+                    torch.from_numpy(b.context_lens).cuda(), b.scale)
+            outs.append(o(*args, out_dtype=torch.float32).cpu().numpy())
+    assert np.array_equal(outs[0], outs[2])
+    assert np.array_equal(outs[1], outs[3])
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    w = _small("share", num_seqs=5, num_heads=4, num_kv_heads=4, head_dim=128, dtype="f16",
+               block_size=32, num_blocks=300, max_blocks_per_seq=40, lens="uniform:1:300",
+               shared_prefix_tokens=256, long_seqs=1, long_len=1200)
+    b = W.make_batch(w, seed=4)
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    # private copies: give every sequence its own copy of the prefix blocks
+    B = b.block_tables.shape[0]
+    free = [x for x in range(w.num_blocks) if x not in set(b.block_tables[b.block_tables >= 0].tolist())]
+    kc2, vc2, bt2 = kc.copy(), vc.copy(), b.block_tables.copy()
+    for i in range(B):
+        for j, blk in enumerate(b.shared_blocks):
+            nb = free.pop()
+            kc2[nb] = kc[blk]
+            vc2[nb] = vc[blk]
+            bt2[i, j] = nb
+    res = []
+    for K, V, BT in ((kc, vc, b.block_tables), (kc2, vc2, bt2)):
+        args = (to_device_tensor(b.query, "f16", "cuda"), to_device_tensor(K, "f16", "cuda"),
+                to_device_tensor(V, "f16", "cuda"), torch.from_numpy(BT).cuda(),
+                torch.from_numpy(b.context_lens).cuda(), b.scale)
+        res.append(palib.decode_split(*args, partition_size=256, out_dtype=torch.float32).cpu().numpy())
+    assert np.array_equal(res[0], res[1])
+    ref = oracle.decode(b.query, kc, vc, b.block_tables, b.context_lens, b.scale, "f16")
+    _assert_close(res[0].astype(np.float64), ref, "f32", "shared prefix")
+
+
+def test_nan_poisoned_tails_do_not_change_bits():
+    w = _small("nanp", num_seqs=6, num_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16",
+               block_size=16, num_blocks=128, max_blocks_per_seq=32, lens="uniform:1:400")
+    outs = []
+    for poison, unalloc in (("zero", "zero"), ("nan", "nan")):
+        b = W.make_batch(w, seed=12, poison=poison, unallocated=unalloc)
+        bt = b.block_tables.copy()
+        if poison == "nan":
+            bt[bt < 0] = 1 << 30  # padding entries past each table's end are never read
+        db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=64)
+        db.block_tables = torch.from_numpy(bt).cuda()
+        outs.append(db.step().cpu().numpy())
+    assert np.isfinite(outs[1]).all()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_exported_lse_merge_matches_oracle_merge():
+    w = _small("merge", num_seqs=4, num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16",
+               block_size=16, num_blocks=200, max_blocks_per_seq=48, lens="uniform:1:768")
+    b = W.make_batch(w, seed=2, lens=[0, 100, 513, 768])
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    m, l, o = oracle.decode_partitions(b.query, kc, vc, b.block_tables, b.context_lens, b.scale,
+                                       "f16", 128, max_partitions=6)
+    ref = oracle.lse_merge(m, l, o, b.context_lens, 128)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    out = torch.full((4, 4, 64), -7.0, device="cuda")
+    palib.lse_merge(dev(o), dev(m), dev(l), torch.from_numpy(b.context_lens).cuda(), 128, out=out)
+    got = out.cpu().numpy().astype(np.float64)
+    # sequences with <= 1 partition are left untouched by the merge
+    assert np.all(got[0] == -7.0) and np.all(got[1] == -7.0)
+    np.testing.assert_allclose(got[2:], ref[2:], rtol=0, atol=1e-5)
+
+
+def test_fused_qkv_strided_cache_write():
+    """K/V read straight out of a fused [T, 3, H, D] projection buffer."""
+    T, H, D, NB, BS = 9, 4, 64, 8, 16
+    rng = np.random.default_rng(0)
+    qkv = torch.from_numpy(rng.standard_normal((T, 3, H, D)).astype(np.float16)).cuda()
+    key, value = qkv[:, 1], qkv[:, 2]
+    sentinel = torch.full((NB, BS, H, D), 3.5, dtype=torch.float16, device="cuda")
+    kc, vc = sentinel.clone(), sentinel.clone()
+    slots = torch.tensor([5, -1, 17, 127, 0, 64, 65, -3, 100], dtype=torch.int64, device="cuda")
+    palib.reshape_and_cache(key, value, kc, vc, slots)
+    rk, rv = oracle.reshape_and_cache(key.cpu().numpy(), value.cpu().numpy(), sentinel.cpu().numpy(),
+                                      sentinel.cpu().numpy(), slots.cpu().numpy())
+    assert np.array_equal(kc.cpu().numpy().view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(vc.cpu().numpy().view(np.uint16), rv.view(np.uint16))
