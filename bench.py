@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--out-dtype", choices=["native", "f32"], default="native")
     ap.add_argument("--rotations", type=int, default=0, help="batch copies cycled (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--lens", default=None,
+                    help="override the context-length recipe (e.g. fixed:1094); not the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     return ap.parse_args()
@@ -111,6 +113,9 @@ def main():
 
     palib.load()  # fails loudly if libpa.so is missing
     w = W.WORKLOADS[args.workload]
+    if args.lens:
+        import dataclasses
+        w = dataclasses.replace(w, lens=args.lens, name=w.name + "+lens=" + args.lens)
     path = default_path(w) if args.path == "auto" else args.path
     t_gen = time.perf_counter()
     batch = W.make_batch(w, seed=args.seed)

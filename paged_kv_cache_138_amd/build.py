@@ -49,9 +49,11 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose=False, jobs=None):
-    """Compile every csrc/*.hip and link libpa.so. Always rebuilds."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose=False, jobs=None, extra_flags=(), out=None):
+    """Compile every csrc/*.hip and link libpa.so (or `out`). Always rebuilds."""
+    out = out or LIB
+    objdir = OBJDIR if out == LIB else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no sources under %s" % CSRC)
@@ -59,21 +61,25 @@ def build(verbose=False, jobs=None):
     objs = []
     cmds = []
     for s in srcs:
-        o = os.path.join(OBJDIR, os.path.basename(s) + ".o")
+        o = os.path.join(objdir, os.path.basename(s) + ".o")
         objs.append(o)
-        cmds.append([cc] + DEVICE_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o])
+        cmds.append([cc] + DEVICE_FLAGS + list(extra_flags) +
+                    ["-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o])
     jobs = jobs or min(8, len(cmds))
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--out", default=None, help="library path (default: in-tree libpa.so)")
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="extra preprocessor definition for a variant build")
     args = ap.parse_args()
-    print(build(verbose=args.verbose))
+    print(build(verbose=args.verbose, extra_flags=["-D" + d for d in args.defines], out=args.out))
     sys.exit(0)

@@ -50,7 +50,24 @@ struct AttnArgs {
     float scale_log2;  // scale * log2(e)
 };
 
-constexpr int kWaves = 4;
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+constexpr int kWaves = PA_WAVES;  // wavefronts per workgroup
+
+// One transpose-reduce step over groups of lanes: lanes whose index has
+// bit HALF set keep the upper half of their list, the others the lower half,
+// and each adds its partner's copy of the half it keeps.
+template <int HALF, int N>
+__device__ __forceinline__ void tr_step(float (&pd)[N], int c) {
+    const bool upper = (c & HALF) != 0;
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+        const float send = upper ? pd[k] : pd[k + HALF];
+        const float keep = upper ? pd[k + HALF] : pd[k];
+        pd[k] = keep + tr_partner<HALF>(send);
+    }
+}
 
 template <class KV, class OUT, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
@@ -63,13 +80,16 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
     constexpr int DPL = D / 64;         // output elements per lane in the epilogue
     static_assert(CHUNK == 64, "one score per lane per chunk");
     static_assert(BS % RPI == 0 && CHUNK % BS == 0, "block must tile the chunk");
+    static_assert(LPR == 8 || LPR == 16, "head_dim 64 or 128");
 
     __shared__ float sm_m[NW];
     __shared__ float sm_l[NW];
     __shared__ float sm_acc[NW][D];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // the wave index is uniform inside a wavefront; saying so keeps every
+    // chunk, block-table and address computation in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;  // row within a load instruction
     const int c = lane % LPR;  // 8-element slice of the row
 
@@ -91,11 +111,15 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
     const int nb = (L + BS - 1) / BS;
 
     const int kvh = head / (Hq / a.num_kv_heads);
-    const size_t row_stride = (size_t)a.num_kv_heads * D;  // elements
-    const size_t block_stride = row_stride * BS;
-    const uint16_t* kc = a.key_cache + (size_t)kvh * D + c * 8;
-    const uint16_t* vc = a.value_cache + (size_t)kvh * D + c * 8;
+    const size_t row_bytes = (size_t)a.num_kv_heads * D * 2;
+    const size_t block_bytes = row_bytes * BS;
+    const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
+    const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    // byte offsets, inside a block, of the rows this lane reads
+    uint32_t loff[IPB];
+#pragma unroll
+    for (int j = 0; j < IPB; ++j) loff[j] = (uint32_t)((j * RPI + r) * row_bytes + c * 16);
 
     const u32x4 q = *(const u32x4*)(a.query + ((size_t)seq * Hq + head) * D + c * 8);
 
@@ -105,38 +129,37 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
-    for (int cs = start + wave * CHUNK; cs < end; cs += NW * CHUNK) {
-        const int lb0 = cs / BS;
-        int phys[BPC];
-        bool pok[BPC];
+    // per-block load descriptors of the chunk starting at token cs: the
+    // range of each covers exactly the block's rows below `end`, so rows
+    // past the context and blocks past the table (or with an id outside the
+    // pool) read as zeros and are never fetched
+    struct ChunkIds {
+        __amdgpu_buffer_rsrc_t k[BPC], v[BPC];
+        bool ok[BPC];
+    };
+    auto fetch_ids = [&](int cs, ChunkIds& ci) {
 #pragma unroll
         for (int b = 0; b < BPC; ++b) {
-            const int lb = lb0 + b;
+            const int lb = cs / BS + b;
             const int pid = lb < nb ? bt[lb] : -1;
-            pok[b] = pid >= 0 && pid < a.num_blocks;
-            phys[b] = pok[b] ? pid : 0;
+            const int rows = min(max(end - (cs + b * BS), 0), BS);
+            const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
+            const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
+            const size_t boff = (size_t)(ok ? pid : 0) * block_bytes;
+            ci.k[b] = make_rsrc(kbase + boff, nrec);
+            ci.v[b] = make_rsrc(vbase + boff, nrec);
+            ci.ok[b] = ok;
         }
-        // ---- K rows of the chunk ------------------------------------------
-        u32x4 kr[NI];
+    };
+    auto issue = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[NI]) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int b = i / IPB;
-            const int row = (i % IPB) * RPI + r;
-            const bool ok = pok[b] && (cs + b * BS + row) < end;
-            const size_t off = (size_t)phys[b] * block_stride + (size_t)row * row_stride;
-            kr[i] = ok ? *(const u32x4*)(kc + off) : u32x4{0u, 0u, 0u, 0u};
-        }
-        // ---- V rows (issued early, used after the softmax update) --------
-        u32x4 vr[NI];
+        for (int b = 0; b < BPC; ++b) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int b = i / IPB;
-            const int row = (i % IPB) * RPI + r;
-            const bool ok = pok[b] && (cs + b * BS + row) < end;
-            const size_t off = (size_t)phys[b] * block_stride + (size_t)row * row_stride;
-            vr[i] = ok ? *(const u32x4*)(vc + off) : u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < IPB; ++j) buf[b * IPB + j] = buffer_load16(rs[b], loff[j]);
         }
-        // ---- partial dots over this lane's 8 elements ---------------------
+    };
+    // scores of the chunk's 64 tokens, one per lane (log2 units, -inf if absent)
+    auto scores = [&](const u32x4 (&kr)[NI], int cs, const bool (&pok)[BPC]) -> float {
         float pd[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -145,31 +168,25 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
             t = KV::dot2(kr[i].z, q.z, t);
             pd[i] = KV::dot2(kr[i].w, q.w, t);
         }
-        // ---- transpose-reduce across the LPR lanes of each row group -------
-        // after the step with mask `half`, a lane keeps the half of its list
-        // selected by bit `half` of c; at the end lane c owns load c.
-#pragma unroll
-        for (int half = NI / 2; half >= 1; half >>= 1) {
-            const bool upper = (c & half) != 0;
-#pragma unroll
-            for (int k = 0; k < half; ++k) {
-                const float send = upper ? pd[k] : pd[k + half];
-                const float keep = upper ? pd[k + half] : pd[k];
-                pd[k] = keep + __shfl_xor(send, half, 64);
-            }
-        }
+        // lane c of each row group ends up with the full score of load c
+        if constexpr (NI >= 16) tr_step<8>(pd, c);
+        tr_step<4>(pd, c);
+        tr_step<2>(pd, c);
+        tr_step<1>(pd, c);
         const int myb = c / IPB;
         const int mytok = cs + myb * BS + (c % IPB) * RPI + r;
-        bool mok = pok[0];
+        bool ok = pok[0];
 #pragma unroll
         for (int b = 1; b < BPC; ++b)
-            if (myb == b) mok = pok[b];
-        mok = mok && mytok < end;
-        const float s = mok ? pd[0] * a.scale_log2 : -INFINITY;
-        // ---- online softmax update ----------------------------------------
+            if (myb == b) ok = pok[b];
+        ok = ok && mytok < end;
+        return ok ? pd[0] * a.scale_log2 : -INFINITY;
+    };
+    // online softmax update; returns this lane's weight exp2(s - m)
+    auto update = [&](float s) -> float {
         const float mn = fmaxf(m, wave_max(s));
         float alpha, pr;
-        if (mn == -INFINITY) {  // no valid token yet (uniform)
+        if (mn == -INFINITY) {  // nothing valid yet (uniform)
             alpha = 1.f;
             pr = 0.f;
         } else {
@@ -180,10 +197,13 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
         lsum = lsum * alpha + pr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-        // ---- p·V ------------------------------------------------------------
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const float pb = __shfl(pr, (lane & ~(LPR - 1)) | i, 64);
+        return pr;
+    };
+    // acc += Σ_rows weight(row) · V(row) for this lane's 8 elements
+    auto pv = [&](const u32x4 (&vr)[NI], float pr) {
+        static_for<0, NI>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            const float pb = group_bcast<LPR, i>(pr);
             acc[0] += pb * KV::lo(vr[i].x);
             acc[1] += pb * KV::hi(vr[i].x);
             acc[2] += pb * KV::lo(vr[i].y);
@@ -192,6 +212,33 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
             acc[5] += pb * KV::hi(vr[i].z);
             acc[6] += pb * KV::lo(vr[i].w);
             acc[7] += pb * KV::hi(vr[i].w);
+        });
+    };
+
+    // ---- chunks, software-pipelined: the next chunk's K is in flight during
+    // this chunk's p·V, and its V during the next score pass -----------------
+    int cs = start + wave * CHUNK;
+    if (cs < end) {
+        ChunkIds cur;
+        u32x4 kr[NI], vr[NI];
+        fetch_ids(cs, cur);
+        issue(cur.k, kr);
+        issue(cur.v, vr);
+        for (;;) {
+            const int nx = cs + NW * CHUNK;
+            const bool more = nx < end;
+            ChunkIds nxt;
+            if (more) fetch_ids(nx, nxt);
+            const float pr = update(scores(kr, cs, cur.ok));
+            if (!more) {
+                pv(vr, pr);
+                break;
+            }
+            issue(nxt.k, kr);
+            pv(vr, pr);
+            issue(nxt.v, vr);
+            cur = nxt;
+            cs = nx;
         }
     }
 

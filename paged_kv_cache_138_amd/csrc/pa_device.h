@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -106,10 +108,91 @@ __device__ __forceinline__ float fast_exp2(float x) {
     return __builtin_amdgcn_exp2f(x);
 }
 
+// DPP lane permutations inside 16-lane rows (CDNA DPP controls).
+namespace dpp {
+constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int kXor1 = quad_perm(1, 0, 3, 2);
+constexpr int kXor2 = quad_perm(2, 3, 0, 1);
+constexpr int kHalfMirror = 0x141;  // lane i of 8 <- lane 7-i
+constexpr int kRowRor8 = 0x128;     // lane i of 16 <- lane (i+8) mod 16
+constexpr int kRowNewBcast0 = 0x150;  // all 16 lanes of a row <- its lane n (0x150 + n)
+}  // namespace dpp
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Value of lane `src` of this lane's group of G lanes (G = 8 or 16).
+template <int G, int SRC>
+__device__ __forceinline__ float group_bcast(float v) {
+    static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+    if constexpr (G == 16) {
+        return dpp_mov<dpp::kRowNewBcast0 + SRC>(v);
+    } else {
+        // ds_swizzle bitmask mode over 32 lanes: lane = (lane & 0x18) | SRC
+        constexpr int pattern = 0x18 | (SRC << 5);
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), pattern));
+    }
+}
+
+// Partner lane for the transpose-reduce step that splits on bit `HALF` of
+// the lane's index inside its group. Steps run from the high bit down; any
+// pairing works that flips bit HALF while keeping the higher bits (those of
+// earlier steps), so row rotation by 8 and the half-row mirror serve for the
+// two high bits.
+template <int HALF>
+__device__ __forceinline__ float tr_partner(float v) {
+    if constexpr (HALF == 8) return dpp_mov<dpp::kRowRor8>(v);
+    else if constexpr (HALF == 4) return dpp_mov<dpp::kHalfMirror>(v);
+    else if constexpr (HALF == 2) return dpp_mov<dpp::kXor2>(v);
+    else return dpp_mov<dpp::kXor1>(v);
+}
+
+// Maximum over the 64 lanes, returned in every lane: DPP inside each
+// 16-lane row, then the four row results read as scalars.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+    v = fmaxf(v, dpp_mov<dpp::kXor1>(v));
+    v = fmaxf(v, dpp_mov<dpp::kXor2>(v));
+    v = fmaxf(v, dpp_mov<dpp::kHalfMirror>(v));
+    v = fmaxf(v, dpp_mov<dpp::kRowRor8>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Buffer resource for a byte range starting at `base` (wavefront-uniform):
+// buffer loads at offsets >= num_records return zero without touching
+// memory, which masks absent rows and blocks for free.
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t num_records) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_records,
+                                             kBufferFlags);
+}
+
+// Cache policy of the KV stream: every cache row is read once per step, so
+// loads are marked non-temporal (the `nt` bit); on MI355X this lifts a pure
+// 16-byte streaming read from about 6.2 to about 7.0 TB/s.
+#ifndef PA_LOAD_AUX
+#define PA_LOAD_AUX 2
+#endif
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, PA_LOAD_AUX);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
