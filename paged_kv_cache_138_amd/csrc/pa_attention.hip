@@ -22,6 +22,8 @@
 //     shuffles; exp2 with log2(e) folded into the scale.
 //   * p·V: each lane scales its 8 V elements by the broadcast weight of its
 //     row; the rows are summed at the end of the partition.
+#include "pa_attn_args.h"
+#include "pa_attn_gqa.h"
 #include "pa_device.h"
 #include "pa_host.h"
 
@@ -29,26 +31,6 @@
 
 namespace pa {
 namespace {
-
-struct AttnArgs {
-    void* out;
-    const uint16_t* query;
-    const uint16_t* key_cache;
-    const uint16_t* value_cache;
-    const int32_t* block_tables;
-    const int32_t* context_lens;
-    float* part_max;
-    float* part_sum;
-    float* part_out;
-    int num_seqs;
-    int num_heads;
-    int num_kv_heads;
-    int max_blocks_per_seq;
-    int num_blocks;
-    int partition_size;
-    int max_partitions;
-    float scale_log2;  // scale * log2(e)
-};
 
 #ifndef PA_WAVES
 #define PA_WAVES 4
@@ -383,6 +365,53 @@ attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs) {
     return nullptr;
 }
 
+// grouped-query instances (MFMA), 2 <= num_heads / num_kv_heads <= 16
+template <class KV, class OUT, int D>
+attn_fn pick_gqa_bs(int bs) {
+    switch (bs) {
+        case 16: return attn_gqa_kernel<KV, OUT, D, 16, kWaves>;
+        case 32: return attn_gqa_kernel<KV, OUT, D, 32, kWaves>;
+    }
+    return nullptr;
+}
+
+template <class KV, class OUT>
+attn_fn pick_gqa_d(int d, int bs) {
+    switch (d) {
+        case 64: return pick_gqa_bs<KV, OUT, 64>(bs);
+        case 128: return pick_gqa_bs<KV, OUT, 128>(bs);
+    }
+    return nullptr;
+}
+
+template <class KV>
+attn_fn pick_gqa_out(pa_dtype out, pa_dtype kv, int d, int bs) {
+    if (out == PA_F32) return pick_gqa_d<KV, OutF32>(d, bs);
+    if (out != kv) return nullptr;
+    if (kv == PA_F16) return pick_gqa_d<KV, OutF16>(d, bs);
+    return pick_gqa_d<KV, OutBF16>(d, bs);
+}
+
+constexpr int kMaxGroupMfma = 16;
+
+bool use_gqa(int num_heads, int num_kv_heads) {
+    const int g = num_heads / num_kv_heads;
+    return g >= 2 && g <= kMaxGroupMfma;
+}
+
+// kernel and grid width (workgroups per sequence and partition)
+attn_fn pick_kernel(pa_dtype kv, pa_dtype out, int d, int bs, int num_heads, int num_kv_heads,
+                    int* per_seq) {
+    if (use_gqa(num_heads, num_kv_heads)) {
+        *per_seq = num_kv_heads;
+        if (kv == PA_F16) return pick_gqa_out<KvF16>(out, kv, d, bs);
+        if (kv == PA_BF16) return pick_gqa_out<KvBF16>(out, kv, d, bs);
+        return nullptr;
+    }
+    *per_seq = num_heads;
+    return pick_attn(kv, out, d, bs);
+}
+
 template <class OUT>
 merge_fn pick_merge_d(int d) {
     switch (d) {
@@ -493,13 +522,15 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
     pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
                                    context_lens, s, scale, kv_dtype);
     if (st != PA_OK || num_seqs == 0) return st;
-    attn_fn fn = pick_attn(kv_dtype, out_dtype, head_dim, block_size);
+    int per_seq = 0;
+    attn_fn fn = pick_kernel(kv_dtype, out_dtype, head_dim, block_size, num_heads, num_kv_heads,
+                             &per_seq);
     PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
                            scale);
     a.partition_size = max_blocks_per_seq * block_size;  // one partition per sequence
     a.max_partitions = 1;
-    const int64_t grid = (int64_t)num_seqs * num_heads;
+    const int64_t grid = (int64_t)num_seqs * per_seq;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
     return check_launch("pa_decode");
@@ -540,7 +571,9 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
                "workspace must be 256-byte aligned");
     PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
                "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
-    attn_fn fn = pick_attn(kv_dtype, out_dtype, head_dim, block_size);
+    int per_seq = 0;
+    attn_fn fn = pick_kernel(kv_dtype, out_dtype, head_dim, block_size, num_heads, num_kv_heads,
+                             &per_seq);
     merge_fn mfn = pick_merge(out_dtype, head_dim);
     PA_REQUIRE(fn && mfn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
     char* ws = (char*)workspace;
@@ -551,7 +584,7 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
     a.part_out = (float*)(ws + lay.off_out);
     a.partition_size = partition_size;
     a.max_partitions = lay.np;
-    const int64_t grid = (int64_t)num_seqs * num_heads * lay.np;
+    const int64_t grid = (int64_t)num_seqs * per_seq * lay.np;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
     st = check_launch("pa_decode_split (partitions)");

@@ -1,0 +1,332 @@
+// Grouped-query paged decode attention on MFMA (gfx950).
+//
+// When G = num_heads / num_kv_heads query heads share one kv head, the G
+// query rows against one K/V block form a real small GEMM, so this kernel
+// reads each K/V row once for all G heads and does both products on the
+// matrix cores (v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation):
+//
+//   Sᵀ[16 tokens x 16 heads] = K[16 x 32 d] · Qᵀ[32 d x 16 heads], 4 per
+//       16-token sub-block for head_dim 128 (heads G..15 are zero padding);
+//   Oᵀ[16 d x 16 heads] += Vᵀ[16 d x 32 tokens] · Pᵀ[32 tokens x 16 heads],
+//       one per 16-column tile of head_dim, for each 32-token chunk.
+//
+// Register layouts (lane l, g = l/16, n = l%16): an MFMA output leaves lane l
+// holding column n and rows 4g..4g+3, so both products keep head n in lane
+// n's column; the online softmax of head n is entirely lane-local apart from
+// one max over the four lanes {n, n+16, n+32, n+48}. The contraction index of
+// each product is free to permute as long as both operands use the same map,
+// which is used twice:
+//   * q·k: lane (g, n) holds d = 32j + 8g .. +7 of K row n and of q row n;
+//     K rows come straight from HBM, 64 contiguous bytes per row per load.
+//   * p·v: the score registers themselves (tokens 4g..4g+3 and 16+4g..+3)
+//     are the Pᵀ operand; Vᵀ with the matching token order is read from the
+//     wave's LDS copy of the chunk by the gfx950 transpose read
+//     ds_read_b64_tr_b16 (in each 16-lane group, lane 4e+q names 4 elements
+//     of row e and lane j receives column j of the 4 rows).
+// P is split into hi + lo halves in the 16-bit type before the p·v products,
+// so the weights keep ~16 bits of precision.
+//
+// The work decomposition, masking by buffer ranges, partitions and the
+// cross-wave merge follow the head-per-workgroup kernel.
+#pragma once
+
+#include "pa_attn_args.h"
+#include "pa_device.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <class KV>
+struct Mma;
+
+template <>
+struct Mma<KvBF16> {
+    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
+                                                      0);
+    }
+    // x rounded to the 16-bit type (bits) and the value it stands for
+    static __device__ __forceinline__ uint32_t round16(float x, float* back) {
+        const __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32, round to nearest even
+        const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, h);
+        *back = __uint_as_float(b << 16);
+        return b;
+    }
+};
+
+template <>
+struct Mma<KvF16> {
+    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t round16(float x, float* back) {
+        const _Float16 h = (_Float16)x;
+        *back = (float)h;
+        return (uint32_t)__builtin_bit_cast(uint16_t, h);
+    }
+};
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <class KV, class OUT, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
+    constexpr int CH = 32;              // tokens per chunk
+    constexpr int NJ = D / 32;          // q·k products per 16-token sub-block
+    constexpr int NT = D / 16;          // 16-wide output tiles of head_dim
+    constexpr int LPR = D / 8;          // lanes per row in a coalesced V load
+    constexpr int RPI = 64 / LPR;       // rows per coalesced V load
+    constexpr int VL = CH / RPI;        // V loads per chunk
+    constexpr int BPC = CH / BS;        // blocks per chunk (BS = 16 or 32)
+    constexpr int VROW = D * 2 + 32;    // LDS bytes per V row (padding spreads banks)
+    constexpr int VTILE = CH * VROW;    // LDS bytes per wave
+    static_assert(BS == 16 || BS == 32, "block size 16 or 32");
+    static_assert(16 * D * 4 <= VTILE, "the wave's LDS tile also holds its partial output");
+    static_assert(VL * RPI == CH, "coalesced V loads tile the chunk");
+
+    __shared__ __attribute__((aligned(16))) char sm_v[NW][VTILE];
+    __shared__ float sm_m[NW][16];
+    __shared__ float sm_l[NW][16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;   // lane group
+    const int n = lane & 15;   // head inside the group (column of every product)
+    const int vr = lane / LPR; // row of a coalesced V load
+    const int vc = lane % LPR; // 16-byte slice of that row
+
+    const int Hq = a.num_heads;
+    const int Hkv = a.num_kv_heads;
+    const int G = Hq / Hkv;
+    int bid = blockIdx.x;
+    const int kvh = bid % Hkv;
+    bid /= Hkv;
+    const int seq = bid % a.num_seqs;
+    const int part = bid / a.num_seqs;
+
+    const int Lmax = a.max_blocks_per_seq * BS;
+    int L = a.context_lens[seq];
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int P = a.partition_size;
+    const int nparts = (L + P - 1) / P;
+    if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+    const int start = part * P;
+    const int end = min(start + P, L);
+    const int nb = (L + BS - 1) / BS;
+
+    const size_t row_bytes = (size_t)Hkv * D * 2;
+    const size_t block_bytes = row_bytes * BS;
+    const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
+    const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    char* vt = sm_v[wave];
+
+    // Qᵀ operand: lane (g, n) holds q[head n][32j + 8g .. +7]; padding heads are 0
+    u32x4 qb[NJ];
+    {
+        const bool real = n < G;
+        const uint16_t* qrow = a.query + ((size_t)seq * Hq + (size_t)kvh * G + (real ? n : 0)) * D;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            qb[j] = u32x4{0u, 0u, 0u, 0u};
+            if (real) qb[j] = *(const u32x4*)(qrow + 32 * j + 8 * g);
+        }
+    }
+
+    float m = -INFINITY;  // running max of head n's scores (log2 units)
+    float lsum = 0.f;     // this lane's share of head n's Σ exp2(s - m)
+    f32x4 oacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    struct ChunkIds {
+        __amdgpu_buffer_rsrc_t k[BPC], v[BPC];
+        bool ok[BPC];
+    };
+    auto fetch_ids = [&](int cs, ChunkIds& ci) {
+#pragma unroll
+        for (int b = 0; b < BPC; ++b) {
+            const int lb = cs / BS + b;
+            const int pid = lb < nb ? bt[lb] : -1;
+            const int blk_tok0 = lb * BS;
+            const int rows = min(max(end - blk_tok0, 0), BS);
+            const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
+            const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
+            const size_t boff = (size_t)(ok ? pid : 0) * block_bytes;
+            ci.k[b] = make_rsrc(kbase + boff, nrec);
+            ci.v[b] = make_rsrc(vbase + boff, nrec);
+            ci.ok[b] = ok;
+        }
+    };
+    // Chunks start on block boundaries: partitions are whole blocks and a
+    // 32-token chunk is two 16-token blocks or one 32-token block.
+    // K operand: sub-block s holds chunk tokens 16s .. 16s+15, lane (g, n) the
+    // token 16s + n and the 16 bytes at 64j + 16g of its row
+    auto issue_k = [&](const ChunkIds& ci, u32x4 (&kb)[2][NJ]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int b = (BS == 16) ? s : 0;
+            const int row0 = (BS == 16) ? 0 : 16 * s;
+            const uint32_t off = (uint32_t)((row0 + n) * row_bytes + 16 * g);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) kb[s][j] = buffer_load16(ci.k[b], off + 64 * j);
+        }
+    };
+    // V rows, coalesced: load i brings row vr + RPI*i of the chunk
+    auto issue_v = [&](const ChunkIds& ci, u32x4 (&vb)[VL]) {
+#pragma unroll
+        for (int i = 0; i < VL; ++i) {
+            const int t = vr + RPI * i;  // the RPI rows of one load share a block
+            const int b = (BS == 16) ? (RPI * i) / 16 : 0;
+            const int row = t - b * 16;
+            vb[i] = buffer_load16(ci.v[b], (uint32_t)(row * row_bytes + vc * 16));
+        }
+    };
+
+    auto process = [&](int cs, const ChunkIds& ci, const u32x4 (&kb)[2][NJ], bool has_next,
+                       auto&& prefetch_k, const u32x4 (&vb)[VL], auto&& prefetch_v) {
+        // ---- scores Sᵀ: lane (g, n) gets head n, tokens 16s + 4g + k ------
+        f32x4 sc[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            sc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) sc[s] = Mma<KV>::mma(kb[s][j], qb[j], sc[s]);
+        }
+        float sv[8];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int b = (BS == 16) ? s : 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int tok = cs + 16 * s + 4 * g + k;
+                const bool ok = ci.ok[b] && tok < end;
+                sv[4 * s + k] = ok ? sc[s][k] * a.scale_log2 : -INFINITY;
+            }
+        }
+        if (has_next) prefetch_k();
+        // ---- online softmax of head n ------------------------------------
+        float cm = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float mn = fmaxf(m, cm);
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+        float pr[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = mn == -INFINITY ? 0.f : fast_exp2(sv[e] - mn);
+            ps += pr[e];
+        }
+        m = mn;
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+        // Pᵀ operand in hi + lo halves
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float back, back2;
+            hw[e] = Mma<KV>::round16(pr[e], &back);
+            lw[e] = Mma<KV>::round16(pr[e] - back, &back2);
+        }
+        const u32x4 phi = u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
+                                hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
+        const u32x4 plo = u32x4{lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16),
+                                lw[4] | (lw[5] << 16), lw[6] | (lw[7] << 16)};
+        // ---- V chunk into the wave's LDS tile, then Vᵀ by transpose reads --
+#pragma unroll
+        for (int i = 0; i < VL; ++i)
+            *(u32x4*)(vt + (vr + RPI * i) * VROW + vc * 16) = vb[i];
+        if (has_next) prefetch_v();
+        const int e4 = n >> 2, q4 = n & 3;
+        const char* r0 = vt + (4 * g + e4) * VROW + q4 * 8;
+        const char* r1 = r0 + 16 * VROW;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const u32x2 lo = lds_read_tr16(r0 + 32 * t);
+            const u32x2 hi = lds_read_tr16(r1 + 32 * t);
+            const u32x4 av = u32x4{lo.x, lo.y, hi.x, hi.y};
+            oacc[t] = Mma<KV>::mma(av, phi, oacc[t]);
+            oacc[t] = Mma<KV>::mma(av, plo, oacc[t]);
+        }
+    };
+
+    int cs = start + wave * CH;
+    if (cs < end) {
+        ChunkIds cur;
+        u32x4 kb[2][NJ], vb[VL];
+        fetch_ids(cs, cur);
+        issue_k(cur, kb);
+        issue_v(cur, vb);
+        for (;;) {
+            const int nx = cs + NW * CH;
+            const bool more = nx < end;
+            ChunkIds nxt;
+            if (more) fetch_ids(nx, nxt);
+            process(cs, cur, kb, more, [&] { issue_k(nxt, kb); }, vb,
+                    [&] { issue_v(nxt, vb); });
+            if (!more) break;
+            cur = nxt;
+            cs = nx;
+        }
+    }
+
+    // ---- per-wave results: head n's (max, sum) and its output rows --------
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (g == 0) {
+        sm_m[wave][n] = m;
+        sm_l[wave][n] = lsum;
+    }
+    // the wave's V tile is free now: it holds O[16 heads][D] as floats
+    float* so = (float*)vt;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) so[n * D + 16 * t + 4 * g + k] = oacc[t][k];
+    }
+    __syncthreads();
+
+    // ---- merge the waves; every thread finishes some (head, dim) pairs ----
+    const size_t sh0 = (size_t)seq * Hq + (size_t)kvh * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+        float tot = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float wt = sm_m[w][h] == -INFINITY ? 0.f : fast_exp2(sm_m[w][h] - M);
+            tot += wt * sm_l[w][h];
+            o += wt * ((const float*)sm_v[w])[h * D + d];
+        }
+        const float res = tot > 0.f ? o / tot : 0.f;
+        const size_t sh = sh0 + h;
+        if (nparts <= 1) {
+            OUT::store(a.out, sh * D + d, res);
+        } else {
+            const size_t pidx = sh * a.max_partitions + part;
+            a.part_out[pidx * D + d] = res;
+            if (d == 0) {
+                a.part_max[pidx] = M * kLn2;
+                a.part_sum[pidx] = tot;
+            }
+        }
+    }
+}
+
+}  // namespace pa
