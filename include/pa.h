@@ -144,12 +144,11 @@ size_t pa_decode_split_workspace_bytes(int num_seqs, int num_heads, int head_dim
  *   workspace         device buffer of at least
  *                     pa_decode_split_workspace_bytes(...) bytes, 256-byte
  *                     aligned, owned by the caller; its contents on entry are
- *                     ignored and on exit unspecified.
+ *                     ignored and on exit unspecified. Calls that share a
+ *                     workspace must not overlap in time.
  *
- * Two launches on `stream`: the partition kernel writes each partition's
- * (max logit, Σ exp, normalised partial output) for sequences with more than
- * one partition - sequences with a single partition get their final output
- * directly - then the merge combines the partitions by log-sum-exp.
+ * Two launches on `stream`: pa_decode_partitions, then pa_lse_merge over the
+ * workspace (the merge skips sequences with a single partition).
  */
 pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                           const void* key_cache, const void* value_cache,
@@ -160,8 +159,27 @@ pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_partitions - the first launch of pa_decode_split on its own.
+ *
+ * Same arguments as pa_decode_split. One workgroup handles one partition of
+ * one (sequence, head) - of one (sequence, kv head) when 2..16 query heads
+ * share a kv head. A sequence with a single partition (L_i <= partition_size)
+ * gets its final output in `out`; for the others each partition p stores its
+ * row of the workspace: part_max = the largest scaled logit (natural-log
+ * units), part_sum = Σ exp(s - part_max), part_out = the normalised partial
+ * output. pa_lse_merge then finishes `out`.
+ */
+pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
+                               const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               float scale, pa_dtype kv_dtype, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_lse_merge - combine per-partition results (the second launch of
- * pa_decode_split, exported so it can be checked on its own).
+ * pa_decode_split).
  *
  *   part_max  float [num_seqs, num_heads, max_partitions]: m_p, the largest
  *             scaled logit scale·q·k of partition p (natural-log units).

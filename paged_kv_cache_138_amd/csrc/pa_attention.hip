@@ -24,6 +24,7 @@
 //     row; the rows are summed at the end of the partition.
 #include "pa_attn_args.h"
 #include "pa_attn_gqa.h"
+#include "pa_merge.h"
 #include "pa_device.h"
 #include "pa_host.h"
 
@@ -240,7 +241,6 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) sm_acc[wave][c * 8 + e] = acc[e];
     }
     __syncthreads();
-    if (wave != 0) return;
 
     float M = -INFINITY;
 #pragma unroll
@@ -252,32 +252,22 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
         wt[w] = sm_m[w] == -INFINITY ? 0.f : fast_exp2(sm_m[w] - M);
         tot += wt[w] * sm_l[w];
     }
-    float o[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) {
+    const size_t sh = (size_t)seq * Hq + head;
+    const size_t pidx = sh * a.max_partitions + part;
+    for (int d = threadIdx.x; d < D; d += NW * 64) {
         float t = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) t += wt[w] * sm_acc[w][lane * DPL + k];
-        o[k] = tot > 0.f ? t / tot : 0.f;
-    }
-    const size_t sh = (size_t)seq * Hq + head;
-    if (nparts <= 1) {
-        const size_t base = sh * D + (size_t)lane * DPL;
-        if constexpr (DPL == 2) {
-            OUT::store2(a.out, base, o[0], o[1]);
+        for (int w = 0; w < NW; ++w) t += wt[w] * sm_acc[w][d];
+        const float o = tot > 0.f ? t / tot : 0.f;
+        if (nparts <= 1) {
+            OUT::store(a.out, sh * D + d, o);
         } else {
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) OUT::store(a.out, base + k, o[k]);
+            a.part_out[pidx * D + d] = o;
         }
-    } else {
-        const size_t pidx = sh * a.max_partitions + part;
-        float* po = a.part_out + pidx * D + (size_t)lane * DPL;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) po[k] = o[k];
-        if (lane == 0) {
-            a.part_max[pidx] = M * kLn2;  // natural-log units
-            a.part_sum[pidx] = tot;
-        }
+    }
+    if (nparts > 1 && threadIdx.x == 0) {
+        a.part_max[pidx] = M * kLn2;  // natural-log units
+        a.part_sum[pidx] = tot;
     }
 }
 
@@ -293,37 +283,25 @@ struct MergeArgs {
     int partition_size;
 };
 
-// One wavefront per (sequence, head): combine that head's partitions.
+// 256 threads merge 256 / head_dim workspace rows (row = one query head of
+// one sequence), one output element per thread; rows of sequences with at
+// most one partition are skipped (the partition kernel wrote them).
 template <class OUT, int D>
-__global__ __launch_bounds__(64) void lse_merge_kernel(MergeArgs a) {
-    constexpr int DPL = D / 64;
-    const int lane = threadIdx.x;
-    const int sh = blockIdx.x;
-    const int seq = sh / a.num_heads;
+__global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
+    constexpr int RPW = 256 / D;
+    // a wavefront covers 64 consecutive elements of one row (D >= 64)
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * RPW + threadIdx.x / D);
+    const int d = threadIdx.x % D;
+    if (row >= a.num_seqs * a.num_heads) return;
+    const int seq = row / a.num_heads;
     int L = a.context_lens[seq];
     if (L < 0) L = 0;
     int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
     if (np > a.max_partitions) np = a.max_partitions;
     if (np <= 1) return;
-    const float* pm = a.part_max + (size_t)sh * a.max_partitions;
-    const float* ps = a.part_sum + (size_t)sh * a.max_partitions;
-    const float* po = a.part_out + (size_t)sh * a.max_partitions * D + (size_t)lane * DPL;
-    float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, pm[p]);
-    float tot = 0.f;
-    float o[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float mp = pm[p];
-        const float w = mp == -INFINITY ? 0.f : ps[p] * fast_exp2((mp - M) * kLog2e);
-        tot += w;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) o[k] += w * po[(size_t)p * D + k];
-    }
-    const size_t base = (size_t)sh * D + (size_t)lane * DPL;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) OUT::store(a.out, base + k, tot > 0.f ? o[k] / tot : 0.f);
+    const size_t r = (size_t)row * a.max_partitions;
+    const float o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D);
+    OUT::store(a.out, (size_t)row * D + d, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -484,6 +462,7 @@ AttnArgs make_args(void* out, const void* query, const void* kc, const void* vc,
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+
 struct SplitLayout {
     int np;
     size_t off_max, off_sum, off_out, total;
@@ -499,7 +478,7 @@ bool split_layout(int num_seqs, int num_heads, int head_dim, int max_blocks_per_
     const size_t rows = (size_t)num_seqs * num_heads * np;
     lay->np = np;
     lay->off_max = 0;
-    lay->off_sum = align256(rows * sizeof(float));
+    lay->off_sum = lay->off_max + align256(rows * sizeof(float));
     lay->off_out = lay->off_sum + align256(rows * sizeof(float));
     lay->total = lay->off_out + align256(rows * head_dim * sizeof(float));
     return true;
@@ -546,6 +525,84 @@ extern "C" size_t pa_decode_split_workspace_bytes(int num_seqs, int num_heads, i
     return lay.total;
 }
 
+namespace {
+
+pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
+                            const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const DecodeShape& s, float scale, pa_dtype kv_dtype,
+                            int partition_size, void* workspace, size_t workspace_bytes,
+                            void* stream, const char* what, SplitLayout* lay_out) {
+    pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                   context_lens, s, scale, kv_dtype);
+    if (st != PA_OK) return st;
+    PA_REQUIRE(partition_size > 0 && partition_size % s.block_size == 0, PA_ERR_SHAPE,
+               "partition_size %d must be a positive multiple of block_size %d",
+               partition_size, s.block_size);
+    SplitLayout lay;
+    split_layout(s.num_seqs, s.num_heads, s.head_dim, s.max_blocks_per_seq, s.block_size,
+                 partition_size, &lay);
+    *lay_out = lay;
+    if (s.num_seqs == 0) return PA_OK;
+    PA_REQUIRE(workspace, PA_ERR_WORKSPACE, "workspace is NULL");
+    PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PA_ERR_WORKSPACE,
+               "workspace must be 256-byte aligned");
+    PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
+               "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+    int per_seq = 0;
+    attn_fn fn = pick_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, s.num_heads,
+                             s.num_kv_heads, &per_seq);
+    PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    char* ws = (char*)workspace;
+    AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
+                           scale);
+    a.part_max = (float*)(ws + lay.off_max);
+    a.part_sum = (float*)(ws + lay.off_sum);
+    a.part_out = (float*)(ws + lay.off_out);
+    a.partition_size = partition_size;
+    a.max_partitions = lay.np;
+    const int64_t grid = (int64_t)s.num_seqs * per_seq * lay.np;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+    return check_launch(what);
+}
+
+pa_status launch_merge(void* out, pa_dtype out_dtype, const float* part_out,
+                       const float* part_max, const float* part_sum,
+                       const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
+                       int max_partitions, int partition_size, void* stream, const char* what) {
+    merge_fn mfn = pick_merge(out_dtype, head_dim);
+    PA_REQUIRE(mfn, PA_ERR_UNSUPPORTED, "no merge instance");
+    MergeArgs m{out, part_out, part_max, part_sum, context_lens,
+                num_seqs, num_heads, max_partitions, partition_size};
+    const int64_t rows = (int64_t)num_seqs * num_heads;
+    const int64_t rpw = 256 / head_dim;
+    const int64_t grid = (rows + rpw - 1) / rpw;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    hipLaunchKernelGGL(mfn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, m);
+    return check_launch(what);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
+                                          const void* key_cache, const void* value_cache,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int max_blocks_per_seq,
+                                          int num_blocks, float scale, pa_dtype kv_dtype,
+                                          int partition_size, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    SplitLayout lay;
+    return launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
+                             context_lens, s, scale, kv_dtype, partition_size, workspace,
+                             workspace_bytes, stream, "pa_decode_partitions", &lay);
+}
+
 extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                                      const void* key_cache, const void* value_cache,
                                      const int32_t* block_tables, const int32_t* context_lens,
@@ -556,44 +613,17 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
     clear_error();
     const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                         max_blocks_per_seq, num_blocks};
-    pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
-                                   context_lens, s, scale, kv_dtype);
-    if (st != PA_OK) return st;
-    PA_REQUIRE(partition_size > 0 && partition_size % block_size == 0, PA_ERR_SHAPE,
-               "partition_size %d must be a positive multiple of block_size %d",
-               partition_size, block_size);
-    if (num_seqs == 0) return PA_OK;
     SplitLayout lay;
-    split_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
-                 &lay);
-    PA_REQUIRE(workspace, PA_ERR_WORKSPACE, "workspace is NULL");
-    PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PA_ERR_WORKSPACE,
-               "workspace must be 256-byte aligned");
-    PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
-               "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
-    int per_seq = 0;
-    attn_fn fn = pick_kernel(kv_dtype, out_dtype, head_dim, block_size, num_heads, num_kv_heads,
-                             &per_seq);
-    merge_fn mfn = pick_merge(out_dtype, head_dim);
-    PA_REQUIRE(fn && mfn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    pa_status st = launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                     context_lens, s, scale, kv_dtype, partition_size, workspace,
+                                     workspace_bytes, stream, "pa_decode_split (partitions)",
+                                     &lay);
+    if (st != PA_OK || num_seqs == 0) return st;
     char* ws = (char*)workspace;
-    AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
-                           scale);
-    a.part_max = (float*)(ws + lay.off_max);
-    a.part_sum = (float*)(ws + lay.off_sum);
-    a.part_out = (float*)(ws + lay.off_out);
-    a.partition_size = partition_size;
-    a.max_partitions = lay.np;
-    const int64_t grid = (int64_t)num_seqs * per_seq * lay.np;
-    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
-    st = check_launch("pa_decode_split (partitions)");
-    if (st != PA_OK) return st;
-    MergeArgs m{out, a.part_out, a.part_max, a.part_sum, context_lens,
-                num_seqs, num_heads, lay.np, partition_size};
-    hipLaunchKernelGGL(mfn, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
-                       (hipStream_t)stream, m);
-    return check_launch("pa_decode_split (merge)");
+    return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
+                        (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
+                        context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
+                        stream, "pa_decode_split (merge)");
 }
 
 extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,
@@ -613,11 +643,7 @@ extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* pa
                "null pointer argument");
     PA_REQUIRE(aligned16(out) && aligned16(part_out), PA_ERR_ALIGNMENT,
                "out and part_out must be 16-byte aligned");
-    merge_fn mfn = pick_merge(out_dtype, head_dim);
-    PA_REQUIRE(mfn, PA_ERR_UNSUPPORTED, "no merge instance");
-    MergeArgs m{out, part_out, part_max, part_sum, context_lens,
-                num_seqs, num_heads, max_partitions, partition_size};
-    hipLaunchKernelGGL(mfn, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
-                       (hipStream_t)stream, m);
-    return check_launch("pa_lse_merge");
+    return launch_merge(out, out_dtype, part_out, part_max, part_sum, context_lens, num_seqs,
+                        num_heads, head_dim, max_partitions, partition_size, stream,
+                        "pa_lse_merge");
 }

@@ -54,6 +54,8 @@ def load():
     lib.pa_decode.restype = i32
     lib.pa_decode_split.argtypes = dec + [i32, vp, sz, vp]
     lib.pa_decode_split.restype = i32
+    lib.pa_decode_partitions.argtypes = dec + [i32, vp, sz, vp]
+    lib.pa_decode_partitions.restype = i32
     lib.pa_decode_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_split_workspace_bytes.restype = sz
     lib.pa_lse_merge.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
@@ -173,21 +175,50 @@ def make_workspace(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def decode_split(query, key_cache, value_cache, block_tables, context_lens, scale, partition_size=512,
-                 workspace=None, out=None, out_dtype=None):
-    """Paged decode attention as partitions + log-sum-exp merge."""
+def _split_call(name, query, key_cache, value_cache, block_tables, context_lens, scale, partition_size,
+                workspace, out, out_dtype):
     out, (B, Hq, Hkv, D, BS, MB, NB) = _decode_common(
         query, key_cache, value_cache, block_tables, context_lens, out, out_dtype)
     if workspace is None:
         workspace = make_workspace(B, Hq, D, MB, BS, partition_size, query.device)
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    st = load().pa_decode_split(_ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache),
-                                _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv,
-                                D, BS, MB, NB, float(scale), _DT[key_cache.dtype], int(partition_size),
-                                _ptr(workspace), nbytes, _stream(query))
-    _check(st, "pa_decode_split")
+    st = getattr(load(), name)(_ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache),
+                               _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv,
+                               D, BS, MB, NB, float(scale), _DT[key_cache.dtype], int(partition_size),
+                               _ptr(workspace), nbytes, _stream(query))
+    _check(st, name)
     return out
+
+
+def decode_split(query, key_cache, value_cache, block_tables, context_lens, scale, partition_size=512,
+                 workspace=None, out=None, out_dtype=None):
+    """Paged decode attention as partitions + log-sum-exp merge."""
+    return _split_call("pa_decode_split", query, key_cache, value_cache, block_tables, context_lens,
+                       scale, partition_size, workspace, out, out_dtype)
+
+
+def decode_partitions(query, key_cache, value_cache, block_tables, context_lens, scale,
+                      partition_size=512, workspace=None, out=None, out_dtype=None):
+    """The partition launch of decode_split alone: single-partition sequences
+    get their output, the others leave per-partition rows in `workspace`."""
+    return _split_call("pa_decode_partitions", query, key_cache, value_cache, block_tables,
+                       context_lens, scale, partition_size, workspace, out, out_dtype)
+
+
+def workspace_views(workspace, num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
+                    partition_size):
+    """(part_max, part_sum, part_out) float32 views of a split workspace."""
+    lmax = max_blocks_per_seq * block_size
+    NP = -(-lmax // partition_size)
+    rows = num_seqs * num_heads * NP
+    up = lambda x: (x + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    o_max, o_sum = 0, up(rows * 4)
+    o_out = o_sum + up(rows * 4)
+    view = lambda off, n: f[off:off + 4 * n].view(torch.float32)
+    return (view(o_max, rows).view(num_seqs, num_heads, NP), view(o_sum, rows).view(num_seqs, num_heads, NP),
+            view(o_out, rows * head_dim).view(num_seqs, num_heads, NP, head_dim))
 
 
 def lse_merge(part_out, part_max, part_sum, context_lens, partition_size, out=None, out_dtype=torch.float32):

@@ -67,6 +67,19 @@ class DeviceBatch:
         palib.reshape_and_cache(self.new_key, self.new_value, self.key_cache, self.value_cache,
                                 self.slot_mapping)
 
+    def partitions(self):
+        """Split path, first launch only (see lib.decode_partitions)."""
+        palib.decode_partitions(self.query, self.key_cache, self.value_cache, self.block_tables,
+                                self.context_lens, self.scale, self.partition_size,
+                                workspace=self.workspace, out=self.out)
+
+    def merge(self):
+        """Split path, second launch: log-sum-exp merge over the workspace."""
+        B, Hq, D = self.query.shape
+        pm, ps, po = palib.workspace_views(self.workspace, B, Hq, D, self.block_tables.shape[1],
+                                           self.key_cache.shape[1], self.partition_size)
+        palib.lse_merge(po, pm, ps, self.context_lens, self.partition_size, out=self.out)
+
     def attend(self):
         if self.split:
             palib.decode_split(self.query, self.key_cache, self.value_cache, self.block_tables,

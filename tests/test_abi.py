@@ -43,7 +43,7 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_size_formula(lib):
-    # NP = ceil(128*16/512) = 4; max and sum: 32*40*4 floats, out: *128
+    # NP = ceil(128*16/512) = 4; max and sum: 32*40*4 floats each, out: *128
     n = lib.pa_decode_split_workspace_bytes(32, 40, 128, 128, 16, 512)
     rows = 32 * 40 * 4
     up = lambda x: (x + 255) // 256 * 256

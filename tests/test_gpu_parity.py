@@ -300,3 +300,29 @@ def test_fused_qkv_strided_cache_write():
                                       sentinel.cpu().numpy(), slots.cpu().numpy())
     assert np.array_equal(kc.cpu().numpy().view(np.uint16), rk.view(np.uint16))
     assert np.array_equal(vc.cpu().numpy().view(np.uint16), rv.view(np.uint16))
+
+
+def test_split_workspace_reuse_garbage_and_shapes():
+    """One workspace, filled with random bytes, reused across calls of
+    different shapes and repeated calls: every result matches the oracle."""
+    cases = [
+        dict(num_seqs=3, num_heads=4, num_kv_heads=4, head_dim=128, dtype="f16", block_size=16,
+             num_blocks=200, max_blocks_per_seq=64, lens="uniform:100:1000"),
+        dict(num_seqs=7, num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", block_size=16,
+             num_blocks=400, max_blocks_per_seq=64, lens="uniform:1:1000"),
+        dict(num_seqs=5, num_heads=8, num_kv_heads=8, head_dim=64, dtype="f16", block_size=32,
+             num_blocks=200, max_blocks_per_seq=32, lens="uniform:1:1000"),
+    ]
+    ws = torch.randint(0, 256, (8 << 20,), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for ci, kw in enumerate(cases):
+            w = _small("reuse%d" % ci, **kw)
+            b = W.make_batch(w, seed=50 + ci)
+            db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=128)
+            db.write_cache()
+            out = palib.decode_split(db.query, db.key_cache, db.value_cache, db.block_tables,
+                                     db.context_lens, db.scale, 128, workspace=ws,
+                                     out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            _, _, ref = _oracle_step(b)
+            _assert_close(to_host_f64(out), ref, "f32", "reuse case %d rep %d" % (ci, rep))
