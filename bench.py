@@ -91,9 +91,9 @@ def copy_calibration(mib):
 
 def default_path(workload):
     # measured on MI355X: the split path (partitions of the workload's
-    # partition size, then the merge) is faster except for the lognormal
-    # LLaMA-7B-like batch, where most contexts fit one partition anyway
-    return "decode" if workload.name.startswith("llama7b") else "split"
+    # partition size, then the merge) beats the single launch on every
+    # workload: long sequences no longer end the launch alone
+    return "split"
 
 
 def cpu_baseline(batch, target_s):

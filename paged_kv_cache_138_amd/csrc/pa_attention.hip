@@ -37,6 +37,10 @@ namespace {
 #define PA_WAVES 4
 #endif
 constexpr int kWaves = PA_WAVES;  // wavefronts per workgroup
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
+constexpr int kGqaWaves = PA_GQA_WAVES;
 
 // One transpose-reduce step over groups of lanes: lanes whose index has
 // bit HALF set keep the upper half of their list, the others the lower half,
@@ -52,8 +56,13 @@ __device__ __forceinline__ void tr_step(float (&pd)[N], int c) {
     }
 }
 
+#ifndef PA_MHA_WAVES_PER_EU
+#define PA_MHA_WAVES_PER_EU 3
+#endif
+
 template <class KV, class OUT, int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_kernel(AttnArgs a) {
     constexpr int LPR = D / 8;          // lanes per cache row
     constexpr int RPI = 64 / LPR;       // rows per load instruction
     constexpr int IPB = BS / RPI;       // load instructions per block
@@ -77,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
     const int c = lane % LPR;  // 8-element slice of the row
 
     const int Hq = a.num_heads;
-    int bid = blockIdx.x;
+    int bid = blockIdx.x;  // (sequence, query head, partition), head fastest
     const int head = bid % Hq;
     bid /= Hq;
     const int seq = bid % a.num_seqs;
@@ -187,14 +196,20 @@ __global__ __launch_bounds__(NW * 64) void attn_partition_kernel(AttnArgs a) {
         static_for<0, NI>([&](auto I) {
             constexpr int i = decltype(I)::value;
             const float pb = group_bcast<LPR, i>(pr);
-            acc[0] += pb * KV::lo(vr[i].x);
-            acc[1] += pb * KV::hi(vr[i].x);
-            acc[2] += pb * KV::lo(vr[i].y);
-            acc[3] += pb * KV::hi(vr[i].y);
-            acc[4] += pb * KV::lo(vr[i].z);
-            acc[5] += pb * KV::hi(vr[i].z);
-            acc[6] += pb * KV::lo(vr[i].w);
-            acc[7] += pb * KV::hi(vr[i].w);
+            // tie the row to its weight so its unpacking (explicit shifts for
+            // bf16) is not hoisted ahead of the softmax, where all 16 rows'
+            // unpacked values would be live at once
+            uint32_t x = vr[i].x, y = vr[i].y, z = vr[i].z, w = vr[i].w;
+            if constexpr (std::is_same<KV, KvBF16>::value)
+                asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w) : "v"(pb));
+            acc[0] += pb * KV::lo(x);
+            acc[1] += pb * KV::hi(x);
+            acc[2] += pb * KV::lo(y);
+            acc[3] += pb * KV::hi(y);
+            acc[4] += pb * KV::lo(z);
+            acc[5] += pb * KV::hi(z);
+            acc[6] += pb * KV::lo(w);
+            acc[7] += pb * KV::hi(w);
         });
     };
 
@@ -347,8 +362,8 @@ attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs) {
 template <class KV, class OUT, int D>
 attn_fn pick_gqa_bs(int bs) {
     switch (bs) {
-        case 16: return attn_gqa_kernel<KV, OUT, D, 16, kWaves>;
-        case 32: return attn_gqa_kernel<KV, OUT, D, 32, kWaves>;
+        case 16: return attn_gqa_kernel<KV, OUT, D, 16, kGqaWaves>;
+        case 32: return attn_gqa_kernel<KV, OUT, D, 32, kGqaWaves>;
     }
     return nullptr;
 }
@@ -379,9 +394,11 @@ bool use_gqa(int num_heads, int num_kv_heads) {
 
 // kernel and grid width (workgroups per sequence and partition)
 attn_fn pick_kernel(pa_dtype kv, pa_dtype out, int d, int bs, int num_heads, int num_kv_heads,
-                    int* per_seq) {
+                    int* per_seq, int* threads) {
+    *threads = kWaves * 64;
     if (use_gqa(num_heads, num_kv_heads)) {
         *per_seq = num_kv_heads;
+        *threads = kGqaWaves * 64;
         if (kv == PA_F16) return pick_gqa_out<KvF16>(out, kv, d, bs);
         if (kv == PA_BF16) return pick_gqa_out<KvBF16>(out, kv, d, bs);
         return nullptr;
@@ -463,6 +480,7 @@ AttnArgs make_args(void* out, const void* query, const void* kc, const void* vc,
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 
+
 struct SplitLayout {
     int np;
     size_t off_max, off_sum, off_out, total;
@@ -501,9 +519,9 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
     pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
                                    context_lens, s, scale, kv_dtype);
     if (st != PA_OK || num_seqs == 0) return st;
-    int per_seq = 0;
+    int per_seq = 0, threads = 0;
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, head_dim, block_size, num_heads, num_kv_heads,
-                             &per_seq);
+                             &per_seq, &threads);
     PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
                            scale);
@@ -511,7 +529,7 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
     a.max_partitions = 1;
     const int64_t grid = (int64_t)num_seqs * per_seq;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, (hipStream_t)stream, a);
     return check_launch("pa_decode");
 }
 
@@ -549,9 +567,9 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
                "workspace must be 256-byte aligned");
     PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
                "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
-    int per_seq = 0;
+    int per_seq = 0, threads = 0;
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, s.num_heads,
-                             s.num_kv_heads, &per_seq);
+                             s.num_kv_heads, &per_seq, &threads);
     PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
     char* ws = (char*)workspace;
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
@@ -563,7 +581,7 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     a.max_partitions = lay.np;
     const int64_t grid = (int64_t)s.num_seqs * per_seq * lay.np;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, (hipStream_t)stream, a);
     return check_launch(what);
 }
 

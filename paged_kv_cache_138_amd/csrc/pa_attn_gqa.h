@@ -16,18 +16,22 @@
 // one max over the four lanes {n, n+16, n+32, n+48}. The contraction index of
 // each product is free to permute as long as both operands use the same map,
 // which is used twice:
-//   * q·k: lane (g, n) holds d = 32j + 8g .. +7 of K row n and of q row n;
-//     K rows come straight from HBM, 64 contiguous bytes per row per load.
+//   * q·k: lane (g, n) holds d = 32j + 8g .. +7 of K row n and of q row n,
+//     read from the wave's LDS copy of the chunk with ds_read_b128.
 //   * p·v: the score registers themselves (tokens 4g..4g+3 and 16+4g..+3)
 //     are the Pᵀ operand; Vᵀ with the matching token order is read from the
-//     wave's LDS copy of the chunk by the gfx950 transpose read
+//     wave's LDS copy of the chunk's V rows by the gfx950 transpose read
 //     ds_read_b64_tr_b16 (in each 16-lane group, lane 4e+q names 4 elements
 //     of row e and lane j receives column j of the 4 rows).
 // P is split into hi + lo halves in the 16-bit type before the p·v products,
 // so the weights keep ~16 bits of precision.
 //
-// The work decomposition, masking by buffer ranges, partitions and the
-// cross-wave merge follow the head-per-workgroup kernel.
+// K and V rows reach LDS through the same coalesced loads as the
+// head-per-workgroup kernel (head_dim/8 lanes per row, whole 128-byte lines
+// per request). LDS rows are padded to 2*head_dim + 16 bytes, which keeps
+// both the 16-byte reads of K and the transpose reads of V free of bank
+// conflicts. The work decomposition, masking by buffer ranges, partitions
+// and the cross-wave merge follow the head-per-workgroup kernel.
 #pragma once
 
 #include "pa_attn_args.h"
@@ -78,22 +82,34 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+#ifndef PA_GQA_WAVES_PER_EU
+#define PA_GQA_WAVES_PER_EU 2
+#endif
+#ifndef PA_GQA_CHUNK
+#define PA_GQA_CHUNK 32
+#endif
+
 template <class KV, class OUT, int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
-    constexpr int CH = 32;              // tokens per chunk
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(AttnArgs a) {
+    constexpr int CH = PA_GQA_CHUNK;    // tokens per chunk (32 or 64)
+    constexpr int NS = CH / 16;         // 16-token sub-blocks of a chunk
+    constexpr int NH = CH / 32;         // 32-token halves (one p·v contraction each)
     constexpr int NJ = D / 32;          // q·k products per 16-token sub-block
     constexpr int NT = D / 16;          // 16-wide output tiles of head_dim
     constexpr int LPR = D / 8;          // lanes per row in a coalesced V load
     constexpr int RPI = 64 / LPR;       // rows per coalesced V load
     constexpr int VL = CH / RPI;        // V loads per chunk
     constexpr int BPC = CH / BS;        // blocks per chunk (BS = 16 or 32)
-    constexpr int VROW = D * 2 + 32;    // LDS bytes per V row (padding spreads banks)
-    constexpr int VTILE = CH * VROW;    // LDS bytes per wave
+    constexpr int ROWB = D * 2 + 16;    // LDS bytes per K or V row (padding spreads banks)
+    constexpr int TILE = CH * ROWB;     // LDS bytes of one chunk's K (then V) rows
+    constexpr int OROW = D + 4;         // floats per row of the wave's partial output
     static_assert(BS == 16 || BS == 32, "block size 16 or 32");
-    static_assert(16 * D * 4 <= VTILE, "the wave's LDS tile also holds its partial output");
-    static_assert(VL * RPI == CH, "coalesced V loads tile the chunk");
+    static_assert(CH == 32 || CH == 64, "chunk of 32 or 64 tokens");
+    static_assert(16 * OROW * 4 <= TILE, "the wave's LDS tile also holds its partial output");
+    static_assert(VL * RPI == CH, "coalesced loads tile the chunk");
 
-    __shared__ __attribute__((aligned(16))) char sm_v[NW][VTILE];
+    __shared__ __attribute__((aligned(16))) char sm_v[NW][TILE];
     __shared__ float sm_m[NW][16];
     __shared__ float sm_l[NW][16];
 
@@ -107,7 +123,7 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
     const int Hq = a.num_heads;
     const int Hkv = a.num_kv_heads;
     const int G = Hq / Hkv;
-    int bid = blockIdx.x;
+    int bid = blockIdx.x;  // (sequence, kv head, partition), kv head fastest
     const int kvh = bid % Hkv;
     bid /= Hkv;
     const int seq = bid % a.num_seqs;
@@ -128,7 +144,9 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
     const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
     const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-    char* vt = sm_v[wave];
+    // the wave's LDS tile holds the current chunk's K rows, then its V rows
+    // (a wave's LDS operations complete in order)
+    char* tile = sm_v[wave];
 
     // Qᵀ operand: lane (g, n) holds q[head n][32j + 8g .. +7]; padding heads are 0
     u32x4 qb[NJ];
@@ -167,45 +185,42 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
             ci.ok[b] = ok;
         }
     };
-    // Chunks start on block boundaries: partitions are whole blocks and a
-    // 32-token chunk is two 16-token blocks or one 32-token block.
-    // K operand: sub-block s holds chunk tokens 16s .. 16s+15, lane (g, n) the
-    // token 16s + n and the 16 bytes at 64j + 16g of its row
-    auto issue_k = [&](const ChunkIds& ci, u32x4 (&kb)[2][NJ]) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int b = (BS == 16) ? s : 0;
-            const int row0 = (BS == 16) ? 0 : 16 * s;
-            const uint32_t off = (uint32_t)((row0 + n) * row_bytes + 16 * g);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) kb[s][j] = buffer_load16(ci.k[b], off + 64 * j);
-        }
-    };
-    // V rows, coalesced: load i brings row vr + RPI*i of the chunk
-    auto issue_v = [&](const ChunkIds& ci, u32x4 (&vb)[VL]) {
+    // Chunks start on block boundaries (partitions are whole blocks). Load i
+    // of a chunk brings rows vr + RPI*i (the RPI rows of one load share a block).
+    auto issue_rows = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[VL]) {
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
-            const int t = vr + RPI * i;  // the RPI rows of one load share a block
-            const int b = (BS == 16) ? (RPI * i) / 16 : 0;
-            const int row = t - b * 16;
-            vb[i] = buffer_load16(ci.v[b], (uint32_t)(row * row_bytes + vc * 16));
+            const int t = vr + RPI * i;
+            const int b = (RPI * i) / BS;
+            const int row = t - b * BS;
+            buf[i] = buffer_load16(rs[b], (uint32_t)(row * row_bytes + vc * 16));
         }
     };
+    auto issue_k = [&](const ChunkIds& ci, u32x4 (&kb)[VL]) { issue_rows(ci.k, kb); };
+    auto issue_v = [&](const ChunkIds& ci, u32x4 (&vb)[VL]) { issue_rows(ci.v, vb); };
+    auto to_lds = [&](char* tile, const u32x4 (&buf)[VL]) {
+#pragma unroll
+        for (int i = 0; i < VL; ++i) *(u32x4*)(tile + (vr + RPI * i) * ROWB + vc * 16) = buf[i];
+    };
 
-    auto process = [&](int cs, const ChunkIds& ci, const u32x4 (&kb)[2][NJ], bool has_next,
+    auto process = [&](int cs, const ChunkIds& ci, const u32x4 (&kb)[VL], bool has_next,
                        auto&& prefetch_k, const u32x4 (&vb)[VL], auto&& prefetch_v) {
         // ---- scores Sᵀ: lane (g, n) gets head n, tokens 16s + 4g + k ------
-        f32x4 sc[2];
+        to_lds(tile, kb);
+        if (has_next) prefetch_k();
+        f32x4 sc[NS];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NS; ++s) {
             sc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const char* krow = tile + (16 * s + n) * ROWB + 16 * g;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) sc[s] = Mma<KV>::mma(kb[s][j], qb[j], sc[s]);
+            for (int j = 0; j < NJ; ++j)
+                sc[s] = Mma<KV>::mma(*(const u32x4*)(krow + 64 * j), qb[j], sc[s]);
         }
-        float sv[8];
+        float sv[4 * NS];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int b = (BS == 16) ? s : 0;
+        for (int s = 0; s < NS; ++s) {
+            const int b = (16 * s) / BS;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int tok = cs + 16 * s + 4 * g + k;
@@ -213,19 +228,18 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
                 sv[4 * s + k] = ok ? sc[s][k] * a.scale_log2 : -INFINITY;
             }
         }
-        if (has_next) prefetch_k();
         // ---- online softmax of head n ------------------------------------
         float cm = sv[0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) cm = fmaxf(cm, sv[e]);
+        for (int e = 1; e < 4 * NS; ++e) cm = fmaxf(cm, sv[e]);
         cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
         const float mn = fmaxf(m, cm);
         const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
-        float pr[8];
+        float pr[4 * NS];
         float ps = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4 * NS; ++e) {
             pr[e] = mn == -INFINITY ? 0.f : fast_exp2(sv[e] - mn);
             ps += pr[e];
         }
@@ -233,40 +247,46 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
         lsum = lsum * alpha + ps;
 #pragma unroll
         for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
-        // Pᵀ operand in hi + lo halves
-        uint32_t hw[8], lw[8];
+        // Pᵀ operands (one per 32-token half) in hi + lo halves
+        u32x4 phi[NH], plo[NH];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float back, back2;
-            hw[e] = Mma<KV>::round16(pr[e], &back);
-            lw[e] = Mma<KV>::round16(pr[e] - back, &back2);
+        for (int h = 0; h < NH; ++h) {
+            uint32_t hw[8], lw[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float back, back2;
+                hw[e] = Mma<KV>::round16(pr[8 * h + e], &back);
+                lw[e] = Mma<KV>::round16(pr[8 * h + e] - back, &back2);
+            }
+            phi[h] = u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
+                           hw[6] | (hw[7] << 16)};
+            plo[h] = u32x4{lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16), lw[4] | (lw[5] << 16),
+                           lw[6] | (lw[7] << 16)};
         }
-        const u32x4 phi = u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
-                                hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
-        const u32x4 plo = u32x4{lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16),
-                                lw[4] | (lw[5] << 16), lw[6] | (lw[7] << 16)};
-        // ---- V chunk into the wave's LDS tile, then Vᵀ by transpose reads --
-#pragma unroll
-        for (int i = 0; i < VL; ++i)
-            *(u32x4*)(vt + (vr + RPI * i) * VROW + vc * 16) = vb[i];
+        // ---- V rows into the tile (after the K reads), Vᵀ by transpose reads
+        to_lds(tile, vb);
         if (has_next) prefetch_v();
         const int e4 = n >> 2, q4 = n & 3;
-        const char* r0 = vt + (4 * g + e4) * VROW + q4 * 8;
-        const char* r1 = r0 + 16 * VROW;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const u32x2 lo = lds_read_tr16(r0 + 32 * t);
-            const u32x2 hi = lds_read_tr16(r1 + 32 * t);
-            const u32x4 av = u32x4{lo.x, lo.y, hi.x, hi.y};
-            oacc[t] = Mma<KV>::mma(av, phi, oacc[t]);
-            oacc[t] = Mma<KV>::mma(av, plo, oacc[t]);
+        for (int h = 0; h < NH; ++h) {
+            // half h: tokens 32h + 4g + e (e < 4) and 32h + 16 + 4g + e - 4
+            const char* r0 = tile + (32 * h + 4 * g + e4) * ROWB + q4 * 8;
+            const char* r1 = r0 + 16 * ROWB;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const u32x2 lo = lds_read_tr16(r0 + 32 * t);
+                const u32x2 hi = lds_read_tr16(r1 + 32 * t);
+                const u32x4 av = u32x4{lo.x, lo.y, hi.x, hi.y};
+                oacc[t] = Mma<KV>::mma(av, phi[h], oacc[t]);
+                oacc[t] = Mma<KV>::mma(av, plo[h], oacc[t]);
+            }
         }
     };
 
     int cs = start + wave * CH;
     if (cs < end) {
         ChunkIds cur;
-        u32x4 kb[2][NJ], vb[VL];
+        u32x4 kb[VL], vb[VL];
         fetch_ids(cs, cur);
         issue_k(cur, kb);
         issue_v(cur, vb);
@@ -290,12 +310,13 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
         sm_m[wave][n] = m;
         sm_l[wave][n] = lsum;
     }
-    // the wave's V tile is free now: it holds O[16 heads][D] as floats
-    float* so = (float*)vt;
+    // the wave's tiles are free now: they hold O[16 heads][D] as floats, in
+    // rows of OROW floats so the 16 heads' stores fall in different banks
+    float* so = (float*)tile;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) so[n * D + 16 * t + 4 * g + k] = oacc[t][k];
+        for (int k = 0; k < 4; ++k) so[n * OROW + 16 * t + 4 * g + k] = oacc[t][k];
     }
     __syncthreads();
 
@@ -312,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) void attn_gqa_kernel(AttnArgs a) {
         for (int w = 0; w < NW; ++w) {
             const float wt = sm_m[w][h] == -INFINITY ? 0.f : fast_exp2(sm_m[w][h] - M);
             tot += wt * sm_l[w][h];
-            o += wt * ((const float*)sm_v[w])[h * D + d];
+            o += wt * ((const float*)sm_v[w])[h * OROW + d];
         }
         const float res = tot > 0.f ? o / tot : 0.f;
         const size_t sh = sh0 + h;
