@@ -168,55 +168,59 @@ def main():
     batch = W.make_batch(w, seed=args.seed)
     t_gen = time.perf_counter() - t_gen
     out_dtype = torch.float32 if args.out_dtype == "f32" else None
-    base = DeviceBatch(batch, out_dtype=out_dtype, split=(path == "split"),
-                       partition_size=args.partition_size)
-    unique_bytes, logical_bytes = W.step_bytes(batch, None if out_dtype is None else "f32")
-    write_bytes = W.cache_write_bytes(batch)
-    # rotation copies: enough that the cycle's footprint is >= 8x the LLC
-    kv_block = 2 * base.key_cache[0].numel() * base.key_cache.element_size()
-    footprint = kv_block * len(batch.allocated_blocks)
-    R = args.rotations or max(2, min(16, -(-8 * LLC_BYTES // max(footprint, 1))))
-    copies = [RotatedBatch(base, seed=1000 + r) for r in range(R)]
-    del base
-    torch.cuda.synchronize()
-
-    for k in range(args.warmup):
-        copies[k % R].step()
-    torch.cuda.synchronize()
-    # all copies must agree bit for bit (same logical data, different placement)
-    ref = copies[0].out.clone()
-    for c in copies[1:]:
-        c.step()
-    torch.cuda.synchronize()
-    for c in copies[1:]:
-        assert torch.equal(c.out.view(torch.int16) if c.out.dtype != torch.float32 else c.out,
-                           ref.view(torch.int16) if ref.dtype != torch.float32 else ref), \
-            "rotated copies disagree"
-
-    K = args.steps
-    split = path == "split"
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        copies[k % R].step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    # the dominant kernel alone: K back-to-back launches between two HIP events
-    # on the launch stream (pa_decode, or the partition launch of the split path)
-    dom = (lambda c: c.partitions()) if split else (lambda c: c.attend())
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for k in range(K):
-        dom(copies[k % R])
-    e1.record()
-    torch.cuda.synchronize()
-    attn_avg_ms = e0.elapsed_time(e1) / K
-    if split:  # leave every copy's output complete
-        for c in copies:
-            c.merge()
+    # all GPU work runs on one dedicated stream of default priority; the
+    # legacy default stream adds a few microseconds of synchronisation per step
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        base = DeviceBatch(batch, out_dtype=out_dtype, split=(path == "split"),
+                           partition_size=args.partition_size)
+        unique_bytes, logical_bytes = W.step_bytes(batch, None if out_dtype is None else "f32")
+        write_bytes = W.cache_write_bytes(batch)
+        # rotation copies: enough that the cycle's footprint is >= 8x the LLC
+        kv_block = 2 * base.key_cache[0].numel() * base.key_cache.element_size()
+        footprint = kv_block * len(batch.allocated_blocks)
+        R = args.rotations or max(2, min(16, -(-8 * LLC_BYTES // max(footprint, 1))))
+        copies = [RotatedBatch(base, seed=1000 + r) for r in range(R)]
+        del base
         torch.cuda.synchronize()
+
+        for k in range(args.warmup):
+            copies[k % R].step()
+        torch.cuda.synchronize()
+        # all copies must agree bit for bit (same logical data, different placement)
+        ref = copies[0].out.clone()
+        for c in copies[1:]:
+            c.step()
+        torch.cuda.synchronize()
+        for c in copies[1:]:
+            assert torch.equal(c.out.view(torch.int16) if c.out.dtype != torch.float32 else c.out,
+                               ref.view(torch.int16) if ref.dtype != torch.float32 else ref), \
+                "rotated copies disagree"
+
+        K = args.steps
+        split = path == "split"
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            copies[k % R].step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / K
+        # the dominant kernel alone: K back-to-back launches between two HIP events
+        # on the launch stream (pa_decode, or the partition launch of the split path)
+        dom = (lambda c: c.partitions()) if split else (lambda c: c.attend())
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(K):
+            dom(copies[k % R])
+        e1.record()
+        torch.cuda.synchronize()
+        attn_avg_ms = e0.elapsed_time(e1) / K
+        if split:  # leave every copy's output complete
+            for c in copies:
+                c.merge()
+            torch.cuda.synchronize()
     step_bytes = unique_bytes + write_bytes
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbs = unique_bytes / (attn_avg_ms * 1e-3) / 1e9
