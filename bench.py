@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama13b")
-    ap.add_argument("--path", choices=["auto", "decode", "split"], default="auto")
+    ap.add_argument("--path", choices=["auto", "decode", "split", "split_prefix"], default="auto")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--out-dtype", choices=["native", "f32"], default="native")
     ap.add_argument("--rotations", type=int, default=0, help="batch copies cycled (0 = auto)")
@@ -92,8 +92,9 @@ def copy_calibration(mib):
 def default_path(workload):
     # measured on MI355X: the split path (partitions of the workload's
     # partition size, then the merge) beats the single launch on every
-    # workload: long sequences no longer end the launch alone
-    return "split"
+    # workload: long sequences no longer end the launch alone; a batch whose
+    # sequences share a prefix computes the prefix partitions once per 16 rows
+    return "split_prefix" if workload.shared_prefix_tokens else "split"
 
 
 def cpu_baseline(batch, target_s):
@@ -172,8 +173,9 @@ def main():
     # legacy default stream adds a few microseconds of synchronisation per step
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        base = DeviceBatch(batch, out_dtype=out_dtype, split=(path == "split"),
-                           partition_size=args.partition_size)
+        base = DeviceBatch(batch, out_dtype=out_dtype, split=path.startswith("split"),
+                           partition_size=args.partition_size,
+                           shared_prefix=(path == "split_prefix"))
         unique_bytes, logical_bytes = W.step_bytes(batch, None if out_dtype is None else "f32")
         write_bytes = W.cache_write_bytes(batch)
         # rotation copies: enough that the cycle's footprint is >= 8x the LLC
@@ -198,7 +200,7 @@ def main():
                 "rotated copies disagree"
 
         K = args.steps
-        split = path == "split"
+        split = path.startswith("split")
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(K):
@@ -252,7 +254,9 @@ def main():
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic("%s/%s" % (w.name, path)),
                      "kernel": "%s: %d back-to-back launches between HIP events, avg %.2f us"
-                               % ("pa_decode_partitions" if split else "pa_decode", K,
+                               % ({"split": "pa_decode_partitions", "decode": "pa_decode",
+                                   "split_prefix": "pa_decode_partitions_shared_prefix (prefix "
+                                                   "and suffix kernels)"}[path], K,
                                   attn_avg_ms * 1e3)},
         "host_data_generation_s": round(t_gen, 2),
     }
@@ -262,7 +266,7 @@ def main():
 
 
 def base_partition(path, args, w):
-    if path != "split":
+    if not path.startswith("split"):
         return None
     return args.partition_size or w.partition_size
 

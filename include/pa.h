@@ -178,6 +178,46 @@ pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Shared-prefix variants. When every sequence of the batch begins with the
+ * same physical blocks - a prompt prefix cached once and referenced by all
+ * tables ("vLLM 核心：PagedAttention 与 Continuous Batching" §3 Prefix
+ * Caching; lqnn.cn/news/170268 §3.2-§3.4) - the partitions covering that
+ * prefix are computed once per 16 query rows: one workgroup takes 16 / G
+ * sequences x G query heads of a kv head (G = num_heads / num_kv_heads,
+ * at most 16) and reads each prefix block once for all of them on the
+ * matrix cores. The remaining partitions, the workspace and the merge are
+ * those of pa_decode_split, and the result is the same up to rounding order.
+ *
+ *   shared_prefix_tokens  tokens every sequence shares; a multiple of
+ *                     partition_size (hence of block_size); 0 gives plain
+ *                     pa_decode_partitions / pa_decode_split.
+ * Caller contract (not checked on the device): for every sequence i,
+ * block_tables[i][j] == block_tables[0][j] for j < shared_prefix_tokens /
+ * block_size, and context_lens[i] >= shared_prefix_tokens. The prefix blocks
+ * are read through row 0 of block_tables.
+ */
+pa_status pa_decode_partitions_shared_prefix(void* out, pa_dtype out_dtype, const void* query,
+                                             const void* key_cache, const void* value_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, int num_seqs,
+                                             int num_heads, int num_kv_heads, int head_dim,
+                                             int block_size, int max_blocks_per_seq,
+                                             int num_blocks, float scale, pa_dtype kv_dtype,
+                                             int partition_size, int shared_prefix_tokens,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
+pa_status pa_decode_split_shared_prefix(void* out, pa_dtype out_dtype, const void* query,
+                                        const void* key_cache, const void* value_cache,
+                                        const int32_t* block_tables,
+                                        const int32_t* context_lens, int num_seqs,
+                                        int num_heads, int num_kv_heads, int head_dim,
+                                        int block_size, int max_blocks_per_seq, int num_blocks,
+                                        float scale, pa_dtype kv_dtype, int partition_size,
+                                        int shared_prefix_tokens, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * pa_lse_merge - combine per-partition results (the second launch of
  * pa_decode_split).
  *

@@ -90,7 +90,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     const int head = bid % Hq;
     bid /= Hq;
     const int seq = bid % a.num_seqs;
-    const int part = bid / a.num_seqs;
+    const int part = bid / a.num_seqs + a.part_begin;
 
     const int Lmax = a.max_blocks_per_seq * BS;
     int L = a.context_lens[seq];
@@ -358,31 +358,38 @@ attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs) {
     return nullptr;
 }
 
-// grouped-query instances (MFMA), 2 <= num_heads / num_kv_heads <= 16
-template <class KV, class OUT, int D>
+// grouped-query instances (MFMA), 2 <= num_heads / num_kv_heads <= 16, and
+// the shared-prefix mode of the same kernel (1 <= G <= 16)
+template <class KV, class OUT, int D, bool PREFIX>
 attn_fn pick_gqa_bs(int bs) {
     switch (bs) {
-        case 16: return attn_gqa_kernel<KV, OUT, D, 16, kGqaWaves>;
-        case 32: return attn_gqa_kernel<KV, OUT, D, 32, kGqaWaves>;
+        case 16: return attn_gqa_kernel<KV, OUT, D, 16, kGqaWaves, PREFIX>;
+        case 32: return attn_gqa_kernel<KV, OUT, D, 32, kGqaWaves, PREFIX>;
     }
     return nullptr;
 }
 
-template <class KV, class OUT>
+template <class KV, class OUT, bool PREFIX>
 attn_fn pick_gqa_d(int d, int bs) {
     switch (d) {
-        case 64: return pick_gqa_bs<KV, OUT, 64>(bs);
-        case 128: return pick_gqa_bs<KV, OUT, 128>(bs);
+        case 64: return pick_gqa_bs<KV, OUT, 64, PREFIX>(bs);
+        case 128: return pick_gqa_bs<KV, OUT, 128, PREFIX>(bs);
     }
     return nullptr;
 }
 
-template <class KV>
+template <class KV, bool PREFIX = false>
 attn_fn pick_gqa_out(pa_dtype out, pa_dtype kv, int d, int bs) {
-    if (out == PA_F32) return pick_gqa_d<KV, OutF32>(d, bs);
+    if (out == PA_F32) return pick_gqa_d<KV, OutF32, PREFIX>(d, bs);
     if (out != kv) return nullptr;
-    if (kv == PA_F16) return pick_gqa_d<KV, OutF16>(d, bs);
-    return pick_gqa_d<KV, OutBF16>(d, bs);
+    if (kv == PA_F16) return pick_gqa_d<KV, OutF16, PREFIX>(d, bs);
+    return pick_gqa_d<KV, OutBF16, PREFIX>(d, bs);
+}
+
+attn_fn pick_prefix_kernel(pa_dtype kv, pa_dtype out, int d, int bs) {
+    if (kv == PA_F16) return pick_gqa_out<KvF16, true>(out, kv, d, bs);
+    if (kv == PA_BF16) return pick_gqa_out<KvBF16, true>(out, kv, d, bs);
+    return nullptr;
 }
 
 constexpr int kMaxGroupMfma = 16;
@@ -549,14 +556,23 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
                             const void* key_cache, const void* value_cache,
                             const int32_t* block_tables, const int32_t* context_lens,
                             const DecodeShape& s, float scale, pa_dtype kv_dtype,
-                            int partition_size, void* workspace, size_t workspace_bytes,
-                            void* stream, const char* what, SplitLayout* lay_out) {
+                            int partition_size, int prefix_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream, const char* what,
+                            SplitLayout* lay_out) {
     pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
                                    context_lens, s, scale, kv_dtype);
     if (st != PA_OK) return st;
     PA_REQUIRE(partition_size > 0 && partition_size % s.block_size == 0, PA_ERR_SHAPE,
                "partition_size %d must be a positive multiple of block_size %d",
                partition_size, s.block_size);
+    PA_REQUIRE(prefix_tokens >= 0 && prefix_tokens % partition_size == 0 &&
+                   (int64_t)prefix_tokens <= (int64_t)s.max_blocks_per_seq * s.block_size,
+               PA_ERR_SHAPE,
+               "shared_prefix_tokens %d must be a multiple of partition_size %d and fit "
+               "max_blocks_per_seq * block_size", prefix_tokens, partition_size);
+    PA_REQUIRE(prefix_tokens == 0 || s.num_heads / s.num_kv_heads <= kMaxGroupMfma,
+               PA_ERR_UNSUPPORTED, "shared-prefix mode needs num_heads / num_kv_heads <= %d",
+               kMaxGroupMfma);
     SplitLayout lay;
     split_layout(s.num_seqs, s.num_heads, s.head_dim, s.max_blocks_per_seq, s.block_size,
                  partition_size, &lay);
@@ -570,7 +586,11 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     int per_seq = 0, threads = 0;
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, s.num_heads,
                              s.num_kv_heads, &per_seq, &threads);
-    PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    attn_fn pfn = prefix_tokens > 0 ? pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim,
+                                                         s.block_size)
+                                    : nullptr;
+    PA_REQUIRE(fn && (prefix_tokens == 0 || pfn), PA_ERR_UNSUPPORTED,
+               "no kernel instance for this dtype/shape");
     char* ws = (char*)workspace;
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
                            scale);
@@ -579,8 +599,24 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     a.part_out = (float*)(ws + lay.off_out);
     a.partition_size = partition_size;
     a.max_partitions = lay.np;
-    const int64_t grid = (int64_t)s.num_seqs * per_seq * lay.np;
+    a.prefix_tokens = prefix_tokens;
+    const int prefix_parts = prefix_tokens / partition_size;
+    if (prefix_parts > 0) {
+        // shared prefix: 16 / G sequences x G heads per workgroup
+        const int rows = 16 / (s.num_heads / s.num_kv_heads);
+        const int64_t tiles = (s.num_seqs + rows - 1) / rows;
+        const int64_t grid = (int64_t)s.num_kv_heads * tiles * prefix_parts;
+        PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+        a.part_begin = 0;
+        hipLaunchKernelGGL(pfn, dim3((unsigned)grid), dim3(kGqaWaves * 64), 0,
+                           (hipStream_t)stream, a);
+        st = check_launch(what);
+        if (st != PA_OK) return st;
+    }
+    const int64_t grid = (int64_t)s.num_seqs * per_seq * (lay.np - prefix_parts);
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    if (grid == 0) return PA_OK;
+    a.part_begin = prefix_parts;
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, (hipStream_t)stream, a);
     return check_launch(what);
 }
@@ -617,8 +653,24 @@ extern "C" pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const v
                         max_blocks_per_seq, num_blocks};
     SplitLayout lay;
     return launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
-                             context_lens, s, scale, kv_dtype, partition_size, workspace,
+                             context_lens, s, scale, kv_dtype, partition_size, 0, workspace,
                              workspace_bytes, stream, "pa_decode_partitions", &lay);
+}
+
+extern "C" pa_status pa_decode_partitions_shared_prefix(
+    void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
+    const void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int num_blocks, float scale, pa_dtype kv_dtype, int partition_size,
+    int shared_prefix_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    SplitLayout lay;
+    return launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
+                             context_lens, s, scale, kv_dtype, partition_size,
+                             shared_prefix_tokens, workspace, workspace_bytes, stream,
+                             "pa_decode_partitions_shared_prefix", &lay);
 }
 
 extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
@@ -633,15 +685,37 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
                         max_blocks_per_seq, num_blocks};
     SplitLayout lay;
     pa_status st = launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
-                                     context_lens, s, scale, kv_dtype, partition_size, workspace,
-                                     workspace_bytes, stream, "pa_decode_split (partitions)",
-                                     &lay);
+                                     context_lens, s, scale, kv_dtype, partition_size, 0,
+                                     workspace, workspace_bytes, stream,
+                                     "pa_decode_split (partitions)", &lay);
     if (st != PA_OK || num_seqs == 0) return st;
     char* ws = (char*)workspace;
     return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
                         (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
                         context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
                         stream, "pa_decode_split (merge)");
+}
+
+extern "C" pa_status pa_decode_split_shared_prefix(
+    void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
+    const void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int num_blocks, float scale, pa_dtype kv_dtype, int partition_size,
+    int shared_prefix_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    SplitLayout lay;
+    pa_status st = launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                     context_lens, s, scale, kv_dtype, partition_size,
+                                     shared_prefix_tokens, workspace, workspace_bytes, stream,
+                                     "pa_decode_split_shared_prefix (partitions)", &lay);
+    if (st != PA_OK || num_seqs == 0) return st;
+    char* ws = (char*)workspace;
+    return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
+                        (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
+                        context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
+                        stream, "pa_decode_split_shared_prefix (merge)");
 }
 
 extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,

@@ -22,6 +22,8 @@ struct AttnArgs {
     int num_blocks;
     int partition_size;
     int max_partitions;
+    int part_begin;     // first partition index the grid covers
+    int prefix_tokens;  // shared-prefix mode: tokens every sequence shares (block_tables row 0)
     float scale_log2;  // scale * log2(e)
 };
 

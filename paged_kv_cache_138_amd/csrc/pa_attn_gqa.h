@@ -89,7 +89,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 #define PA_GQA_CHUNK 32
 #endif
 
-template <class KV, class OUT, int D, int BS, int NW>
+// PREFIX = false: a workgroup serves the G query heads of one (sequence, kv
+// head) over one partition of that sequence's context.
+// PREFIX = true (shared-prefix mode): every sequence's first prefix_tokens
+// tokens are the same physical blocks (block_tables row 0). A workgroup then
+// serves 16 / G sequences x G heads of one kv head over one partition of the
+// shared prefix, so each prefix block is read once per 16 query rows instead
+// of once per (sequence, kv head).
+template <class KV, class OUT, int D, int BS, int NW, bool PREFIX>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(AttnArgs a) {
     constexpr int CH = PA_GQA_CHUNK;    // tokens per chunk (32 or 64)
@@ -123,36 +130,54 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     const int Hq = a.num_heads;
     const int Hkv = a.num_kv_heads;
     const int G = Hq / Hkv;
-    int bid = blockIdx.x;  // (sequence, kv head, partition), kv head fastest
+    const int P = a.partition_size;
+    const int Lmax = a.max_blocks_per_seq * BS;
+    auto ctx_len = [&](int sq) {
+        const int l = a.context_lens[sq];
+        return l < 0 ? 0 : (l > Lmax ? Lmax : l);
+    };
+    int bid = blockIdx.x;  // kv head fastest, then sequence (or row tile), then partition
     const int kvh = bid % Hkv;
     bid /= Hkv;
-    const int seq = bid % a.num_seqs;
-    const int part = bid / a.num_seqs;
-
-    const int Lmax = a.max_blocks_per_seq * BS;
-    int L = a.context_lens[seq];
-    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-    const int P = a.partition_size;
-    const int nparts = (L + P - 1) / P;
-    if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+    // rows of every product: row r is query head r_head of sequence r_seq
+    const int R = PREFIX ? 16 / G : 1;  // sequences per workgroup
+    int seq0, part, Lsrc, nparts = 0;
+    const int32_t* bt;
+    if constexpr (PREFIX) {
+        const int ntiles = (a.num_seqs + R - 1) / R;
+        seq0 = (bid % ntiles) * R;
+        part = bid / ntiles + a.part_begin;
+        Lsrc = a.prefix_tokens;
+        bt = a.block_tables;  // the shared prefix, as row 0 lists it
+    } else {
+        seq0 = bid % a.num_seqs;
+        part = bid / a.num_seqs + a.part_begin;
+        Lsrc = ctx_len(seq0);
+        nparts = (Lsrc + P - 1) / P;
+        if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+        bt = a.block_tables + (size_t)seq0 * a.max_blocks_per_seq;
+    }
     const int start = part * P;
-    const int end = min(start + P, L);
-    const int nb = (L + BS - 1) / BS;
+    const int end = min(start + P, Lsrc);
+    const int nb = (Lsrc + BS - 1) / BS;
+    auto row_seq = [&](int r) { return seq0 + r / G; };
+    auto row_head = [&](int r) { return kvh * G + r % G; };
+    auto row_ok = [&](int r) { return r < R * G && row_seq(r) < a.num_seqs; };
 
     const size_t row_bytes = (size_t)Hkv * D * 2;
     const size_t block_bytes = row_bytes * BS;
     const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
     const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
-    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
     // the wave's LDS tile holds the current chunk's K rows, then its V rows
     // (a wave's LDS operations complete in order)
     char* tile = sm_v[wave];
 
-    // Qᵀ operand: lane (g, n) holds q[head n][32j + 8g .. +7]; padding heads are 0
+    // Qᵀ operand: lane (g, n) holds row n's q[32j + 8g .. +7]; unused rows are 0
     u32x4 qb[NJ];
     {
-        const bool real = n < G;
-        const uint16_t* qrow = a.query + ((size_t)seq * Hq + (size_t)kvh * G + (real ? n : 0)) * D;
+        const bool real = row_ok(n);
+        const uint16_t* qrow =
+            a.query + ((size_t)(real ? row_seq(n) : 0) * Hq + (real ? row_head(n) : 0)) * D;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             qb[j] = u32x4{0u, 0u, 0u, 0u};
@@ -320,11 +345,11 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     }
     __syncthreads();
 
-    // ---- merge the waves; every thread finishes some (head, dim) pairs ----
-    const size_t sh0 = (size_t)seq * Hq + (size_t)kvh * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    // ---- merge the waves; every thread finishes some (row, dim) pairs ------
+    for (int idx = threadIdx.x; idx < R * G * D; idx += NW * 64) {
         const int h = idx / D;
         const int d = idx - h * D;
+        if (!row_ok(h)) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
@@ -336,8 +361,9 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             o += wt * ((const float*)sm_v[w])[h * OROW + d];
         }
         const float res = tot > 0.f ? o / tot : 0.f;
-        const size_t sh = sh0 + h;
-        if (nparts <= 1) {
+        const size_t sh = (size_t)row_seq(h) * Hq + row_head(h);
+        const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : nparts;
+        if (np <= 1) {
             OUT::store(a.out, sh * D + d, res);
         } else {
             const size_t pidx = sh * a.max_partitions + part;

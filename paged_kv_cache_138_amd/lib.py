@@ -56,6 +56,10 @@ def load():
     lib.pa_decode_split.restype = i32
     lib.pa_decode_partitions.argtypes = dec + [i32, vp, sz, vp]
     lib.pa_decode_partitions.restype = i32
+    lib.pa_decode_partitions_shared_prefix.argtypes = dec + [i32, i32, vp, sz, vp]
+    lib.pa_decode_partitions_shared_prefix.restype = i32
+    lib.pa_decode_split_shared_prefix.argtypes = dec + [i32, i32, vp, sz, vp]
+    lib.pa_decode_split_shared_prefix.restype = i32
     lib.pa_decode_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_split_workspace_bytes.restype = sz
     lib.pa_lse_merge.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
@@ -176,17 +180,18 @@ def make_workspace(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size
 
 
 def _split_call(name, query, key_cache, value_cache, block_tables, context_lens, scale, partition_size,
-                workspace, out, out_dtype):
+                workspace, out, out_dtype, prefix=None):
     out, (B, Hq, Hkv, D, BS, MB, NB) = _decode_common(
         query, key_cache, value_cache, block_tables, context_lens, out, out_dtype)
     if workspace is None:
         workspace = make_workspace(B, Hq, D, MB, BS, partition_size, query.device)
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
+    extra = [] if prefix is None else [int(prefix)]
     st = getattr(load(), name)(_ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache),
                                _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv,
                                D, BS, MB, NB, float(scale), _DT[key_cache.dtype], int(partition_size),
-                               _ptr(workspace), nbytes, _stream(query))
+                               *extra, _ptr(workspace), nbytes, _stream(query))
     _check(st, name)
     return out
 
@@ -204,6 +209,26 @@ def decode_partitions(query, key_cache, value_cache, block_tables, context_lens,
     get their output, the others leave per-partition rows in `workspace`."""
     return _split_call("pa_decode_partitions", query, key_cache, value_cache, block_tables,
                        context_lens, scale, partition_size, workspace, out, out_dtype)
+
+
+def decode_split_shared_prefix(query, key_cache, value_cache, block_tables, context_lens, scale,
+                               shared_prefix_tokens, partition_size=512, workspace=None, out=None,
+                               out_dtype=None):
+    """decode_split for a batch whose sequences all begin with the same
+    shared_prefix_tokens tokens (the blocks of block_tables row 0); the prefix
+    partitions are computed once per 16 query rows."""
+    return _split_call("pa_decode_split_shared_prefix", query, key_cache, value_cache, block_tables,
+                       context_lens, scale, partition_size, workspace, out, out_dtype,
+                       prefix=shared_prefix_tokens)
+
+
+def decode_partitions_shared_prefix(query, key_cache, value_cache, block_tables, context_lens, scale,
+                                    shared_prefix_tokens, partition_size=512, workspace=None,
+                                    out=None, out_dtype=None):
+    """The partition launches of decode_split_shared_prefix alone."""
+    return _split_call("pa_decode_partitions_shared_prefix", query, key_cache, value_cache,
+                       block_tables, context_lens, scale, partition_size, workspace, out, out_dtype,
+                       prefix=shared_prefix_tokens)
 
 
 def workspace_views(workspace, num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,

@@ -39,7 +39,8 @@ def to_host_f64(t):
 class DeviceBatch:
     """GPU copies of a workloads.Batch plus the step's output buffers."""
 
-    def __init__(self, batch, device="cuda", out_dtype=None, split=True, partition_size=None):
+    def __init__(self, batch, device="cuda", out_dtype=None, split=True, partition_size=None,
+                 shared_prefix=False):
         w = batch.workload
         self.batch = batch
         self.device = device
@@ -55,6 +56,11 @@ class DeviceBatch:
         self.scale = batch.scale
         self.split = split
         self.partition_size = partition_size or w.partition_size
+        # shared-prefix launches when every sequence starts with the same
+        # blocks and the prefix is a whole number of partitions
+        pt = w.shared_prefix_tokens
+        self.prefix_tokens = pt if (shared_prefix and split and pt > 0
+                                    and pt % self.partition_size == 0) else 0
         B, Hq, D = self.query.shape
         od = out_dtype if out_dtype is not None else self.query.dtype
         self.out = torch.empty((B, Hq, D), dtype=od, device=device)
@@ -68,7 +74,13 @@ class DeviceBatch:
                                 self.slot_mapping)
 
     def partitions(self):
-        """Split path, first launch only (see lib.decode_partitions)."""
+        """Split path, partition launches only (see lib.decode_partitions)."""
+        if self.prefix_tokens:
+            palib.decode_partitions_shared_prefix(
+                self.query, self.key_cache, self.value_cache, self.block_tables, self.context_lens,
+                self.scale, self.prefix_tokens, self.partition_size, workspace=self.workspace,
+                out=self.out)
+            return
         palib.decode_partitions(self.query, self.key_cache, self.value_cache, self.block_tables,
                                 self.context_lens, self.scale, self.partition_size,
                                 workspace=self.workspace, out=self.out)
@@ -81,7 +93,12 @@ class DeviceBatch:
         palib.lse_merge(po, pm, ps, self.context_lens, self.partition_size, out=self.out)
 
     def attend(self):
-        if self.split:
+        if self.split and self.prefix_tokens:
+            palib.decode_split_shared_prefix(
+                self.query, self.key_cache, self.value_cache, self.block_tables, self.context_lens,
+                self.scale, self.prefix_tokens, self.partition_size, workspace=self.workspace,
+                out=self.out)
+        elif self.split:
             palib.decode_split(self.query, self.key_cache, self.value_cache, self.block_tables,
                                self.context_lens, self.scale, self.partition_size,
                                workspace=self.workspace, out=self.out)
@@ -113,6 +130,7 @@ class RotatedBatch(DeviceBatch):
         self.scale = src.scale
         self.split = src.split
         self.partition_size = src.partition_size
+        self.prefix_tokens = src.prefix_tokens
         bt = src.block_tables
         used = torch.unique(bt[bt >= 0])
         n = int(used.numel())

@@ -41,7 +41,8 @@ def test_full_size_workload(name):
     print("full-size parity:", name, flush=True)
     b = W.make_batch(w, seed=0)
     path = bench.default_path(w)
-    db = DeviceBatch(b, out_dtype=None, split=(path == "split"))
+    db = DeviceBatch(b, out_dtype=None, split=path.startswith("split"),
+                     shared_prefix=(path == "split_prefix"))
     out = db.step()
     torch.cuda.synchronize()
     got = to_host_f64(out)
