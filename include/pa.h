@@ -162,8 +162,9 @@ pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
  * pa_decode_partitions - the first launch of pa_decode_split on its own.
  *
  * Same arguments as pa_decode_split. One workgroup handles one partition of
- * one (sequence, head) - of one (sequence, kv head) when 2..16 query heads
- * share a kv head. A sequence with a single partition (L_i <= partition_size)
+ * one (sequence, head) - of two adjacent heads when the grid is large
+ * compared with the device, and of one (sequence, kv head) when 2..16 query
+ * heads share a kv head. A sequence with a single partition (L_i <= partition_size)
  * gets its final output in `out`; for the others each partition p stores its
  * row of the workspace: part_max = the largest scaled logit (natural-log
  * units), part_sum = Σ exp(s - part_max), part_out = the normalised partial

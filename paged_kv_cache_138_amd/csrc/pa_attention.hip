@@ -30,6 +30,9 @@
 
 #include <math.h>
 
+#include <mutex>
+#include <unordered_map>
+
 namespace pa {
 namespace {
 
@@ -69,7 +72,6 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     constexpr int NI = LPR;             // load instructions per chunk
     constexpr int CHUNK = RPI * NI;     // tokens per chunk (64)
     constexpr int BPC = CHUNK / BS;     // blocks per chunk
-    constexpr int DPL = D / 64;         // output elements per lane in the epilogue
     static_assert(CHUNK == 64, "one score per lane per chunk");
     static_assert(BS % RPI == 0 && CHUNK % BS == 0, "block must tile the chunk");
     static_assert(LPR == 8 || LPR == 16, "head_dim 64 or 128");
@@ -78,19 +80,32 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     __shared__ float sm_l[NW];
     __shared__ float sm_acc[NW][D];
 
-    const int lane = threadIdx.x & 63;
     // the wave index is uniform inside a wavefront; saying so keeps every
     // chunk, block-table and address computation in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = lane / LPR;  // row within a load instruction
-    const int c = lane % LPR;  // 8-element slice of the row
 
+    // the workgroup serves 2^heads_log2 adjacent query heads of one
+    // (sequence, partition); each head gets NW / 2^heads_log2 waves, which
+    // take the partition's 64-token chunks in turn. Adjacent heads' rows are
+    // adjacent in a cache row, so serving several heads at once reads longer
+    // contiguous runs of each block at about the same time.
+    constexpr int LOG_NW = NW == 4 ? 2 : (NW == 2 ? 1 : 0);
+    static_assert((1 << LOG_NW) == NW, "NW must be 1, 2 or 4");
+    const int hl = a.heads_log2;
+    const int nwh = NW >> hl;                     // waves per head
+    const int hslot = wave >> (LOG_NW - hl);      // head within the workgroup
+    const int sub = wave & (nwh - 1);             // wave within the head
     const int Hq = a.num_heads;
-    int bid = blockIdx.x;  // (sequence, query head, partition), head fastest
-    const int head = bid % Hq;
-    bid /= Hq;
+    const int ngroups = Hq >> hl;
+
+    int bid = blockIdx.x;  // (sequence, head group, partition), head group fastest
+    const int head = (bid % ngroups) * (1 << hl) + hslot;
+    bid /= ngroups;
     const int seq = bid % a.num_seqs;
     const int part = bid / a.num_seqs + a.part_begin;
+    const int lane = threadIdx.x & 63;
+    const int r = lane / LPR;  // row within a load instruction
+    const int c = lane % LPR;  // 8-element slice of the row
 
     const int Lmax = a.max_blocks_per_seq * BS;
     int L = a.context_lens[seq];
@@ -108,10 +123,9 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
     const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-    // byte offsets, inside a block, of the rows this lane reads
-    uint32_t loff[IPB];
-#pragma unroll
-    for (int j = 0; j < IPB; ++j) loff[j] = (uint32_t)((j * RPI + r) * row_bytes + c * 16);
+    // byte offset, inside a block, of the first row this lane reads; load j
+    // of a block reads RPI * j rows further
+    const uint32_t loff0 = (uint32_t)(r * row_bytes + c * 16);
 
     const u32x4 q = *(const u32x4*)(a.query + ((size_t)seq * Hq + head) * D + c * 8);
 
@@ -144,10 +158,15 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         }
     };
     auto issue = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[NI]) {
+        // recomputing the IPB offsets here (one add each) keeps them out of
+        // the registers that live across the chunk loop
+        uint32_t o = loff0;
+        asm volatile("" : "+v"(o));
 #pragma unroll
         for (int b = 0; b < BPC; ++b) {
 #pragma unroll
-            for (int j = 0; j < IPB; ++j) buf[b * IPB + j] = buffer_load16(rs[b], loff[j]);
+            for (int j = 0; j < IPB; ++j)
+                buf[b * IPB + j] = buffer_load16(rs[b], o + (uint32_t)(j * RPI * row_bytes));
         }
     };
     // scores of the chunk's 64 tokens, one per lane (log2 units, -inf if absent)
@@ -215,7 +234,8 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
 
     // ---- chunks, software-pipelined: the next chunk's K is in flight during
     // this chunk's p·V, and its V during the next score pass -----------------
-    int cs = start + wave * CHUNK;
+    int cs = start + sub * CHUNK;
+    const int cstep = nwh * CHUNK;
     if (cs < end) {
         ChunkIds cur;
         u32x4 kr[NI], vr[NI];
@@ -223,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         issue(cur.k, kr);
         issue(cur.v, vr);
         for (;;) {
-            const int nx = cs + NW * CHUNK;
+            const int nx = cs + cstep;
             const bool more = nx < end;
             ChunkIds nxt;
             if (more) fetch_ids(nx, nxt);
@@ -257,22 +277,28 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     }
     __syncthreads();
 
+    // the waves hslot*nwh .. hslot*nwh + nwh - 1 hold this head's states
+    const int w0 = hslot * nwh;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w]);
+    for (int w = 0; w < nwh; ++w) M = fmaxf(M, sm_m[w0 + w]);
     float wt[NW];
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        wt[w] = sm_m[w] == -INFINITY ? 0.f : fast_exp2(sm_m[w] - M);
-        tot += wt[w] * sm_l[w];
+        wt[w] = 0.f;
+        if (w < nwh) {
+            const float mw = sm_m[w0 + w];
+            if (mw != -INFINITY) wt[w] = fast_exp2(mw - M);
+            tot += wt[w] * sm_l[w0 + w];
+        }
     }
     const size_t sh = (size_t)seq * Hq + head;
     const size_t pidx = sh * a.max_partitions + part;
-    for (int d = threadIdx.x; d < D; d += NW * 64) {
+    for (int d = sub * 64 + lane; d < D; d += nwh * 64) {
         float t = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) t += wt[w] * sm_acc[w][d];
+        for (int w = 0; w < NW; ++w)
+            if (w < nwh) t += wt[w] * sm_acc[w0 + w][d];
         const float o = tot > 0.f ? t / tot : 0.f;
         if (nparts <= 1) {
             OUT::store(a.out, sh * D + d, o);
@@ -280,7 +306,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
             a.part_out[pidx * D + d] = o;
         }
     }
-    if (nparts > 1 && threadIdx.x == 0) {
+    if (nparts > 1 && sub == 0 && lane == 0) {
         a.part_max[pidx] = M * kLn2;  // natural-log units
         a.part_sum[pidx] = tot;
     }
@@ -399,9 +425,47 @@ bool use_gqa(int num_heads, int num_kv_heads) {
     return g >= 2 && g <= kMaxGroupMfma;
 }
 
+// Query heads per workgroup of the MHA kernel on the split path (log2).
+// One head per workgroup gives the finest work units, which matters when
+// the grid is only a few times what the device holds at once (the last,
+// ragged units then decide the end of the kernel). When the grid is many
+// times larger - many sequences or long maximum contexts, where most of the
+// (sequence, partition) rectangle may be empty - two adjacent heads per
+// workgroup halve the workgroups to dispatch and read each block row's
+// heads side by side. The single-pass path keeps one head per workgroup, so
+// that a sequence's context is spread over all the waves of its workgroup.
+int mha_heads_log2(int num_heads, int64_t rect_workgroups, int resident, bool split) {
+    if (!split || num_heads % 2 != 0) return 0;
+    return rect_workgroups / 2 >= (int64_t)6 * resident ? 1 : 0;
+}
+
+// Workgroups of fn that fit on the current device at once (at least 1).
+int resident_workgroups(const void* fn, int threads) {
+    static std::mutex mu;
+    static std::unordered_map<const void*, int> per_cu;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 1;
+        cus[dev] = n > 0 ? n : 1;
+    }
+    auto it = per_cu.find(fn);
+    if (it == per_cu.end()) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess)
+            n = 1;
+        it = per_cu.emplace(fn, n > 0 ? n : 1).first;
+    }
+    return it->second * cus[dev];
+}
+
 // kernel and grid width (workgroups per sequence and partition)
 attn_fn pick_kernel(pa_dtype kv, pa_dtype out, int d, int bs, int num_heads, int num_kv_heads,
-                    int* per_seq, int* threads) {
+                    int heads_log2, int* per_seq, int* threads) {
     *threads = kWaves * 64;
     if (use_gqa(num_heads, num_kv_heads)) {
         *per_seq = num_kv_heads;
@@ -410,7 +474,7 @@ attn_fn pick_kernel(pa_dtype kv, pa_dtype out, int d, int bs, int num_heads, int
         if (kv == PA_BF16) return pick_gqa_out<KvBF16>(out, kv, d, bs);
         return nullptr;
     }
-    *per_seq = num_heads;
+    *per_seq = num_heads >> heads_log2;
     return pick_attn(kv, out, d, bs);
 }
 
@@ -509,6 +573,7 @@ bool split_layout(int num_seqs, int num_heads, int head_dim, int max_blocks_per_
     return true;
 }
 
+
 }  // namespace
 }  // namespace pa
 
@@ -527,11 +592,13 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
                                    context_lens, s, scale, kv_dtype);
     if (st != PA_OK || num_seqs == 0) return st;
     int per_seq = 0, threads = 0;
+    const int hl = 0;  // one head per workgroup: its waves share the whole context
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, head_dim, block_size, num_heads, num_kv_heads,
-                             &per_seq, &threads);
+                             hl, &per_seq, &threads);
     PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
                            scale);
+    a.heads_log2 = hl;
     a.partition_size = max_blocks_per_seq * block_size;  // one partition per sequence
     a.max_partitions = 1;
     const int64_t grid = (int64_t)num_seqs * per_seq;
@@ -583,9 +650,17 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
                "workspace must be 256-byte aligned");
     PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
                "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+    const int prefix_parts = prefix_tokens / partition_size;
     int per_seq = 0, threads = 0;
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, s.num_heads,
-                             s.num_kv_heads, &per_seq, &threads);
+                             s.num_kv_heads, 0, &per_seq, &threads);
+    int hl = 0;
+    if (fn && !use_gqa(s.num_heads, s.num_kv_heads)) {
+        const int64_t rect = (int64_t)s.num_seqs * s.num_heads * (lay.np - prefix_parts);
+        hl = mha_heads_log2(s.num_heads, rect, resident_workgroups((const void*)fn, threads),
+                            true);
+        per_seq = s.num_heads >> hl;
+    }
     attn_fn pfn = prefix_tokens > 0 ? pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim,
                                                          s.block_size)
                                     : nullptr;
@@ -600,7 +675,7 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     a.partition_size = partition_size;
     a.max_partitions = lay.np;
     a.prefix_tokens = prefix_tokens;
-    const int prefix_parts = prefix_tokens / partition_size;
+    a.heads_log2 = hl;
     if (prefix_parts > 0) {
         // shared prefix: 16 / G sequences x G heads per workgroup
         const int rows = 16 / (s.num_heads / s.num_kv_heads);

@@ -5,6 +5,7 @@
 
 namespace pa {
 
+
 struct AttnArgs {
     void* out;
     const uint16_t* query;
@@ -24,6 +25,7 @@ struct AttnArgs {
     int max_partitions;
     int part_begin;     // first partition index the grid covers
     int prefix_tokens;  // shared-prefix mode: tokens every sequence shares (block_tables row 0)
+    int heads_log2;     // MHA kernel: log2 of the query heads one workgroup serves (0, 1, 2)
     float scale_log2;  // scale * log2(e)
 };
 

@@ -69,6 +69,14 @@ SMALL_CASES = [
          num_blocks=200, max_blocks_per_seq=64, lens="uniform:200:1000"),
     dict(num_seqs=6, num_heads=4, num_kv_heads=1, head_dim=64, dtype="bf16", block_size=32,
          num_blocks=64, max_blocks_per_seq=8, lens="uniform:1:256"),
+    # MHA head counts that give the split path 1 and 2 heads per workgroup,
+    # and a group too large for the MFMA kernel (34 query heads on one kv head)
+    dict(num_seqs=4, num_heads=3, num_kv_heads=3, head_dim=128, dtype="f16", block_size=32,
+         num_blocks=128, max_blocks_per_seq=32, lens="uniform:1:900"),
+    dict(num_seqs=3, num_heads=6, num_kv_heads=6, head_dim=64, dtype="bf16", block_size=16,
+         num_blocks=96, max_blocks_per_seq=32, lens="uniform:1:500"),
+    dict(num_seqs=3, num_heads=34, num_kv_heads=1, head_dim=64, dtype="bf16", block_size=16,
+         num_blocks=64, max_blocks_per_seq=20, lens="uniform:1:300"),
 ]
 
 
