@@ -161,7 +161,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         // recomputing the IPB offsets here (one add each) keeps them out of
         // the registers that live across the chunk loop
         uint32_t o = loff0;
-        asm volatile("" : "+v"(o));
+        asm("" : "+v"(o));
 #pragma unroll
         for (int b = 0; b < BPC; ++b) {
 #pragma unroll
@@ -220,7 +220,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
             // unpacked values would be live at once
             uint32_t x = vr[i].x, y = vr[i].y, z = vr[i].z, w = vr[i].w;
             if constexpr (std::is_same<KV, KvBF16>::value)
-                asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w) : "v"(pb));
+                asm("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w) : "v"(pb));
             acc[0] += pb * KV::lo(x);
             acc[1] += pb * KV::hi(x);
             acc[2] += pb * KV::lo(y);
@@ -437,6 +437,17 @@ bool use_gqa(int num_heads, int num_kv_heads) {
 int mha_heads_log2(int num_heads, int64_t rect_workgroups, int resident, bool split) {
     if (!split || num_heads % 2 != 0) return 0;
     return rect_workgroups / 2 >= (int64_t)6 * resident ? 1 : 0;
+}
+
+#ifndef PA_GQA_HEADS
+#define PA_GQA_HEADS 2
+#endif
+// kv heads per workgroup of the grouped-query kernel on the split path (log2)
+int gqa_heads_log2(int num_kv_heads) {
+    int hl = 0;
+    while ((2 << hl) <= PA_GQA_HEADS && (2 << hl) <= kGqaWaves && num_kv_heads % (2 << hl) == 0)
+        ++hl;
+    return hl;
 }
 
 // Workgroups of fn that fit on the current device at once (at least 1).
@@ -660,6 +671,9 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
         hl = mha_heads_log2(s.num_heads, rect, resident_workgroups((const void*)fn, threads),
                             true);
         per_seq = s.num_heads >> hl;
+    } else if (fn) {
+        hl = gqa_heads_log2(s.num_kv_heads);
+        per_seq = s.num_kv_heads >> hl;
     }
     attn_fn pfn = prefix_tokens > 0 ? pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim,
                                                          s.block_size)

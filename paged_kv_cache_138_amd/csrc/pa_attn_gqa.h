@@ -136,9 +136,21 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         const int l = a.context_lens[sq];
         return l < 0 ? 0 : (l > Lmax ? Lmax : l);
     };
-    int bid = blockIdx.x;  // kv head fastest, then sequence (or row tile), then partition
-    const int kvh = bid % Hkv;
-    bid /= Hkv;
+    // Without a shared prefix the workgroup may serve 2^heads_log2 adjacent
+    // kv heads of one (sequence, partition), each with NW / 2^heads_log2
+    // waves taking the partition's chunks in turn: adjacent kv heads' rows
+    // are adjacent in a cache row, so their reads run side by side.
+    constexpr int LOG_NW = NW == 4 ? 2 : (NW == 2 ? 1 : 0);
+    static_assert((1 << LOG_NW) == NW, "NW must be 1, 2 or 4");
+    const int hl = PREFIX ? 0 : a.heads_log2;
+    const int nwh = NW >> hl;                 // waves per kv head
+    const int hslot = wave >> (LOG_NW - hl);  // kv head within the workgroup
+    const int sub = wave & (nwh - 1);         // wave within the kv head
+    const int ngroups = Hkv >> hl;
+    int bid = blockIdx.x;  // kv head group fastest, then sequence (or row tile), then partition
+    const int kvh0 = (bid % ngroups) << hl;
+    const int kvh = kvh0 + hslot;
+    bid /= ngroups;
     // rows of every product: row r is query head r_head of sequence r_seq
     const int R = PREFIX ? 16 / G : 1;  // sequences per workgroup
     int seq0, part, Lsrc, nparts = 0;
@@ -228,11 +240,16 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         for (int i = 0; i < VL; ++i) *(u32x4*)(tile + (vr + RPI * i) * ROWB + vc * 16) = buf[i];
     };
 
-    auto process = [&](int cs, const ChunkIds& ci, const u32x4 (&kb)[VL], bool has_next,
+    // The next chunk's loads are issued on every pass, also after the last
+    // chunk, where its descriptors have no range and the loads return zeros
+    // without touching memory: a load issued only on some paths would make
+    // the wait counts of every path assume it absent, and each wait for
+    // this chunk's V would then also wait for the next chunk's K.
+    auto process = [&](int cs, const ChunkIds& ci, const u32x4 (&kb)[VL],
                        auto&& prefetch_k, const u32x4 (&vb)[VL], auto&& prefetch_v) {
         // ---- scores Sᵀ: lane (g, n) gets head n, tokens 16s + 4g + k ------
         to_lds(tile, kb);
-        if (has_next) prefetch_k();
+        prefetch_k();
         f32x4 sc[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -290,7 +307,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         }
         // ---- V rows into the tile (after the K reads), Vᵀ by transpose reads
         to_lds(tile, vb);
-        if (has_next) prefetch_v();
+        prefetch_v();
         const int e4 = n >> 2, q4 = n & 3;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
@@ -308,7 +325,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         }
     };
 
-    int cs = start + wave * CH;
+    int cs = start + sub * CH;
     if (cs < end) {
         ChunkIds cur;
         u32x4 kb[VL], vb[VL];
@@ -316,12 +333,11 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         issue_k(cur, kb);
         issue_v(cur, vb);
         for (;;) {
-            const int nx = cs + NW * CH;
+            const int nx = cs + nwh * CH;
             const bool more = nx < end;
             ChunkIds nxt;
-            if (more) fetch_ids(nx, nxt);
-            process(cs, cur, kb, more, [&] { issue_k(nxt, kb); }, vb,
-                    [&] { issue_v(nxt, vb); });
+            fetch_ids(nx, nxt);  // descriptors without range when !more
+            process(cs, cur, kb, [&] { issue_k(nxt, kb); }, vb, [&] { issue_v(nxt, vb); });
             if (!more) break;
             cur = nxt;
             cs = nx;
@@ -345,23 +361,30 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     }
     __syncthreads();
 
-    // ---- merge the waves; every thread finishes some (row, dim) pairs ------
-    for (int idx = threadIdx.x; idx < R * G * D; idx += NW * 64) {
-        const int h = idx / D;
-        const int d = idx - h * D;
+    // ---- merge the waves of each kv head; every thread finishes some
+    // (kv head, row, dim) triples ------------------------------------------
+    for (int idx = threadIdx.x; idx < (R * G * D << hl); idx += NW * 64) {
+        const int hs = idx / (R * G * D);
+        const int h = idx / D - hs * (R * G);
+        const int d = idx % D;
         if (!row_ok(h)) continue;
+        const int w0 = hs * nwh;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+        for (int w = 0; w < NW; ++w)
+            if (w < nwh) M = fmaxf(M, sm_m[w0 + w][h]);
         float tot = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float wt = sm_m[w][h] == -INFINITY ? 0.f : fast_exp2(sm_m[w][h] - M);
-            tot += wt * sm_l[w][h];
-            o += wt * ((const float*)sm_v[w])[h * OROW + d];
+            if (w < nwh) {
+                const float mw = sm_m[w0 + w][h];
+                const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+                tot += wt * sm_l[w0 + w][h];
+                o += wt * ((const float*)sm_v[w0 + w])[h * OROW + d];
+            }
         }
         const float res = tot > 0.f ? o / tot : 0.f;
-        const size_t sh = (size_t)row_seq(h) * Hq + row_head(h);
+        const size_t sh = (size_t)row_seq(h) * Hq + (kvh0 + hs) * G + h % G;
         const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : nparts;
         if (np <= 1) {
             OUT::store(a.out, sh * D + d, res);

@@ -77,6 +77,10 @@ SMALL_CASES = [
          num_blocks=96, max_blocks_per_seq=32, lens="uniform:1:500"),
     dict(num_seqs=3, num_heads=34, num_kv_heads=1, head_dim=64, dtype="bf16", block_size=16,
          num_blocks=64, max_blocks_per_seq=20, lens="uniform:1:300"),
+    # four kv heads of four query heads each: the split path may serve
+    # several adjacent kv heads per workgroup
+    dict(num_seqs=5, num_heads=16, num_kv_heads=4, head_dim=128, dtype="f16", block_size=16,
+         num_blocks=200, max_blocks_per_seq=40, lens="uniform:1:640"),
 ]
 
 
