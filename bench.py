@@ -1,9 +1,11 @@
 """Benchmark one decode step of paged attention on one MI355X.
 
 A step is the whole hot path over one seeded synthetic batch: the new
-tokens' K/V are scattered into their slots (pa_reshape_and_cache), then
-every sequence's query attends over its paged context (pa_decode, or
-pa_decode_split for the long-context workloads). Inputs are resident in HBM
+tokens' K/V are scattered into their slots and every sequence's query attends
+over its paged context. On the split path (every workload without a shared
+prefix) both happen in pa_decode_split_append, whose partition launch stores
+each new row and attends to it, then the merge; with --unfused, or with a
+shared prefix, pa_reshape_and_cache runs first as its own launch. Inputs are resident in HBM
 before timing starts; the timed loop cycles through copies of the batch whose
 blocks sit at different physical places, so no step re-reads the previous
 step's blocks out of the 256 MB last-level cache.
@@ -37,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--path", choices=["auto", "decode", "split", "split_prefix"], default="auto")
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--unfused", action="store_true",
+                    help="split path: run the scatter as its own launch instead of inside the "
+                         "partition launch (pa_decode_split_append)")
     ap.add_argument("--out-dtype", choices=["native", "f32"], default="native")
     ap.add_argument("--rotations", type=int, default=0, help="batch copies cycled (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
@@ -175,7 +180,9 @@ def main():
     with torch.cuda.stream(stream):
         base = DeviceBatch(batch, out_dtype=out_dtype, split=path.startswith("split"),
                            partition_size=args.partition_size,
-                           shared_prefix=(path == "split_prefix"))
+                           shared_prefix=(path == "split_prefix"),
+                           fused=(path == "split" and not args.unfused))
+        fused = base.fused
         unique_bytes, logical_bytes = W.step_bytes(batch, None if out_dtype is None else "f32")
         write_bytes = W.cache_write_bytes(batch)
         # rotation copies: enough that the cycle's footprint is >= 8x the LLC
@@ -243,7 +250,8 @@ def main():
         "config": {"workload": w.name, "description": w.description, "num_seqs": B,
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "sum_context_lens": int(batch.context_lens.sum()),
-                   "path": path, "partition_size": base_partition(path, args, w),
+                   "path": path, "fused_append": fused,
+                   "partition_size": base_partition(path, args, w),
                    "out_dtype": args.out_dtype, "rotations": R, "seed": args.seed},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seq_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
@@ -252,9 +260,10 @@ def main():
                        "cache_write": write_bytes},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic("%s/%s" % (w.name, path)),
+                     "traffic": stored_traffic(traffic_key(w.name, path, fused)),
                      "kernel": "%s: %d back-to-back launches between HIP events, avg %.2f us"
-                               % ({"split": "pa_decode_partitions", "decode": "pa_decode",
+                               % ("pa_decode_partitions_append" if fused else
+                                  {"split": "pa_decode_partitions", "decode": "pa_decode",
                                    "split_prefix": "pa_decode_partitions_shared_prefix (prefix "
                                                    "and suffix kernels)"}[path], K,
                                   attn_avg_ms * 1e3)},
@@ -263,6 +272,10 @@ def main():
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def traffic_key(name, path, fused):
+    return "%s/%s%s" % (name, path, "+append" if fused else "")
 
 
 def base_partition(path, args, w):

@@ -159,6 +159,55 @@ pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_split_append - one decode step's scatter and attention in the
+ * launches of pa_decode_split ("vLLM PagedAttention深度解析与工程实践" §二:
+ * each step appends the new token's K/V, then attends over the sequence).
+ *
+ * Same arguments as pa_decode_split (the caches are written), plus the step's
+ * new rows, one token per sequence:
+ *   new_key, new_value  [num_seqs, num_kv_heads, head_dim] in kv_dtype, token
+ *                     i at element offset i * new_*_token_stride (16-byte
+ *                     aligned, strides >= num_kv_heads*head_dim and multiples
+ *                     of 8, so fused QKV buffers can be passed directly).
+ *   slot_mapping      int64 [num_seqs]: the cache slot of sequence i's new
+ *                     token; negative = no token (padding).
+ * Effect: pa_reshape_and_cache(new_key, new_value, key_cache, value_cache,
+ * slot_mapping, num_seqs, ...) followed by pa_decode_split(...), with the
+ * same result up to rounding order, provided that, for every sequence with a
+ * slot in [0, num_blocks*block_size) and L_i >= 1, that slot is the one its
+ * block table gives position L_i - 1 (block_tables[i][(L_i-1)/block_size] *
+ * block_size + (L_i-1) % block_size): the new token is the last one
+ * attended to. The workgroups of the partition that holds position L_i - 1
+ * take the token's rows from new_key/new_value rather than from the cache,
+ * and store them into the slot; slots outside the cache are skipped, as the
+ * scatter skips them. Not checked on the device.
+ */
+pa_status pa_decode_split_append(void* out, pa_dtype out_dtype, const void* query,
+                                 void* key_cache, void* value_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const void* new_key, const void* new_value,
+                                 const int64_t* slot_mapping, int64_t new_key_token_stride,
+                                 int64_t new_value_token_stride, int num_seqs, int num_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int num_blocks, float scale,
+                                 pa_dtype kv_dtype, int partition_size, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* The partition launch of pa_decode_split_append on its own (the merge is
+ * pa_lse_merge), as pa_decode_partitions is for pa_decode_split. */
+pa_status pa_decode_partitions_append(void* out, pa_dtype out_dtype, const void* query,
+                                      void* key_cache, void* value_cache,
+                                      const int32_t* block_tables,
+                                      const int32_t* context_lens, const void* new_key,
+                                      const void* new_value, const int64_t* slot_mapping,
+                                      int64_t new_key_token_stride,
+                                      int64_t new_value_token_stride, int num_seqs,
+                                      int num_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      float scale, pa_dtype kv_dtype, int partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_partitions - the first launch of pa_decode_split on its own.
  *
  * Same arguments as pa_decode_split. One workgroup handles one partition of

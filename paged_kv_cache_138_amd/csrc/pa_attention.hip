@@ -79,6 +79,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     __shared__ float sm_m[NW];
     __shared__ float sm_l[NW];
     __shared__ float sm_acc[NW][D];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_new[NW][2][D];  // fused append: new K, V rows
 
     // the wave index is uniform inside a wavefront; saying so keeps every
     // chunk, block-table and address computation in scalar registers
@@ -129,6 +130,29 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
 
     const u32x4 q = *(const u32x4*)(a.query + ((size_t)seq * Hq + head) * D + c * 8);
 
+    // Fused append: position L - 1 of the partition that holds it is the new
+    // token, whose rows come from new_key / new_value instead of the cache.
+    // The chunk loop then stops before it (end_c), and one wave per head
+    // folds it in after the loop. That wave keeps its copy of the rows in
+    // LDS (written and read by itself, so no barrier), and at the very end
+    // stores them into the cache slot when its head is the first of its kv
+    // head: a global store ahead of the chunk loop would stop the compiler
+    // from reading the block table with scalar loads.
+    // A sequence with L = 0 has no token to attend, but its row is still
+    // stored (by the workgroups of its partition 0), as the scatter would.
+    const bool owner = a.new_key && part == max(nparts, 1) - 1;
+    const bool slot_ok = owner && a.slot_mapping[seq] >= 0 &&
+                         a.slot_mapping[seq] < (int64_t)a.num_blocks * BS;
+    const bool has_new = slot_ok && L > 0;  // every wave of the head
+    const bool app = has_new && sub == 0;   // the wave that folds it in
+    if (slot_ok && sub == 0 && r == 0) {
+        *(u32x4*)&sm_new[hslot][0][c * 8] =
+            *(const u32x4*)(a.new_key + seq * a.new_key_stride + kvh * D + c * 8);
+        *(u32x4*)&sm_new[hslot][1][c * 8] =
+            *(const u32x4*)(a.new_value + seq * a.new_value_stride + kvh * D + c * 8);
+    }
+    const int end_c = has_new ? L - 1 : end;  // end of the tokens read from the cache
+
     float m = -INFINITY;  // running max of scores (log2 units)
     float lsum = 0.f;     // this lane's share of Σ exp2(s - m)
     float acc[8];
@@ -148,7 +172,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         for (int b = 0; b < BPC; ++b) {
             const int lb = cs / BS + b;
             const int pid = lb < nb ? bt[lb] : -1;
-            const int rows = min(max(end - (cs + b * BS), 0), BS);
+            const int rows = min(max(end_c - (cs + b * BS), 0), BS);
             const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
             const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
             const size_t boff = (size_t)(ok ? pid : 0) * block_bytes;
@@ -190,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
 #pragma unroll
         for (int b = 1; b < BPC; ++b)
             if (myb == b) ok = pok[b];
-        ok = ok && mytok < end;
+        ok = ok && mytok < end_c;
         return ok ? pd[0] * a.scale_log2 : -INFINITY;
     };
     // online softmax update; returns this lane's weight exp2(s - m)
@@ -236,7 +260,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     // this chunk's p·V, and its V during the next score pass -----------------
     int cs = start + sub * CHUNK;
     const int cstep = nwh * CHUNK;
-    if (cs < end) {
+    if (cs < end_c) {
         ChunkIds cur;
         u32x4 kr[NI], vr[NI];
         fetch_ids(cs, cur);
@@ -244,7 +268,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         issue(cur.v, vr);
         for (;;) {
             const int nx = cs + cstep;
-            const bool more = nx < end;
+            const bool more = nx < end_c;
             ChunkIds nxt;
             if (more) fetch_ids(nx, nxt);
             const float pr = update(scores(kr, cs, cur.ok));
@@ -258,6 +282,35 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
             cur = nxt;
             cs = nx;
         }
+    }
+
+    // ---- the fused-append token, once per head -----------------------------
+    if (app) {
+        const u32x4 kn = *(const u32x4*)&sm_new[hslot][0][c * 8];
+        float t = KV::dot2(kn.x, q.x, 0.f);
+        t = KV::dot2(kn.y, q.y, t);
+        t = KV::dot2(kn.z, q.z, t);
+        t = KV::dot2(kn.w, q.w, t);
+#pragma unroll
+        for (int msk = 1; msk < LPR; msk <<= 1) t += __shfl_xor(t, msk, 64);
+        const float sn = t * a.scale_log2;  // the same in every row group
+        const float mn = fmaxf(m, sn);
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+        const float pn = fast_exp2(sn - mn);
+        m = mn;
+        lsum = lsum * alpha + (lane == 0 ? pn : 0.f);
+        const u32x4 vn = *(const u32x4*)&sm_new[hslot][1][c * 8];
+        const float w = r == 0 ? pn : 0.f;  // row group 0 carries the token
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+        acc[0] += w * KV::lo(vn.x);
+        acc[1] += w * KV::hi(vn.x);
+        acc[2] += w * KV::lo(vn.y);
+        acc[3] += w * KV::hi(vn.y);
+        acc[4] += w * KV::lo(vn.z);
+        acc[5] += w * KV::hi(vn.z);
+        acc[6] += w * KV::lo(vn.w);
+        acc[7] += w * KV::hi(vn.w);
     }
 
     // ---- fold the wavefront's rows, then the workgroup's waves -------------
@@ -309,6 +362,11 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     if (nparts > 1 && sub == 0 && lane == 0) {
         a.part_max[pidx] = M * kLn2;  // natural-log units
         a.part_sum[pidx] = tot;
+    }
+    if (slot_ok && sub == 0 && r == 0 && head % (Hq / a.num_kv_heads) == 0) {
+        const size_t dst = (size_t)a.slot_mapping[seq] * (a.num_kv_heads * D) + kvh * D + c * 8;
+        *(u32x4*)((uint16_t*)a.key_cache + dst) = *(const u32x4*)&sm_new[hslot][0][c * 8];
+        *(u32x4*)((uint16_t*)a.value_cache + dst) = *(const u32x4*)&sm_new[hslot][1][c * 8];
     }
 }
 
@@ -630,13 +688,21 @@ extern "C" size_t pa_decode_split_workspace_bytes(int num_seqs, int num_heads, i
 
 namespace {
 
+// the decode step's new rows, for the fused-append calls
+struct AppendRows {
+    const void* new_key;
+    const void* new_value;
+    const int64_t* slot_mapping;
+    int64_t key_stride, value_stride;  // elements between tokens
+};
+
 pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
                             const void* key_cache, const void* value_cache,
                             const int32_t* block_tables, const int32_t* context_lens,
                             const DecodeShape& s, float scale, pa_dtype kv_dtype,
                             int partition_size, int prefix_tokens, void* workspace,
                             size_t workspace_bytes, void* stream, const char* what,
-                            SplitLayout* lay_out) {
+                            SplitLayout* lay_out, const AppendRows* app = nullptr) {
     pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
                                    context_lens, s, scale, kv_dtype);
     if (st != PA_OK) return st;
@@ -690,6 +756,13 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     a.max_partitions = lay.np;
     a.prefix_tokens = prefix_tokens;
     a.heads_log2 = hl;
+    if (app) {
+        a.new_key = (const uint16_t*)app->new_key;
+        a.new_value = (const uint16_t*)app->new_value;
+        a.slot_mapping = app->slot_mapping;
+        a.new_key_stride = app->key_stride;
+        a.new_value_stride = app->value_stride;
+    }
     if (prefix_parts > 0) {
         // shared prefix: 16 / G sequences x G heads per workgroup
         const int rows = 16 / (s.num_heads / s.num_kv_heads);
@@ -783,6 +856,79 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
                         (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
                         context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
                         stream, "pa_decode_split (merge)");
+}
+
+namespace {
+
+// the partition launch of the fused-append calls (validates the new rows)
+pa_status launch_partitions_append(
+    void* out, pa_dtype out_dtype, const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
+    const void* new_value, const int64_t* slot_mapping, int64_t new_key_token_stride,
+    int64_t new_value_token_stride, const DecodeShape& s, float scale, pa_dtype kv_dtype,
+    int partition_size, void* workspace, size_t workspace_bytes, void* stream, const char* what,
+    SplitLayout* lay) {
+    const int64_t row = (int64_t)s.num_kv_heads * s.head_dim;
+    PA_REQUIRE(new_key_token_stride >= row && new_value_token_stride >= row, PA_ERR_SHAPE,
+               "new-token strides must be >= num_kv_heads * head_dim");
+    PA_REQUIRE(new_key_token_stride % 8 == 0 && new_value_token_stride % 8 == 0,
+               PA_ERR_ALIGNMENT, "new-token strides must be multiples of 8 elements");
+    if (s.num_seqs > 0) {
+        PA_REQUIRE(new_key && new_value && slot_mapping, PA_ERR_NULL, "null pointer argument");
+        PA_REQUIRE(aligned16(new_key) && aligned16(new_value), PA_ERR_ALIGNMENT,
+                   "new_key and new_value must be 16-byte aligned");
+    }
+    const AppendRows app{new_key, new_value, slot_mapping, new_key_token_stride,
+                         new_value_token_stride};
+    return launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
+                             context_lens, s, scale, kv_dtype, partition_size, 0, workspace,
+                             workspace_bytes, stream, what, lay, &app);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_partitions_append(
+    void* out, pa_dtype out_dtype, const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
+    const void* new_value, const int64_t* slot_mapping, int64_t new_key_token_stride,
+    int64_t new_value_token_stride, int num_seqs, int num_heads, int num_kv_heads,
+    int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+    pa_dtype kv_dtype, int partition_size, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    SplitLayout lay;
+    return launch_partitions_append(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                    context_lens, new_key, new_value, slot_mapping,
+                                    new_key_token_stride, new_value_token_stride, s, scale,
+                                    kv_dtype, partition_size, workspace, workspace_bytes, stream,
+                                    "pa_decode_partitions_append", &lay);
+}
+
+extern "C" pa_status pa_decode_split_append(
+    void* out, pa_dtype out_dtype, const void* query, void* key_cache, void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const void* new_key,
+    const void* new_value, const int64_t* slot_mapping, int64_t new_key_token_stride,
+    int64_t new_value_token_stride, int num_seqs, int num_heads, int num_kv_heads,
+    int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+    pa_dtype kv_dtype, int partition_size, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    SplitLayout lay;
+    pa_status st = launch_partitions_append(
+        out, out_dtype, query, key_cache, value_cache, block_tables, context_lens, new_key,
+        new_value, slot_mapping, new_key_token_stride, new_value_token_stride, s, scale,
+        kv_dtype, partition_size, workspace, workspace_bytes, stream,
+        "pa_decode_split_append (partitions)", &lay);
+    if (st != PA_OK || num_seqs == 0) return st;
+    char* ws = (char*)workspace;
+    return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
+                        (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
+                        context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
+                        stream, "pa_decode_split_append (merge)");
 }
 
 extern "C" pa_status pa_decode_split_shared_prefix(

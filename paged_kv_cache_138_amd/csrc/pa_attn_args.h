@@ -27,6 +27,16 @@ struct AttnArgs {
     int prefix_tokens;  // shared-prefix mode: tokens every sequence shares (block_tables row 0)
     int heads_log2;     // MHA kernel: log2 of the query heads one workgroup serves (0, 1, 2)
     float scale_log2;  // scale * log2(e)
+    // Fused append (decode step). When new_key is set, row i of new_key /
+    // new_value is sequence i's token at position L_i - 1: the workgroups of
+    // the partition holding that position use it in place of the cache row
+    // and store it into slot slot_mapping[i] (skipped when the slot is
+    // negative or outside the cache, and then the cache row is used).
+    const uint16_t* new_key;
+    const uint16_t* new_value;
+    const int64_t* slot_mapping;
+    int64_t new_key_stride;    // elements between consecutive tokens of new_key
+    int64_t new_value_stride;  // and of new_value
 };
 
 }  // namespace pa

@@ -83,7 +83,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 }
 
 #ifndef PA_GQA_WAVES_PER_EU
-#define PA_GQA_WAVES_PER_EU 2
+#define PA_GQA_WAVES_PER_EU 3
 #endif
 #ifndef PA_GQA_CHUNK
 #define PA_GQA_CHUNK 32
@@ -119,6 +119,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     __shared__ __attribute__((aligned(16))) char sm_v[NW][TILE];
     __shared__ float sm_m[NW][16];
     __shared__ float sm_l[NW][16];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_new[NW][2][D];  // fused append: new K, V rows
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -170,7 +171,31 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         bt = a.block_tables + (size_t)seq0 * a.max_blocks_per_seq;
     }
     const int start = part * P;
-    const int end = min(start + P, Lsrc);
+    // Fused append (not in prefix mode): position L - 1 of the partition
+    // holding it is the new token, taken from new_key / new_value. The
+    // chunk loop stops before it (end), and the first wave of each kv head
+    // folds it in after the loop, from its own copy in LDS; that wave also
+    // stores the rows into the cache slot, at the very end (a global store
+    // ahead of the chunk loop would stop the compiler from reading the
+    // block table with scalar loads).
+    // (A sequence with L = 0 has no token to attend; its row is still
+    // stored, by the workgroups of its partition 0, as the scatter would.)
+    bool has_new = false, store_new = false;
+    if constexpr (!PREFIX) {
+        if (a.new_key && part == max(nparts, 1) - 1) {
+            const int64_t slot = a.slot_mapping[seq0];
+            const bool slot_ok = slot >= 0 && slot < (int64_t)a.num_blocks * BS;
+            has_new = slot_ok && Lsrc > 0;
+            store_new = slot_ok && sub == 0 && vr == 0;
+            if (store_new) {
+                *(u32x4*)&sm_new[wave][0][vc * 8] =
+                    *(const u32x4*)(a.new_key + seq0 * a.new_key_stride + kvh * D + vc * 8);
+                *(u32x4*)&sm_new[wave][1][vc * 8] =
+                    *(const u32x4*)(a.new_value + seq0 * a.new_value_stride + kvh * D + vc * 8);
+            }
+        }
+    }
+    const int end = has_new ? Lsrc - 1 : min(start + P, Lsrc);
     const int nb = (Lsrc + BS - 1) / BS;
     auto row_seq = [&](int r) { return seq0 + r / G; };
     auto row_head = [&](int r) { return kvh * G + r % G; };
@@ -344,6 +369,37 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         }
     }
 
+    // ---- the fused-append token, once per kv head: head n's score is
+    // q_n·k_new (lane group g holds 8 of every 32 elements, then the groups
+    // are summed), and O[n][16t + 4g + k] (oacc[t][k]) gains p_n v_new -------
+    if (has_new && sub == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const u32x4 kn = *(const u32x4*)&sm_new[wave][0][32 * j + 8 * g];
+            t = KV::dot2(kn.x, qb[j].x, t);
+            t = KV::dot2(kn.y, qb[j].y, t);
+            t = KV::dot2(kn.z, qb[j].z, t);
+            t = KV::dot2(kn.w, qb[j].w, t);
+        }
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        const float sn = t * a.scale_log2;
+        const float mn = fmaxf(m, sn);
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+        const float pn = fast_exp2(sn - mn);
+        m = mn;
+        lsum = lsum * alpha + (g == 0 ? pn : 0.f);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const u32x2 vv = *(const u32x2*)&sm_new[wave][1][16 * tt + 4 * g];
+            oacc[tt][0] = oacc[tt][0] * alpha + pn * KV::lo(vv.x);
+            oacc[tt][1] = oacc[tt][1] * alpha + pn * KV::hi(vv.x);
+            oacc[tt][2] = oacc[tt][2] * alpha + pn * KV::lo(vv.y);
+            oacc[tt][3] = oacc[tt][3] * alpha + pn * KV::hi(vv.y);
+        }
+    }
+
     // ---- per-wave results: head n's (max, sum) and its output rows --------
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
@@ -396,6 +452,11 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
                 a.part_sum[pidx] = tot;
             }
         }
+    }
+    if (store_new) {
+        const size_t dst = (size_t)a.slot_mapping[seq0] * (Hkv * D) + kvh * D + vc * 8;
+        *(u32x4*)((uint16_t*)a.key_cache + dst) = *(const u32x4*)&sm_new[wave][0][vc * 8];
+        *(u32x4*)((uint16_t*)a.value_cache + dst) = *(const u32x4*)&sm_new[wave][1][vc * 8];
     }
 }
 

@@ -19,6 +19,30 @@ namespace pa {
 // partitions can be in flight together.
 __device__ __forceinline__ float merge_row_element(const float* pm, const float* ps,
                                                   const float* po, int np, int D) {
+    constexpr int kFew = 8;
+    if (np <= kFew) {
+        // up to 8 partitions: every load is issued before any arithmetic
+        float m[kFew], l[kFew], o[kFew];
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) {
+            const bool in = p < np;
+            m[p] = in ? pm[p] : -INFINITY;
+            l[p] = in ? ps[p] : 0.f;
+            o[p] = in ? po[(size_t)p * D] : 0.f;
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) M = fmaxf(M, m[p]);
+        if (M == -INFINITY) return 0.f;
+        float tot = 0.f, acc = 0.f;
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) {
+            const float w = m[p] == -INFINITY ? 0.f : l[p] * fast_exp2((m[p] - M) * kLog2e);
+            tot += w;
+            acc += w * o[p];
+        }
+        return tot > 0.f ? acc / tot : 0.f;
+    }
     float M = -INFINITY;
 #pragma unroll 8
     for (int p = 0; p < np; ++p) M = fmaxf(M, pm[p]);

@@ -60,6 +60,11 @@ def load():
     lib.pa_decode_partitions_shared_prefix.restype = i32
     lib.pa_decode_split_shared_prefix.argtypes = dec + [i32, i32, vp, sz, vp]
     lib.pa_decode_split_shared_prefix.restype = i32
+    lib.pa_decode_split_append.argtypes = ([vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64]
+                                           + [i32] * 7 + [f32, i32, i32, vp, sz, vp])
+    lib.pa_decode_split_append.restype = i32
+    lib.pa_decode_partitions_append.argtypes = lib.pa_decode_split_append.argtypes
+    lib.pa_decode_partitions_append.restype = i32
     lib.pa_decode_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_split_workspace_bytes.restype = sz
     lib.pa_lse_merge.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
@@ -201,6 +206,44 @@ def decode_split(query, key_cache, value_cache, block_tables, context_lens, scal
     """Paged decode attention as partitions + log-sum-exp merge."""
     return _split_call("pa_decode_split", query, key_cache, value_cache, block_tables, context_lens,
                        scale, partition_size, workspace, out, out_dtype)
+
+
+def decode_split_append(query, key_cache, value_cache, block_tables, context_lens, new_key, new_value,
+                        slot_mapping, scale, partition_size=512, workspace=None, out=None,
+                        out_dtype=None, _name="pa_decode_split_append"):
+    """One decode step: store new_key[i] / new_value[i] ([B, Hkv, D], one new
+    token per sequence) at slot_mapping[i] of the caches and attend, the new
+    token being position L_i - 1 of sequence i (see pa.h)."""
+    out, (B, Hq, Hkv, D, BS, MB, NB) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens, out, out_dtype)
+    _on_gpu(new_key, new_value, slot_mapping)
+    _need(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (B,)
+          and slot_mapping.is_contiguous(), "slot_mapping must be a contiguous int64 [num_seqs] vector")
+    for t in (new_key, new_value):
+        _need(t.dtype == key_cache.dtype, "new rows must have the cache dtype")
+        _need(t.dim() == 3 and tuple(t.shape) == (B, Hkv, D), "new_key/new_value must be [B, Hkv, D]")
+        _need(t.stride(2) == 1 and t.stride(1) == D, "heads and dims of a token must be dense")
+    if workspace is None:
+        workspace = make_workspace(B, Hq, D, MB, BS, partition_size, query.device)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = getattr(load(), _name)(
+        _ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(new_key), _ptr(new_value), _ptr(slot_mapping),
+        new_key.stride(0) if B else Hkv * D, new_value.stride(0) if B else Hkv * D, B, Hq, Hkv, D, BS,
+        MB, NB, float(scale), _DT[key_cache.dtype], int(partition_size), _ptr(workspace), nbytes,
+        _stream(query))
+    _check(st, _name)
+    return out
+
+
+def decode_partitions_append(query, key_cache, value_cache, block_tables, context_lens, new_key,
+                             new_value, slot_mapping, scale, partition_size=512, workspace=None,
+                             out=None, out_dtype=None):
+    """The partition launch of decode_split_append (merge with lse_merge)."""
+    return decode_split_append(query, key_cache, value_cache, block_tables, context_lens, new_key,
+                               new_value, slot_mapping, scale, partition_size, workspace, out,
+                               out_dtype, _name="pa_decode_partitions_append")
 
 
 def decode_partitions(query, key_cache, value_cache, block_tables, context_lens, scale,

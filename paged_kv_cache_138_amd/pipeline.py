@@ -40,7 +40,7 @@ class DeviceBatch:
     """GPU copies of a workloads.Batch plus the step's output buffers."""
 
     def __init__(self, batch, device="cuda", out_dtype=None, split=True, partition_size=None,
-                 shared_prefix=False):
+                 shared_prefix=False, fused=False):
         w = batch.workload
         self.batch = batch
         self.device = device
@@ -61,6 +61,8 @@ class DeviceBatch:
         pt = w.shared_prefix_tokens
         self.prefix_tokens = pt if (shared_prefix and split and pt > 0
                                     and pt % self.partition_size == 0) else 0
+        # one launch pair per step: the scatter runs inside the partition launch
+        self.fused = bool(fused and split and not self.prefix_tokens)
         B, Hq, D = self.query.shape
         od = out_dtype if out_dtype is not None else self.query.dtype
         self.out = torch.empty((B, Hq, D), dtype=od, device=device)
@@ -75,6 +77,12 @@ class DeviceBatch:
 
     def partitions(self):
         """Split path, partition launches only (see lib.decode_partitions)."""
+        if self.fused:
+            palib.decode_partitions_append(
+                self.query, self.key_cache, self.value_cache, self.block_tables, self.context_lens,
+                self.new_key, self.new_value, self.slot_mapping, self.scale, self.partition_size,
+                workspace=self.workspace, out=self.out)
+            return
         if self.prefix_tokens:
             palib.decode_partitions_shared_prefix(
                 self.query, self.key_cache, self.value_cache, self.block_tables, self.context_lens,
@@ -108,6 +116,12 @@ class DeviceBatch:
         return self.out
 
     def step(self):
+        if self.fused:
+            palib.decode_split_append(
+                self.query, self.key_cache, self.value_cache, self.block_tables, self.context_lens,
+                self.new_key, self.new_value, self.slot_mapping, self.scale, self.partition_size,
+                workspace=self.workspace, out=self.out)
+            return self.out
         self.write_cache()
         return self.attend()
 
@@ -131,6 +145,7 @@ class RotatedBatch(DeviceBatch):
         self.split = src.split
         self.partition_size = src.partition_size
         self.prefix_tokens = src.prefix_tokens
+        self.fused = src.fused
         bt = src.block_tables
         used = torch.unique(bt[bt >= 0])
         n = int(used.numel())

@@ -90,3 +90,21 @@ def test_split_rejects_bad_partition_and_workspace(lib):
     assert lib.pa_decode_split(*args, 64, None, 1 << 20, None) == 5
     assert lib.pa_decode_split(*args, 64, p + 16, 1 << 20, None) == 5  # not 256-aligned
     assert lib.pa_decode_split(*args, 64, p, 16, None) == 5
+
+
+def test_fused_append_rejects_bad_new_rows(lib):
+    # host-side checks run before any launch, so dummy (never dereferenced)
+    # pointers suffice
+    p = 1 << 12
+    base = [p, 2, p, p, p, p, p]              # out .. context_lens
+    rows = [p, p, p]                          # new_key, new_value, slot_mapping
+    shape = [2, 8, 8, 128, 16, 8, 64, 0.1, 0, 64]  # B .. kv dtype, partition_size
+    ws = [p, 1 << 20, None]
+    for fn in (lib.pa_decode_split_append, lib.pa_decode_partitions_append):
+        assert fn(*base, *rows, 1000, 1024, *shape, *ws) == 2      # stride < Hkv*D
+        assert fn(*base, *rows, 1028, 1024, *shape, *ws) == 7      # stride not a multiple of 8
+        assert fn(*base, None, p, p, 1024, 1024, *shape, *ws) == 1  # null new_key
+        assert fn(*base, p, p, None, 1024, 1024, *shape, *ws) == 1  # null slot_mapping
+        assert fn(*base, p + 8, p, p, 1024, 1024, *shape, *ws) == 7  # misaligned new_key
+        assert fn(*base, *rows, 1024, 1024, *shape[:-1], 24, *ws) == 2  # partition not a multiple of 16
+        assert fn(*base, *rows, 1024, 1024, *shape, None, 1 << 20, None) == 5  # no workspace

@@ -42,7 +42,7 @@ def test_full_size_workload(name):
     b = W.make_batch(w, seed=0)
     path = bench.default_path(w)
     db = DeviceBatch(b, out_dtype=None, split=path.startswith("split"),
-                     shared_prefix=(path == "split_prefix"))
+                     shared_prefix=(path == "split_prefix"), fused=(path == "split"))
     out = db.step()
     torch.cuda.synchronize()
     got = to_host_f64(out)

@@ -380,3 +380,70 @@ def test_shared_prefix_rejects_misaligned_prefix():
     with pytest.raises(palib.PaError):
         palib.decode_split_shared_prefix(db.query, db.key_cache, db.value_cache, db.block_tables,
                                          db.context_lens, db.scale, 32, 64, workspace=db.workspace)
+
+
+# ---- fused append: the scatter inside the partition launch ----------------
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+@pytest.mark.parametrize("out_kind", ["f32", "native"])
+def test_fused_append_step_matches_oracle_small(case, out_kind):
+    w = _small("fused%d" % case, **SMALL_CASES[case])
+    b = W.make_batch(w, seed=300 + case, unallocated="nan")
+    out_dtype = torch.float32 if out_kind == "f32" else None
+    db = DeviceBatch(b, out_dtype=out_dtype, split=True, partition_size=64, fused=True)
+    assert db.fused
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    # the whole caches, bit-exact: the new rows are stored, nothing else moves
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, "f32" if out_kind == "f32" else w.dtype,
+                  "fused case %d" % case)
+
+
+@pytest.mark.parametrize("part", [16, 64, 512])
+def test_fused_append_equals_scatter_then_split(part):
+    # the new token is summed last in its partition instead of in order, so
+    # the two paths agree to rounding; the caches agree bit for bit
+    w = _small("fs", num_seqs=6, num_heads=8, num_kv_heads=8, head_dim=128, dtype="bf16",
+               block_size=16, num_blocks=300, max_blocks_per_seq=48, lens="uniform:1:700")
+    b = W.make_batch(w, seed=41, lens=[1, 16, 17, 64, 65, 700])
+    a = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=part, fused=True)
+    u = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=part, fused=False)
+    oa, ou = a.step(), u.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(a.key_cache), to_host_bits(u.key_cache))
+    assert np.array_equal(to_host_bits(a.value_cache), to_host_bits(u.value_cache))
+    assert np.abs(to_host_f64(oa) - to_host_f64(ou)).max() < 1e-5
+    _, _, ref = _oracle_step(b)
+    _assert_close(to_host_f64(oa), ref, "f32", "fused P=%d" % part)
+
+
+def test_fused_append_padding_slots_and_strided_rows():
+    # negative and out-of-range slots store nothing and leave the cache row in
+    # use, as the scatter does; new rows may sit inside a wider (fused QKV)
+    # buffer
+    w = _small("fp", num_seqs=5, num_heads=4, num_kv_heads=2, head_dim=64, dtype="f16",
+               block_size=16, num_blocks=64, max_blocks_per_seq=12, lens="uniform:1:180")
+    b = W.make_batch(w, seed=43, poison="zero")
+    NB, BS = w.num_blocks, w.block_size
+    b.slot_mapping[1] = -1
+    b.slot_mapping[3] = NB * BS + 5
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=32, fused=True)
+    B, Hkv, D = db.new_key.shape
+    wide_k = torch.zeros((B, 3 * Hkv * D), dtype=db.new_key.dtype, device="cuda")
+    wide_v = torch.zeros_like(wide_k)
+    wide_k[:, Hkv * D:2 * Hkv * D] = db.new_key.reshape(B, -1)
+    wide_v[:, 2 * Hkv * D:] = db.new_value.reshape(B, -1)
+    db.new_key = wide_k[:, Hkv * D:2 * Hkv * D].view(B, Hkv, D)
+    db.new_value = wide_v[:, 2 * Hkv * D:].view(B, Hkv, D)
+    out = db.step()
+    torch.cuda.synchronize()
+    # a slot outside the cache breaks the caller contract; the kernels skip
+    # it, which for the oracle is a negative slot
+    b.slot_mapping[3] = -1
+    kc, vc, ref = _oracle_step(b)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, "f32", "fused padding")
