@@ -19,9 +19,9 @@ namespace pa {
 // partitions can be in flight together.
 __device__ __forceinline__ float merge_row_element(const float* pm, const float* ps,
                                                   const float* po, int np, int D) {
-    constexpr int kFew = 8;
+    constexpr int kFew = 16;
     if (np <= kFew) {
-        // up to 8 partitions: every load is issued before any arithmetic
+        // up to 16 partitions: every load is issued before any arithmetic
         float m[kFew], l[kFew], o[kFew];
 #pragma unroll
         for (int p = 0; p < kFew; ++p) {

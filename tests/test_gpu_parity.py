@@ -447,3 +447,39 @@ def test_fused_append_padding_slots_and_strided_rows():
     assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
     assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
     _assert_close(to_host_f64(out), ref, "f32", "fused padding")
+
+
+def test_fused_append_zero_length_sequence_still_stores_its_row():
+    # as the scatter would: a sequence with L = 0 and a slot gets its row
+    # stored (by its partition 0) and a zero output
+    w = _small("fz", num_seqs=4, num_heads=4, num_kv_heads=4, head_dim=128, dtype="bf16",
+               block_size=16, num_blocks=40, max_blocks_per_seq=8, lens="fixed:1")
+    b = W.make_batch(w, seed=47, lens=[0, 33, 1, 100])
+    used = set(int(x) for x in np.asarray(b.block_tables).ravel() if x >= 0)
+    free = [i for i in range(w.num_blocks) if i not in used]
+    b.slot_mapping[0] = free[0] * w.block_size + 5
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=32, fused=True)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    got = to_host_f64(out)
+    assert np.all(got[0] == 0.0)
+    _assert_close(got, ref, "f32", "fused L=0")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_two_heads_per_workgroup_on_a_sparse_rectangle(fused):
+    # a long maximum context and a small partition make the (sequence, head,
+    # partition) rectangle many times the device while most of it is empty:
+    # the split path then serves two adjacent heads per workgroup
+    w = _small("rect", num_seqs=8, num_heads=8, num_kv_heads=8, head_dim=128, dtype="f16",
+               block_size=16, num_blocks=256, max_blocks_per_seq=4096, lens="uniform:1:300")
+    b = W.make_batch(w, seed=53, unallocated="nan")
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=16, fused=fused)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, "f32", "sparse rectangle fused=%s" % fused)
