@@ -1,4 +1,6 @@
-// Paged decode attention: pa_decode, pa_decode_split and pa_lse_merge.
+// Paged decode attention: pa_decode, the split path (pa_decode_split,
+// pa_decode_partitions, their shared-prefix and fused-append forms) and
+// pa_lse_merge.
 //
 // What is computed ("vLLM PagedAttention深度解析与工程实践" §二 formula and
 // §4.1; lqnn.cn/news/170268 §2.3 and §6): for sequence i and query head h,
@@ -7,10 +9,11 @@
 // at or past L_i in the last block are never read.
 //
 // Work decomposition (MI355X, 64-lane wavefronts):
-//   * one workgroup = one (sequence, query head, context partition) with NW
-//     wavefronts; the waves take 64-token chunks of the partition in turn and
-//     their softmax states are merged in LDS at the end. The single-pass
-//     pa_decode is the same kernel with one partition covering the context.
+//   * one workgroup = one (sequence, group of 1 or 2 adjacent query heads,
+//     context partition) with NW wavefronts; each head's waves take 64-token
+//     chunks of the partition in turn and their softmax states are merged in
+//     LDS at the end. The single-pass pa_decode is the same kernel with one
+//     head per workgroup and one partition covering the context.
 //   * inside a chunk, one 16-byte load per lane brings 8 elements of a K (or
 //     V) row: head_dim/8 lanes cover a row, 64 lanes cover 64*8/head_dim
 //     rows of one physical block per load instruction, so each load is a

@@ -28,10 +28,11 @@
 //
 // K and V rows reach LDS through the same coalesced loads as the
 // head-per-workgroup kernel (head_dim/8 lanes per row, whole 128-byte lines
-// per request). LDS rows are padded to 2*head_dim + 16 bytes, which keeps
-// both the 16-byte reads of K and the transpose reads of V free of bank
-// conflicts. The work decomposition, masking by buffer ranges, partitions
-// and the cross-wave merge follow the head-per-workgroup kernel.
+// per request). LDS rows are padded to 2*head_dim + 16 bytes, which spreads
+// the 16-byte reads of K and the transpose reads of V over the banks. The
+// work decomposition (1 or 2 adjacent kv heads per workgroup), masking by
+// buffer ranges, partitions, the cross-wave merge and the fused append
+// follow the head-per-workgroup kernel.
 #pragma once
 
 #include "pa_attn_args.h"
