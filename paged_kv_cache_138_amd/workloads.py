@@ -52,6 +52,8 @@ class Workload:
     num_blocks: int
     max_blocks_per_seq: int
     lens: str             # length-distribution recipe, see draw_context_lens
+    # split-path partition size: the GQA long-context workload names 512; the
+    # others leave it open and take the size measured fastest for the shape
     partition_size: int = 512
     shared_prefix_tokens: int = 0
     long_seqs: int = 0        # extra sequences of long_len tokens
@@ -66,6 +68,7 @@ WORKLOADS = {
                     "64 permuted physical blocks, context U[1,128]"),
     "llama13b": Workload(
         "llama13b", 32, 40, 40, 128, "f16", 16, 8192, 128, "uniform:32:2048",
+        partition_size=256,
         description="LLaMA-13B-like decode: 32 seqs, 40 heads, head_dim 128, "
                     "fp16, block 16, 8192-block shuffled free list, "
                     "context U[32,2048]"),
