@@ -13,7 +13,10 @@ step's blocks out of the 256 MB last-level cache.
 Prints one JSON line. `value` is KV GB/s: the step's algorithmic bytes
 (Σ context_len · 2·Hkv·D·e for K and V, plus q, the output, the block-table
 entries used, the context lengths and the cache write) over the measured
-step time.
+step time. The line also carries the dominant launch's roofline (against the
+8 TB/s peak and against a measured streaming-read ceiling), the p10/p50/p90
+of single steps, the standalone scatter's time and bandwidth, and the CPU
+oracle's throughput on a bounded sample of the same batch.
 
     python bench.py [--steps K] [--warmup W] [--workload llama13b]
 """
@@ -49,6 +52,8 @@ def parse():
                     help="override the context-length recipe (e.g. fixed:1094); not the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--ceiling-gib", type=float, default=4.0,
+                    help="buffer size of the streaming-read ceiling measurement (0 skips it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 5 times (counter calibration)")
     return ap.parse_args()
@@ -142,7 +147,13 @@ def cpu_baseline(batch, target_s):
     if limiter is not None:
         limiter.unregister()
     gbs = done_bytes / elapsed / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    model = "?"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": model,
             "sample": "%d sequence-steps of the %s batch (all %d heads; KV bytes %d) in %.1f s of "
                       "oracle decode, 1 BLAS thread; cache-write oracle %.2f s not counted"
                       % (done_seqs, w.name, w.num_heads, done_bytes, elapsed, t_write),
@@ -230,6 +241,33 @@ def main():
             for c in copies:
                 c.merge()
             torch.cuda.synchronize()
+        # the spread of single steps (each between its own events; separate
+        # from the timed loop above, whose mean is the headline)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for k in range(K):
+            ev[k][0].record()
+            copies[k % R].step()
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        single = sorted(a.elapsed_time(b) for a, b in ev)
+        pct = lambda q: single[min(K - 1, int(round(q * (K - 1))))]
+        # the scatter alone: K pa_reshape_and_cache launches recorded in a HIP
+        # graph and replayed, so the host's per-call cost stays out of the
+        # GPU time (each launch is a few microseconds of GPU work)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(K):
+                copies[k % R].write_cache()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        scatter_ms = e0.elapsed_time(e1) / K
+        del graph
+        ceiling = stream_ceiling(args.ceiling_gib) if args.ceiling_gib > 0 else None
     step_bytes = unique_bytes + write_bytes
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     attn_gbs = unique_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -268,7 +306,15 @@ def main():
                                                    "and suffix kernels)"}[path], K,
                                   attn_avg_ms * 1e3)},
         "host_data_generation_s": round(t_gen, 2),
+        "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+        "reshape_and_cache": {"us_per_call": round(scatter_ms * 1e3, 2), "tokens": B,
+                              "timing": "%d launches replayed from one HIP graph" % K,
+                              "bytes": write_bytes,
+                              "GB_per_s": round(write_bytes / (scatter_ms * 1e-3) / 1e9, 2)},
     }
+    if ceiling is not None:
+        res["stream_read_ceiling"] = dict(ceiling, attention_frac_of_ceiling=round(
+            attn_gbs / ceiling["value"], 4))
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
     print(json.dumps(res), flush=True)
@@ -276,6 +322,30 @@ def main():
 
 def traffic_key(name, path, fused):
     return "%s/%s%s" % (name, path, "+append" if fused else "")
+
+
+def stream_ceiling(gib):
+    """Measured streaming-read ceiling: pa_stream_read over a buffer of `gib`
+    GiB (far larger than the last-level cache), 2 warm-up and 10 timed
+    launches between HIP events."""
+    import torch
+    from paged_kv_cache_138_amd import lib as palib
+    nbytes = int(gib * (1 << 30)) // 16 * 16
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        palib.stream_read(buf, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        palib.stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del buf
+    return {"value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "buffer_bytes": nbytes,
+            "kernel": "pa_stream_read (16-byte non-temporal loads)"}
 
 
 def base_partition(path, args, w):

@@ -289,6 +289,18 @@ pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,
                        int head_dim, int max_partitions, int partition_size,
                        void* stream);
 
+/*
+ * pa_stream_read - measurement aid: read every byte of a device buffer once
+ * with the 16-byte non-temporal loads the attention kernels use, writing
+ * (practically) nothing. Timed over a buffer much larger than the
+ * last-level cache it gives the device's streaming-read ceiling, the
+ * measured counterpart of the HBM peak that the attention kernels' bandwidth
+ * is compared with.
+ *   data   device buffer, 16-byte aligned, bytes a multiple of 16.
+ *   sink   device buffer of at least 64 uint32 (almost never written).
+ */
+pa_status pa_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* pa_status_string(pa_status s);
 

@@ -69,6 +69,8 @@ def load():
     lib.pa_decode_split_workspace_bytes.restype = sz
     lib.pa_lse_merge.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.pa_lse_merge.restype = i32
+    lib.pa_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.pa_stream_read.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -304,3 +306,12 @@ def lse_merge(part_out, part_max, part_sum, context_lens, partition_size, out=No
                              _ptr(context_lens), B, Hq, D, NP, int(partition_size), _stream(part_out))
     _check(st, "pa_lse_merge")
     return out
+
+
+def stream_read(data, sink):
+    """Read all of `data` (a contiguous GPU tensor) once; see pa_stream_read."""
+    _on_gpu(data, sink)
+    _need(data.is_contiguous() and sink.is_contiguous(), "tensors must be contiguous")
+    _need(sink.dtype == torch.int32 and sink.numel() >= 64, "sink must hold 64 int32")
+    nbytes = data.numel() * data.element_size()
+    _check(load().pa_stream_read(_ptr(data), nbytes, _ptr(sink), _stream(data)), "pa_stream_read")

@@ -108,3 +108,12 @@ def test_fused_append_rejects_bad_new_rows(lib):
         assert fn(*base, p + 8, p, p, 1024, 1024, *shape, *ws) == 7  # misaligned new_key
         assert fn(*base, *rows, 1024, 1024, *shape[:-1], 24, *ws) == 2  # partition not a multiple of 16
         assert fn(*base, *rows, 1024, 1024, *shape, None, 1 << 20, None) == 5  # no workspace
+
+
+def test_stream_read_rejects_bad_buffers(lib):
+    p = 1 << 12
+    assert lib.pa_stream_read(p, 1000, p, None) == 2        # not a multiple of 16
+    assert lib.pa_stream_read(None, 1024, p, None) == 1
+    assert lib.pa_stream_read(p, 1024, None, None) == 1
+    assert lib.pa_stream_read(p + 8, 1024, p, None) == 7    # misaligned
+    assert lib.pa_stream_read(None, 0, None, None) == 0     # nothing to read
