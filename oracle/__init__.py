@@ -19,4 +19,5 @@ from .paged_attention import (  # noqa: F401
     decode_partitions,
     lse_merge,
     decode_split,
+    copy_blocks,
 )

@@ -17,7 +17,9 @@ Sources (cited by page title and section):
   §6 (ignore unfilled slots of a block; accumulate in fp32 or better).
 * [P4] "优化大模型推理：PagedAttention 如何实现 GPU 显存高效管理":
   "按需分配" (35 tokens at block size 16 -> 3 blocks, 13 idle slots),
-  Figure 2 (logical 0,1,2 -> physical 7,1,12).
+  Figure 2 (logical 0,1,2 -> physical 7,1,12), "写时复制" (copy-on-write:
+  candidates share the prompt's blocks, a block is copied only when written;
+  also [P1] §3.1's list of the design's benefits).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): query head h reads kv head h // (Hq/Hkv); a context length of 0
@@ -244,3 +246,32 @@ def decode_split(query, key_cache, value_cache, block_tables, context_lens, scal
     m, l, o = decode_partitions(query, key_cache, value_cache, block_tables,
                                 context_lens, scale, kv_dtype, partition_size)
     return lse_merge(m, l, o, context_lens, partition_size)
+
+
+# ---------------------------------------------------------------------------
+# Copy-on-write block copy ([P4] "写时复制", [P1] §3.1)
+# ---------------------------------------------------------------------------
+
+
+def copy_blocks(key_cache, value_cache, block_mapping):
+    """Return copies of the caches where, for every pair (src, dst) of
+    block_mapping ([N, 2] integers), physical block dst holds the contents of
+    physical block src, for K and for V (all block_size rows, all heads).
+
+    A shared block that one sequence is about to write is copied first, and
+    the sequence's table then points at the copy ([P4] "写时复制"). All pairs
+    read the caches as they were before the call (destinations are fresh
+    blocks, never a source of another pair, each used once); the copy is
+    bitwise, for any element type.
+    """
+    kc = np.array(key_cache, copy=True)
+    vc = np.array(value_cache, copy=True)
+    src_k = np.asarray(key_cache)
+    src_v = np.asarray(value_cache)
+    pairs = np.asarray(block_mapping).reshape(-1, 2)
+    for n in range(pairs.shape[0]):
+        src, dst = int(pairs[n, 0]), int(pairs[n, 1])
+        kc[dst] = src_k[src]
+        vc[dst] = src_v[src]
+    return kc, vc
+

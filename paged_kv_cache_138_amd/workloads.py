@@ -137,6 +137,39 @@ class BlockManager:
             self.refcount[b] = self.refcount.get(b, 0) + 1
             self.allocated.setdefault(seq_id, []).append(int(b))
 
+    def fork(self, parent_id, child_id):
+        """child_id starts as a copy of parent_id's table: every block shared.
+
+        The parallel-sampling case of the copy-on-write section of "优化大模型
+        推理：PagedAttention 如何实现 GPU 显存高效管理": the candidates reference the
+        prompt's physical blocks until their answers diverge."""
+        self.share(child_id, list(self.allocated.get(parent_id, [])))
+
+    def append_slot(self, seq_id, position):
+        """Slot of seq_id's token at `position` (tokens 0 .. position-1 held).
+
+        A new block is taken when the token opens one. A token that lands in a
+        block other tables still reference is written to a fresh copy of that
+        block instead (copy-on-write: shared content stays read-only and is
+        copied only when written); the copy replaces the block in this table
+        and the pair (source block, new block) is returned for the device
+        copy. The last table still holding a block writes in place. Returns
+        (slot, (src, dst) or None)."""
+        blocks = self.allocated.setdefault(seq_id, [])
+        idx, off = divmod(int(position), self.block_size)
+        if idx == len(blocks):
+            blocks.append(self._pop())
+            return blocks[idx] * self.block_size + off, None
+        if idx != len(blocks) - 1:
+            raise ValueError("position %d is not the next token of the table" % position)
+        last = blocks[idx]
+        if self.refcount[last] > 1:
+            new = self._pop()
+            self.refcount[last] -= 1
+            blocks[idx] = new
+            return new * self.block_size + off, (last, new)
+        return last * self.block_size + off, None
+
     def free(self, seq_id):
         for b in self.allocated.pop(seq_id, []):
             self.refcount[b] -= 1

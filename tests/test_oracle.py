@@ -423,3 +423,84 @@ def test_planted_gather_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(pa, "gather_sequence", off_by_one)
     with pytest.raises(AssertionError):
         test_unfilled_slots_are_ignored_even_when_nan()
+
+
+# ---------------------------------------------------------------------------
+# Copy-on-write block copy ("优化大模型推理…" 写时复制)
+# ---------------------------------------------------------------------------
+
+
+def _cow_scenario(seed=0, D=16, H=2):
+    """The page's parallel-sampling scenario at block size 16: a 1000-token
+    prompt, four candidates; every candidate appends one token."""
+    from paged_kv_cache_138_amd import workloads as W
+    fx = _load("copy_on_write.json")
+    n, k, bs = (fx["printed"][x] for x in ("prompt_tokens", "candidates", "block_size"))
+    m = W.BlockManager(range(80), bs)
+    m.allocate("c0", n)
+    for c in range(1, k):
+        m.fork("c0", "c%d" % c)
+    parent = list(m.allocated["c0"])
+    pairs = []
+    for c in list(range(1, k)) + [0]:
+        _, cow = m.append_slot("c%d" % c, n)
+        if cow is not None:
+            pairs.append(cow)
+    rng = np.random.default_rng(seed)
+    kc = rng.standard_normal((80, bs, H, D)).astype(np.float16)
+    vc = rng.standard_normal((80, bs, H, D)).astype(np.float16)
+    tables = [list(m.allocated["c%d" % c]) for c in range(k)]
+    return n, bs, parent, tables, np.array(pairs, dtype=np.int64), kc, vc
+
+
+def _gather2(kc, vc, table, n, bs):
+    row = np.array(table, dtype=np.int32)
+    return oracle.gather_sequence(kc, row, n, bs), oracle.gather_sequence(vc, row, n, bs)
+
+
+def test_copy_blocks_keeps_every_candidates_prompt():
+    # after the copies, each candidate's table reads the same 1000-token
+    # prompt as the original table did (the copy carries the 8 tokens of the
+    # shared partial block); the comparison is bitwise
+    n, bs, parent, tables, pairs, kc, vc = _cow_scenario()
+    assert len(pairs) == 3
+    kc2, vc2 = oracle.copy_blocks(kc, vc, pairs)
+    ref_k, ref_v = _gather2(kc, vc, parent, n, bs)
+    for t in tables:
+        gk, gv = _gather2(kc2, vc2, t, n, bs)
+        assert np.array_equal(gk.view(np.uint16), ref_k.view(np.uint16))
+        assert np.array_equal(gv.view(np.uint16), ref_v.view(np.uint16))
+    # nothing else moves
+    untouched = [b for b in range(kc.shape[0]) if b not in set(pairs[:, 1].tolist())]
+    assert np.array_equal(kc2[untouched].view(np.uint16), kc[untouched].view(np.uint16))
+    assert np.array_equal(vc2[untouched].view(np.uint16), vc[untouched].view(np.uint16))
+
+
+def test_copy_blocks_then_attention_equals_the_shared_original():
+    # a candidate attending through its copied table gets exactly the
+    # parent's output for the prompt (same data, same logical order)
+    n, bs, parent, tables, pairs, kc, vc = _cow_scenario(seed=1)
+    kc2, vc2 = oracle.copy_blocks(kc, vc, pairs)
+    q = np.random.default_rng(2).standard_normal((1, 2, 16)).astype(np.float16)
+    lens = np.array([n], dtype=np.int32)
+    ref = oracle.decode(q, kc, vc, np.array([parent], dtype=np.int32), lens, 0.25, "f16")
+    for t in tables:
+        got = oracle.decode(q, kc2, vc2, np.array([t], dtype=np.int32), lens, 0.25, "f16")
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("mistake", ["k_only", "swapped"])
+def test_planted_copy_mistakes_are_caught(mistake):
+    n, bs, parent, tables, pairs, kc, vc = _cow_scenario(seed=3)
+    if mistake == "k_only":
+        kc2, _ = oracle.copy_blocks(kc, vc, pairs)
+        vc2 = vc.copy()
+    else:
+        kc2, vc2 = oracle.copy_blocks(kc, vc, pairs[:, ::-1])
+    ok = True
+    ref_k, ref_v = _gather2(kc, vc, parent, n, bs)
+    for t in tables:
+        gk, gv = _gather2(kc2, vc2, t, n, bs)
+        ok &= np.array_equal(gk.view(np.uint16), ref_k.view(np.uint16))
+        ok &= np.array_equal(gv.view(np.uint16), ref_v.view(np.uint16))
+    assert not ok

@@ -134,3 +134,37 @@ def test_lognormal_recipe_is_clipped():
     L = W.draw_context_lens(rng, "lognormal:512:1.0:16:4096", 10000)
     assert L.min() >= 16 and L.max() <= 4096
     assert 450 <= np.median(L) <= 570
+
+
+def test_copy_on_write_parallel_sampling_scenario():
+    # "优化大模型推理…" 写时复制: four candidates share a 1000-token prompt's
+    # blocks; when each appends its first token only the shared, partial
+    # last block is copied, and every candidate but the last holder gets a copy
+    fx = json.load(open(os.path.join(GOLDEN, "copy_on_write.json")))
+    n, k, bs = (fx["printed"][x] for x in ("prompt_tokens", "candidates", "block_size"))
+    m = W.BlockManager(range(256), bs)
+    m.allocate("c0", n)
+    assert len(m.allocated["c0"]) == fx["derived"]["prompt_blocks"]
+    assert n - (len(m.allocated["c0"]) - 1) * bs == fx["derived"]["tokens_in_last_prompt_block"]
+    for c in range(1, k):
+        m.fork("c0", "c%d" % c)
+    shared = list(m.allocated["c0"])
+    pairs = []
+    for c in list(range(1, k)) + [0]:
+        slot, cow = m.append_slot("c%d" % c, n)
+        if cow is not None:
+            pairs.append(cow)
+        blocks = m.allocated["c%d" % c]
+        assert slot == blocks[-1] * bs + n % bs            # the token lands in the table's last block
+        assert blocks[:-1] == shared[:-1]                   # the full blocks stay shared
+    assert len(pairs) == fx["reading"]["copies_when_every_candidate_appends_one_token"]
+    assert all(src == shared[-1] for src, _ in pairs)       # only the partial block is copied
+    assert len({dst for _, dst in pairs}) == len(pairs)     # each copy is a fresh block
+    assert m.refcount[shared[-1]] == 1                      # the last holder kept the original
+    assert all(m.refcount[b] == k for b in shared[:-1])
+    # a token that opens a new block takes a fresh one, no copy
+    m2 = W.BlockManager(range(16), bs)
+    m2.allocate("a", 2 * bs)
+    m2.fork("a", "b")
+    slot, cow = m2.append_slot("b", 2 * bs)
+    assert cow is None and slot // bs not in m2.allocated["a"]
