@@ -52,6 +52,10 @@ def parse():
                     help="override the context-length recipe (e.g. fixed:1094); not the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--op", choices=["decode", "copy_blocks"], default="decode",
+                    help="decode: the decode step (default); copy_blocks: the copy-on-write "
+                         "block copy on the workload's cache shape")
+    ap.add_argument("--pairs", type=int, default=1024, help="copy_blocks: block pairs per launch")
     ap.add_argument("--ceiling-gib", type=float, default=4.0,
                     help="buffer size of the streaming-read ceiling measurement (0 skips it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -168,6 +172,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args)
         return
     import numpy as np
     import torch
@@ -322,6 +329,69 @@ def main():
 
 def traffic_key(name, path, fused):
     return "%s/%s%s" % (name, path, "+append" if fused else "")
+
+
+def bench_copy_blocks(args):
+    """Copy-on-write block copy on the workload's cache shape: --pairs random
+    (src, dst) pairs per launch, two disjoint pair sets alternating so no
+    launch finds its source blocks in the last-level cache. Bytes per launch
+    = pairs x block bytes x 2 caches x (read + write)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_138_amd import lib as palib
+    from paged_kv_cache_138_amd import workloads as W
+    w = W.WORKLOADS[args.workload]
+    NB, BS, Hkv, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    N = min(args.pairs, NB // 4)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        kc = torch.empty((NB, BS, Hkv, D), dtype=tdt, device="cuda").normal_()
+        vc = torch.empty_like(kc).normal_()
+        perm = np.random.default_rng(args.seed).permutation(NB)
+        # set r copies perm[2rN : 2rN + N] onto perm[2rN + N : 2(r + 1)N]
+        maps = [torch.from_numpy(np.stack([perm[2 * r * N: 2 * r * N + N],
+                                           perm[2 * r * N + N: 2 * (r + 1) * N]], axis=1)
+                                 .astype(np.int64)).cuda() for r in range(2)]
+        for m in maps:
+            palib.copy_blocks(kc, vc, m)
+        torch.cuda.synchronize()
+        K = args.steps
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(K):
+            palib.copy_blocks(kc, vc, maps[k % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+    block_bytes = BS * Hkv * D * W.element_bytes(w.dtype)
+    nbytes = N * block_bytes * 2 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"metric": "copy-on-write block copy: HBM GB/s (read + write)", "value": round(gbs, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": 1, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic",
+           "config": {"workload": w.name, "op": "copy_blocks", "pairs": N, "block_bytes": block_bytes},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "pa_copy_blocks: %d launches between HIP events, avg %.2f us"
+                                  % (K, ms * 1e3)}}
+    if args.cpu_seconds > 0:
+        import oracle
+        sample = max(1, min(N, 64))
+        kh = np.zeros((2 * sample, BS, Hkv, D), dtype=np.uint16)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.copy_blocks(kh, kh, np.stack([np.arange(sample), sample + np.arange(sample)], 1))
+            reps += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(reps * sample * block_bytes * 2 * 2 / el / 1e9, 3),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": "%d runs of %d pairs (whole-cache copies included)"
+                                         % (reps, sample)}
+    print(json.dumps(res), flush=True)
 
 
 def stream_ceiling(gib):

@@ -94,6 +94,25 @@ pa_status pa_reshape_and_cache(const void* key, const void* value,
                                int block_size, pa_dtype dtype, void* stream);
 
 /*
+ * pa_copy_blocks - copy-on-write block copy ("优化大模型推理：PagedAttention 如何
+ * 实现 GPU 显存高效管理", 写时复制: sequences share physical blocks until one
+ * of them is about to write into a shared block, which it first copies).
+ *
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ *                     fp16/bf16 (dtype), written in place.
+ *   block_mapping     int64 [num_pairs, 2], device: row n = (src, dst). After
+ *                     the call block dst of both caches holds what block src
+ *                     held before it (all rows and heads, bitwise).
+ * Pairs with an id outside [0, num_blocks) are skipped. Caller contract (not
+ * checked on the device): the destinations are distinct and none is also a
+ * source; otherwise the copies race and the result is unspecified. One
+ * launch on `stream`; no host synchronisation.
+ */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, pa_dtype dtype, void* stream);
+
+/*
  * pa_decode - one query token per sequence attends over its paged context,
  * in a single launch (no workspace).
  *

@@ -37,6 +37,53 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// pa_copy_blocks: copy-on-write block copy ("优化大模型推理：PagedAttention 如何
+// 实现 GPU 显存高效管理", 写时复制: shared blocks are copied only when a
+// sequence is about to write into them).
+//
+// Work item = (pair, 16 KiB slice of a block). Each workgroup reads its slice
+// of the source K and V blocks (8 independent 16-byte loads per thread) and
+// writes them to the destination blocks; the descriptors' ranges end at the
+// block's end, so the lanes past it neither read nor write.
+// ---------------------------------------------------------------------------
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;  // per cache: 4 K + 4 V loads in flight per thread
+constexpr uint32_t kCopySlice = kCopyThreads * kCopyUnroll * 16;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    char* __restrict__ key_cache, char* __restrict__ value_cache,
+    const int64_t* __restrict__ block_mapping, int slices_per_block, uint32_t block_bytes,
+    int64_t num_blocks) {
+    const int pair = blockIdx.x / slices_per_block;
+    const int slice = blockIdx.x - pair * slices_per_block;
+    const int64_t src = block_mapping[2 * (int64_t)pair];
+    const int64_t dst = block_mapping[2 * (int64_t)pair + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;  // uniform
+    const uint32_t begin = (uint32_t)slice * kCopySlice;
+    const uint32_t left = block_bytes - begin;
+    const uint32_t range = left < kCopySlice ? left : kCopySlice;
+    const size_t so = (size_t)src * block_bytes + begin, dof = (size_t)dst * block_bytes + begin;
+    const __amdgpu_buffer_rsrc_t ks = make_rsrc(key_cache + so, range);
+    const __amdgpu_buffer_rsrc_t vs = make_rsrc(value_cache + so, range);
+    const __amdgpu_buffer_rsrc_t kd = make_rsrc(key_cache + dof, range);
+    const __amdgpu_buffer_rsrc_t vd = make_rsrc(value_cache + dof, range);
+    u32x4 k[kCopyUnroll], v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const uint32_t off = (uint32_t)(u * kCopyThreads + threadIdx.x) * 16;
+        k[u] = buffer_load16(ks, off);
+        v[u] = buffer_load16(vs, off);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const uint32_t off = (uint32_t)(u * kCopyThreads + threadIdx.x) * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(k[u], kd, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v[u], vd, (int)off, 0, 0);
+    }
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -77,3 +124,31 @@ extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value, vo
                        (int64_t)num_blocks * block_size);
     return check_launch("pa_reshape_and_cache");
 }
+
+extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache,
+                                    const int64_t* block_mapping, int num_pairs,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, pa_dtype dtype, void* stream) {
+    using namespace pa;
+    clear_error();
+    PA_REQUIRE(num_pairs >= 0, PA_ERR_SHAPE, "num_pairs %d < 0", num_pairs);
+    PA_REQUIRE(num_kv_heads > 0 && head_dim > 0 && num_blocks > 0 && block_size > 0,
+               PA_ERR_SHAPE, "num_kv_heads, head_dim, num_blocks, block_size must be > 0");
+    PA_REQUIRE(dtype == PA_F16 || dtype == PA_BF16, PA_ERR_DTYPE,
+               "cache dtype must be PA_F16 or PA_BF16");
+    const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * 2;
+    PA_REQUIRE(block_bytes % 16 == 0 && block_bytes < ((int64_t)1 << 31), PA_ERR_UNSUPPORTED,
+               "a block must be a multiple of 16 bytes and below 2 GiB");
+    if (num_pairs == 0) return PA_OK;
+    PA_REQUIRE(key_cache && value_cache && block_mapping, PA_ERR_NULL, "null pointer argument");
+    PA_REQUIRE(aligned16(key_cache) && aligned16(value_cache), PA_ERR_ALIGNMENT,
+               "caches must be 16-byte aligned");
+    const int slices = (int)((block_bytes + kCopySlice - 1) / kCopySlice);
+    const int64_t grid = (int64_t)num_pairs * slices;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "too many pairs");
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0,
+                       (hipStream_t)stream, (char*)key_cache, (char*)value_cache, block_mapping,
+                       slices, (uint32_t)block_bytes, (int64_t)num_blocks);
+    return check_launch("pa_copy_blocks");
+}
+

@@ -69,6 +69,8 @@ def load():
     lib.pa_decode_split_workspace_bytes.restype = sz
     lib.pa_lse_merge.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.pa_lse_merge.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_copy_blocks.restype = i32
     lib.pa_stream_read.argtypes = [vp, sz, vp, vp]
     lib.pa_stream_read.restype = i32
     lib.pa_status_string.argtypes = [i32]
@@ -139,6 +141,25 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
         key.stride(0) if T else Hkv * D, value.stride(0) if T else Hkv * D, Hkv, D, NB, BS,
         _DT[key_cache.dtype], _stream(key_cache))
     _check(st, "pa_reshape_and_cache")
+
+
+def copy_blocks(key_cache, value_cache, block_mapping):
+    """Copy block src to block dst of both caches for every row (src, dst) of
+    block_mapping (int64 [N, 2]), in place; see pa_copy_blocks."""
+    _on_gpu(key_cache, value_cache, block_mapping)
+    _need(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+          and block_mapping.shape[1] == 2 and block_mapping.is_contiguous(),
+          "block_mapping must be a contiguous int64 [N, 2] tensor")
+    _need(key_cache.dtype == value_cache.dtype and key_cache.dtype in (torch.float16, torch.bfloat16),
+          "caches must share an fp16/bf16 dtype")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous()
+          and key_cache.shape == value_cache.shape and key_cache.dim() == 4, "caches must be contiguous "
+          "[num_blocks, block_size, num_kv_heads, head_dim] tensors of one shape")
+    NB, BS, Hkv, D = key_cache.shape
+    st = load().pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(block_mapping),
+                               block_mapping.shape[0], Hkv, D, BS, NB, _DT[key_cache.dtype],
+                               _stream(key_cache))
+    _check(st, "pa_copy_blocks")
 
 
 def _decode_common(query, key_cache, value_cache, block_tables, context_lens, out, out_dtype):

@@ -117,3 +117,14 @@ def test_stream_read_rejects_bad_buffers(lib):
     assert lib.pa_stream_read(p, 1024, None, None) == 1
     assert lib.pa_stream_read(p + 8, 1024, p, None) == 7    # misaligned
     assert lib.pa_stream_read(None, 0, None, None) == 0     # nothing to read
+
+
+def test_copy_blocks_rejects_bad_arguments(lib):
+    p = 1 << 12
+    assert lib.pa_copy_blocks(p, p, p, -1, 8, 128, 16, 64, 0, None) == 2
+    assert lib.pa_copy_blocks(p, p, p, 4, 0, 128, 16, 64, 0, None) == 2
+    assert lib.pa_copy_blocks(p, p, p, 4, 8, 128, 16, 64, 2, None) == 3     # fp32 caches
+    assert lib.pa_copy_blocks(p, p, p, 4, 1, 3, 1, 64, 0, None) == 4        # 6-byte blocks
+    assert lib.pa_copy_blocks(p, None, p, 4, 8, 128, 16, 64, 0, None) == 1
+    assert lib.pa_copy_blocks(p + 8, p, p, 4, 8, 128, 16, 64, 0, None) == 7
+    assert lib.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 64, 0, None) == 0

@@ -7,6 +7,7 @@ outputs (a correctly rounded bf16 value already differs from the exact one by
 up to half an ulp, 3.9e-3 in [1, 2)).
 """
 
+import json
 import math
 import os
 
@@ -483,3 +484,67 @@ def test_two_heads_per_workgroup_on_a_sparse_rectangle(fused):
     kc, vc, ref = _oracle_step(b)
     assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
     _assert_close(to_host_f64(out), ref, "f32", "sparse rectangle fused=%s" % fused)
+
+
+# ---- copy-on-write block copy ---------------------------------------------
+
+@pytest.mark.parametrize("dtype,NB,BS,Hkv,D,N", [
+    ("f16", 64, 16, 8, 128, 20),
+    ("bf16", 100, 32, 1, 64, 37),
+    ("f16", 50, 16, 3, 64, 11),    # 6 KiB blocks: one partial 16 KiB slice
+    ("bf16", 300, 16, 40, 128, 120),  # 160 KiB blocks: ten slices
+])
+def test_copy_blocks_bit_exact(dtype, NB, BS, Hkv, D, N):
+    rng = np.random.default_rng(NB + N)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    kc = torch.randn((NB, BS, Hkv, D), generator=torch.Generator().manual_seed(N)).to(tdt).cuda()
+    vc = torch.randn((NB, BS, Hkv, D), generator=torch.Generator().manual_seed(N + 1)).to(tdt).cuda()
+    perm = rng.permutation(NB)
+    pairs = np.stack([perm[:N], perm[N:2 * N]], axis=1).astype(np.int64)
+    bad = np.array([[-1, perm[2 * N]], [perm[2 * N + 1], NB + 3]], dtype=np.int64)  # skipped
+    mapping = np.concatenate([pairs[: N // 2], bad, pairs[N // 2:]], axis=0)
+    kc0, vc0 = to_host_bits(kc), to_host_bits(vc)
+    palib.copy_blocks(kc, vc, torch.from_numpy(mapping).cuda())
+    torch.cuda.synchronize()
+    rk, rv = oracle.copy_blocks(kc0, vc0, pairs)
+    assert np.array_equal(to_host_bits(kc), rk)
+    assert np.array_equal(to_host_bits(vc), rv)
+
+
+def test_copy_on_write_scenario_end_to_end():
+    # the page's parallel-sampling case on the device: four candidates share a
+    # 1000-token prompt; after the copies each candidate attends through its
+    # own table and gets the parent's output bit for bit
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "copy_on_write.json")))
+    n, k, bs = (fx["printed"][x] for x in ("prompt_tokens", "candidates", "block_size"))
+    NB, Hkv, D = 96, 4, 128
+    m = W.BlockManager(np.random.default_rng(5).permutation(NB), bs)
+    m.allocate("c0", n)
+    for c in range(1, k):
+        m.fork("c0", "c%d" % c)
+    parent = list(m.allocated["c0"])
+    pairs = []
+    for c in list(range(1, k)) + [0]:
+        _, cow = m.append_slot("c%d" % c, n)
+        if cow is not None:
+            pairs.append(cow)
+    assert len(pairs) == 3
+    kc = torch.randn((NB, bs, Hkv, D), generator=torch.Generator().manual_seed(7)).half().cuda()
+    vc = torch.randn((NB, bs, Hkv, D), generator=torch.Generator().manual_seed(8)).half().cuda()
+    palib.copy_blocks(kc, vc, torch.tensor(pairs, dtype=torch.int64, device="cuda"))
+    MB = len(parent)
+    tables = [parent] + [list(m.allocated["c%d" % c]) for c in range(k)]
+    bt = torch.tensor(tables, dtype=torch.int32, device="cuda")
+    cl = torch.full((k + 1,), n, dtype=torch.int32, device="cuda")
+    q1 = torch.randn((1, Hkv, D), generator=torch.Generator().manual_seed(9)).half()
+    q = q1.expand(k + 1, Hkv, D).contiguous().cuda()
+    out = palib.decode_split(q, kc, vc, bt, cl, 1.0 / math.sqrt(D), partition_size=256,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for c in range(1, k + 1):
+        assert np.array_equal(got[c], got[0])
+    ref = oracle.decode(q1.numpy(), kc.cpu().numpy(), vc.cpu().numpy(),
+                        np.array([parent], dtype=np.int32), np.array([n], dtype=np.int32),
+                        1.0 / math.sqrt(D), "f16")
+    _assert_close(got[:1].astype(np.float64), ref, "f32", "copy-on-write prompt")
