@@ -20,4 +20,5 @@ from .paged_attention import (  # noqa: F401
     lse_merge,
     decode_split,
     copy_blocks,
+    swap_blocks,
 )

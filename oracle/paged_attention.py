@@ -275,3 +275,25 @@ def copy_blocks(key_cache, value_cache, block_mapping):
         vc[dst] = src_v[src]
     return kc, vc
 
+
+# ---------------------------------------------------------------------------
+# Swapping blocks between pools ("vLLM 核心：PagedAttention 与 Continuous
+# Batching" §5, strategy 1)
+# ---------------------------------------------------------------------------
+
+
+def swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, block_mapping):
+    """Return copies of the destination pool's caches where, for every pair
+    (s, d) of block_mapping ([N, 2]), block d holds block s of the source pool
+    (K and V, bitwise). The swap-out of a preempted request copies its KV
+    blocks from GPU to CPU memory; the swap-in copies them back, possibly to
+    other physical blocks. The destinations are distinct."""
+    kd = np.array(dst_key_cache, copy=True)
+    vd = np.array(dst_value_cache, copy=True)
+    pairs = np.asarray(block_mapping).reshape(-1, 2)
+    for n in range(pairs.shape[0]):
+        src, dst = int(pairs[n, 0]), int(pairs[n, 1])
+        kd[dst] = np.asarray(src_key_cache)[src]
+        vd[dst] = np.asarray(src_value_cache)[src]
+    return kd, vd
+

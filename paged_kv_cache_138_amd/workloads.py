@@ -170,6 +170,22 @@ class BlockManager:
             return new * self.block_size + off, (last, new)
         return last * self.block_size + off, None
 
+    def move_out(self, seq_id, other):
+        """Move seq_id's blocks into the pool managed by `other` (the swap-out
+        of "vLLM 核心：PagedAttention 与 Continuous Batching" §5: a preempted
+        request's KV blocks are copied to CPU memory and its GPU blocks freed).
+        Returns the (block here, block there) pairs to copy. The blocks keep
+        their logical order in the sequence's new table."""
+        if any(self.refcount[b] > 1 for b in self.allocated.get(seq_id, [])):
+            raise ValueError("shared blocks stay resident: only a table's private blocks move")
+        mine = list(self.allocated.get(seq_id, []))
+        if len(other.free_blocks) < len(mine):
+            raise OutOfBlocks("need %d blocks there, %d free" % (len(mine), len(other.free_blocks)))
+        theirs = [other._pop() for _ in mine]
+        other.allocated[seq_id] = theirs
+        self.free(seq_id)
+        return list(zip(mine, theirs))
+
     def free(self, seq_id):
         for b in self.allocated.pop(seq_id, []):
             self.refcount[b] -= 1

@@ -504,3 +504,54 @@ def test_planted_copy_mistakes_are_caught(mistake):
         ok &= np.array_equal(gk.view(np.uint16), ref_k.view(np.uint16))
         ok &= np.array_equal(gv.view(np.uint16), ref_v.view(np.uint16))
     assert not ok
+
+
+# ---------------------------------------------------------------------------
+# Swapping ("vLLM 核心：PagedAttention 与 Continuous Batching" §5)
+# ---------------------------------------------------------------------------
+
+
+def _swap_round_trip(skip_v=False, seed=11):
+    from paged_kv_cache_138_amd import workloads as W
+    bs, H, D, L = 16, 2, 16, 100
+    rng = np.random.default_rng(seed)
+    gpu = W.BlockManager(rng.permutation(40), bs)
+    host = W.BlockManager(range(20), bs)
+    gpu.allocate("a", L)
+    table0 = list(gpu.allocated["a"])
+    kc = rng.standard_normal((40, bs, H, D)).astype(np.float16)
+    vc = rng.standard_normal((40, bs, H, D)).astype(np.float16)
+    hk = np.zeros((20, bs, H, D), np.float16)
+    hv = np.zeros((20, bs, H, D), np.float16)
+    out = np.array(gpu.move_out("a", host), dtype=np.int64)
+    hk, hv2 = oracle.swap_blocks(hk, hv, kc, vc, out)
+    hv = hv if skip_v else hv2
+    gpu.allocate("other", 16 * 8)
+    # the GPU blocks the request had are reused: scribble over them
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in gpu.allocated["other"]:
+        kc2[b] = 7.0
+        vc2[b] = -7.0
+    back = np.array(host.move_out("a", gpu), dtype=np.int64)
+    kc3, vc3 = oracle.swap_blocks(kc2, vc2, hk, hv, back)
+    return L, bs, table0, list(gpu.allocated["a"]), kc, vc, kc3, vc3
+
+
+def test_swap_round_trip_restores_the_sequence():
+    L, bs, t0, t1, kc, vc, kc3, vc3 = _swap_round_trip()
+    g0 = _gather2(kc, vc, t0, L, bs)
+    g1 = _gather2(kc3, vc3, t1, L, bs)
+    assert np.array_equal(g0[0].view(np.uint16), g1[0].view(np.uint16))
+    assert np.array_equal(g0[1].view(np.uint16), g1[1].view(np.uint16))
+    q = np.random.default_rng(4).standard_normal((1, 2, 16)).astype(np.float16)
+    lens = np.array([L], dtype=np.int32)
+    a = oracle.decode(q, kc, vc, np.array([t0], dtype=np.int32), lens, 0.25, "f16")
+    b = oracle.decode(q, kc3, vc3, np.array([t1], dtype=np.int32), lens, 0.25, "f16")
+    assert np.array_equal(a, b)
+
+
+def test_planted_swap_mistake_is_caught():
+    L, bs, t0, t1, kc, vc, kc3, vc3 = _swap_round_trip(skip_v=True)
+    g0 = _gather2(kc, vc, t0, L, bs)
+    g1 = _gather2(kc3, vc3, t1, L, bs)
+    assert not np.array_equal(g0[1].view(np.uint16), g1[1].view(np.uint16))

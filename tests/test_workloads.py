@@ -168,3 +168,27 @@ def test_copy_on_write_parallel_sampling_scenario():
     m2.fork("a", "b")
     slot, cow = m2.append_slot("b", 2 * bs)
     assert cow is None and slot // bs not in m2.allocated["a"]
+
+
+def test_swap_out_and_back_keeps_the_table_order():
+    # "vLLM 核心…" §5 strategy 1: a preempted request's blocks go to CPU
+    # memory (its GPU blocks are freed) and come back when it resumes, into
+    # whatever GPU blocks are free then; the table keeps its logical order
+    gpu = W.BlockManager(range(64), 16)
+    host = W.BlockManager(range(1000, 1032), 16)
+    gpu.allocate("a", 100)                      # 7 blocks
+    gpu.allocate("b", 40)
+    before = list(gpu.allocated["a"])
+    out = gpu.move_out("a", host)
+    assert [g for g, _ in out] == before
+    assert "a" not in gpu.allocated and all(b in gpu.free_blocks[-7:] for b in before)
+    assert host.allocated["a"] == [h for _, h in out]
+    gpu.allocate("c", 16 * 30)                  # someone takes free blocks meanwhile
+    back = host.move_out("a", gpu)
+    assert [h for h, _ in back] == [h for _, h in out]
+    assert gpu.allocated["a"] == [g for _, g in back]
+    assert len(set(gpu.allocated["a"]) & set(gpu.allocated["b"] + gpu.allocated["c"])) == 0
+    # shared blocks stay resident
+    gpu.fork("b", "b2")
+    with pytest.raises(ValueError):
+        gpu.move_out("b2", host)
