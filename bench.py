@@ -52,9 +52,10 @@ def parse():
                     help="override the context-length recipe (e.g. fixed:1094); not the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--op", choices=["decode", "copy_blocks"], default="decode",
+    ap.add_argument("--op", choices=["decode", "copy_blocks", "swap_blocks"], default="decode",
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
-                         "block copy on the workload's cache shape")
+                         "block copy on the workload's cache shape; swap_blocks: blocks to "
+                         "pinned host memory and back")
     ap.add_argument("--pairs", type=int, default=1024, help="copy_blocks: block pairs per launch")
     ap.add_argument("--ceiling-gib", type=float, default=4.0,
                     help="buffer size of the streaming-read ceiling measurement (0 skips it)")
@@ -175,6 +176,9 @@ def main():
         return
     if args.op == "copy_blocks":
         bench_copy_blocks(args)
+        return
+    if args.op == "swap_blocks":
+        bench_swap_blocks(args)
         return
     import numpy as np
     import torch
@@ -391,6 +395,69 @@ def bench_copy_blocks(args):
                                "unit": "GB/s", "cores": 1, "kind": "oracle",
                                "sample": "%d runs of %d pairs (whole-cache copies included)"
                                          % (reps, sample)}
+    print(json.dumps(res), flush=True)
+
+
+def bench_swap_blocks(args):
+    """Swap --pairs random blocks of the workload's cache shape to a pinned
+    host pool (swap-out) and back (swap-in), each as one pa_swap_blocks
+    launch, against the host link's measured ceiling: a DMA copy of a 1 GiB
+    pinned buffer in the same direction."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_138_amd import lib as palib
+    from paged_kv_cache_138_amd import workloads as W
+    w = W.WORKLOADS[args.workload]
+    NB, BS, Hkv, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    N = min(args.pairs, NB // 2)
+    K = max(1, min(args.steps, 10))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        kc = torch.empty((NB, BS, Hkv, D), dtype=tdt, device="cuda").normal_()
+        vc = torch.empty_like(kc).normal_()
+        hk = torch.empty((N, BS, Hkv, D), dtype=tdt).pin_memory()
+        hv = torch.empty_like(hk).pin_memory()
+        perm = np.random.default_rng(args.seed).permutation(NB)
+        out_map = torch.from_numpy(np.stack([perm[:N], np.arange(N)], 1).astype(np.int64)).cuda()
+        in_map = torch.from_numpy(np.stack([np.arange(N), perm[N:2 * N]], 1).astype(np.int64)).cuda()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(K):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / K
+
+        ms_out = timed(lambda: palib.swap_blocks(hk, hv, kc, vc, out_map))
+        ms_in = timed(lambda: palib.swap_blocks(kc, vc, hk, hv, in_map))
+        big_d = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        big_h = torch.empty(1 << 30, dtype=torch.uint8).pin_memory()
+        dma_d2h = timed(lambda: big_h.copy_(big_d, non_blocking=True))
+        dma_h2d = timed(lambda: big_d.copy_(big_h, non_blocking=True))
+    block_bytes = BS * Hkv * D * W.element_bytes(w.dtype)
+    nbytes = N * block_bytes * 2
+    g = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 2)
+    out_gbs, in_gbs = g(nbytes, ms_out), g(nbytes, ms_in)
+    ceil_out, ceil_in = g(1 << 30, dma_d2h), g(1 << 30, dma_h2d)
+    res = {"metric": "swap blocks to pinned host memory and back: host-link GB/s",
+           "value": round((out_gbs + in_gbs) / 2, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+           "warmup": 1, "ms_per_step": round(ms_out + ms_in, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "op": "swap_blocks", "pairs": N, "block_bytes": block_bytes},
+           "swap_out_GB_per_s": out_gbs, "swap_in_GB_per_s": in_gbs,
+           "roofline": {"bound": "host_link", "achieved": round((out_gbs + in_gbs) / 2, 2),
+                        "peak": round((ceil_out + ceil_in) / 2, 2), "unit": "GB/s",
+                        "frac": round((out_gbs + in_gbs) / (ceil_out + ceil_in), 4), "traffic": None,
+                        "peak_is": "measured DMA copy of 1 GiB pinned <-> device (%.1f out, %.1f in GB/s)"
+                                   % (ceil_out, ceil_in),
+                        "kernel": "pa_swap_blocks: %d launches each way, avg %.1f / %.1f us"
+                                  % (K, ms_out * 1e3, ms_in * 1e3)}}
     print(json.dumps(res), flush=True)
 
 

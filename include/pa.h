@@ -113,6 +113,29 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bloc
                          int num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * pa_swap_blocks - copy blocks between two pools, one of which may live in
+ * pinned host memory ("vLLM 核心：PagedAttention 与 Continuous Batching" §5,
+ * strategy 1: a preempted request's KV blocks are copied to CPU memory and
+ * back when it resumes).
+ *
+ *   dst_key_cache, dst_value_cache  [dst_num_blocks, block_size,
+ *                     num_kv_heads, head_dim]: the destination pool.
+ *   src_key_cache, src_value_cache  [src_num_blocks, ...]: the source pool.
+ *   block_mapping     int64 [num_pairs, 2]: row n = (src block, dst block).
+ * Each pool and the mapping must be device memory or pinned host memory the
+ * device can address (e.g. hipHostMalloc'd); anything else returns
+ * PA_ERR_UNSUPPORTED before any launch. Pairs with an id outside their pool
+ * are skipped; destinations must be distinct (caller contract). One kernel
+ * launch on `stream` moves all pairs; for a host pool its bandwidth is that
+ * of the host link.
+ */
+pa_status pa_swap_blocks(void* dst_key_cache, void* dst_value_cache, int dst_num_blocks,
+                         const void* src_key_cache, const void* src_value_cache,
+                         int src_num_blocks, const int64_t* block_mapping, int num_pairs,
+                         int num_kv_heads, int head_dim, int block_size, pa_dtype dtype,
+                         void* stream);
+
+/*
  * pa_decode - one query token per sequence attends over its paged context,
  * in a single launch (no workspace).
  *

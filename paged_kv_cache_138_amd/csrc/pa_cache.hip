@@ -52,23 +52,26 @@ constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;  // per cache: 4 K + 4 V loads in flight per thread
 constexpr uint32_t kCopySlice = kCopyThreads * kCopyUnroll * 16;
 
+// Also the swap between two pools (pa_swap_blocks): source and destination
+// caches are then different allocations, one of them in pinned host memory
+// that the device reads or writes across the host link.
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    char* __restrict__ key_cache, char* __restrict__ value_cache,
-    const int64_t* __restrict__ block_mapping, int slices_per_block, uint32_t block_bytes,
-    int64_t num_blocks) {
+    char* __restrict__ dst_key, char* __restrict__ dst_value, const char* src_key,
+    const char* src_value, const int64_t* __restrict__ block_mapping, int slices_per_block,
+    uint32_t block_bytes, int64_t src_blocks, int64_t dst_blocks) {
     const int pair = blockIdx.x / slices_per_block;
     const int slice = blockIdx.x - pair * slices_per_block;
     const int64_t src = block_mapping[2 * (int64_t)pair];
     const int64_t dst = block_mapping[2 * (int64_t)pair + 1];
-    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;  // uniform
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;  // uniform
     const uint32_t begin = (uint32_t)slice * kCopySlice;
     const uint32_t left = block_bytes - begin;
     const uint32_t range = left < kCopySlice ? left : kCopySlice;
     const size_t so = (size_t)src * block_bytes + begin, dof = (size_t)dst * block_bytes + begin;
-    const __amdgpu_buffer_rsrc_t ks = make_rsrc(key_cache + so, range);
-    const __amdgpu_buffer_rsrc_t vs = make_rsrc(value_cache + so, range);
-    const __amdgpu_buffer_rsrc_t kd = make_rsrc(key_cache + dof, range);
-    const __amdgpu_buffer_rsrc_t vd = make_rsrc(value_cache + dof, range);
+    const __amdgpu_buffer_rsrc_t ks = make_rsrc(src_key + so, range);
+    const __amdgpu_buffer_rsrc_t vs = make_rsrc(src_value + so, range);
+    const __amdgpu_buffer_rsrc_t kd = make_rsrc(dst_key + dof, range);
+    const __amdgpu_buffer_rsrc_t vd = make_rsrc(dst_value + dof, range);
     u32x4 k[kCopyUnroll], v[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
@@ -147,8 +150,77 @@ extern "C" pa_status pa_copy_blocks(void* key_cache, void* value_cache,
     const int64_t grid = (int64_t)num_pairs * slices;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "too many pairs");
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0,
-                       (hipStream_t)stream, (char*)key_cache, (char*)value_cache, block_mapping,
-                       slices, (uint32_t)block_bytes, (int64_t)num_blocks);
+                       (hipStream_t)stream, (char*)key_cache, (char*)value_cache,
+                       (const char*)key_cache, (const char*)value_cache, block_mapping, slices,
+                       (uint32_t)block_bytes, (int64_t)num_blocks, (int64_t)num_blocks);
     return check_launch("pa_copy_blocks");
+}
+
+namespace {
+
+// The address under which the device reaches p: device memory as is, pinned
+// host memory through its mapping. Anything else (pageable host memory,
+// unknown pointers) is refused before a kernel could fault on it.
+bool device_address(const void* p, const void** dev) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of the failed query
+        return false;
+    }
+    if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+        *dev = p;
+        return true;
+    }
+    if (at.type == hipMemoryTypeHost && at.devicePointer) {
+        // p may point inside the allocation: keep its offset from the host base
+        const char* hb = (const char*)at.hostPointer;
+        const char* db = (const char*)at.devicePointer;
+        *dev = hb ? db + ((const char*)p - hb) : db;
+        return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_swap_blocks(void* dst_key_cache, void* dst_value_cache,
+                                    int dst_num_blocks, const void* src_key_cache,
+                                    const void* src_value_cache, int src_num_blocks,
+                                    const int64_t* block_mapping, int num_pairs,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    pa_dtype dtype, void* stream) {
+    using namespace pa;
+    clear_error();
+    PA_REQUIRE(num_pairs >= 0, PA_ERR_SHAPE, "num_pairs %d < 0", num_pairs);
+    PA_REQUIRE(num_kv_heads > 0 && head_dim > 0 && block_size > 0 && src_num_blocks > 0 &&
+                   dst_num_blocks > 0,
+               PA_ERR_SHAPE, "sizes and block counts must be > 0");
+    PA_REQUIRE(dtype == PA_F16 || dtype == PA_BF16, PA_ERR_DTYPE,
+               "cache dtype must be PA_F16 or PA_BF16");
+    const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * 2;
+    PA_REQUIRE(block_bytes % 16 == 0 && block_bytes < ((int64_t)1 << 31), PA_ERR_UNSUPPORTED,
+               "a block must be a multiple of 16 bytes and below 2 GiB");
+    if (num_pairs == 0) return PA_OK;
+    PA_REQUIRE(dst_key_cache && dst_value_cache && src_key_cache && src_value_cache &&
+                   block_mapping,
+               PA_ERR_NULL, "null pointer argument");
+    PA_REQUIRE(aligned16(dst_key_cache) && aligned16(dst_value_cache) &&
+                   aligned16(src_key_cache) && aligned16(src_value_cache),
+               PA_ERR_ALIGNMENT, "caches must be 16-byte aligned");
+    const void *dk, *dv, *sk, *sv, *bm;
+    PA_REQUIRE(device_address(dst_key_cache, &dk) && device_address(dst_value_cache, &dv) &&
+                   device_address(src_key_cache, &sk) && device_address(src_value_cache, &sv) &&
+                   device_address(block_mapping, &bm),
+               PA_ERR_UNSUPPORTED,
+               "every pool and the mapping must be device memory or pinned host memory "
+               "mapped for the device");
+    const int slices = (int)((block_bytes + kCopySlice - 1) / kCopySlice);
+    const int64_t grid = (int64_t)num_pairs * slices;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "too many pairs");
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0,
+                       (hipStream_t)stream, (char*)dk, (char*)dv, (const char*)sk,
+                       (const char*)sv, (const int64_t*)bm, slices, (uint32_t)block_bytes,
+                       (int64_t)src_num_blocks, (int64_t)dst_num_blocks);
+    return check_launch("pa_swap_blocks");
 }
 

@@ -71,6 +71,8 @@ def load():
     lib.pa_lse_merge.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
     lib.pa_stream_read.argtypes = [vp, sz, vp, vp]
     lib.pa_stream_read.restype = i32
     lib.pa_status_string.argtypes = [i32]
@@ -160,6 +162,32 @@ def copy_blocks(key_cache, value_cache, block_mapping):
                                block_mapping.shape[0], Hkv, D, BS, NB, _DT[key_cache.dtype],
                                _stream(key_cache))
     _check(st, "pa_copy_blocks")
+
+
+def swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, block_mapping):
+    """Copy block s of the source pool to block d of the destination pool for
+    every row (s, d) of block_mapping (int64 [N, 2]); either pool may be a
+    pinned CPU tensor (pin_memory=True), see pa_swap_blocks."""
+    caches = (dst_key_cache, dst_value_cache, src_key_cache, src_value_cache)
+    for t in caches + (block_mapping,):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+        _need(t.is_cuda or t.is_pinned(), "tensors must be on the GPU or in pinned host memory")
+    _need(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+          and block_mapping.shape[1] == 2, "block_mapping must be an int64 [N, 2] tensor")
+    dt = dst_key_cache.dtype
+    _need(all(t.dtype == dt for t in caches) and dt in (torch.float16, torch.bfloat16),
+          "caches must share an fp16/bf16 dtype")
+    _need(dst_key_cache.shape == dst_value_cache.shape and src_key_cache.shape == src_value_cache.shape
+          and dst_key_cache.dim() == 4 and dst_key_cache.shape[1:] == src_key_cache.shape[1:],
+          "pools must be [num_blocks, block_size, num_kv_heads, head_dim] of one row shape")
+    NBd, BS, Hkv, D = dst_key_cache.shape
+    NBs = src_key_cache.shape[0]
+    cuda = [t.device for t in caches + (block_mapping,) if t.is_cuda]
+    dev = cuda[0] if cuda else torch.device("cuda", torch.cuda.current_device())
+    st = load().pa_swap_blocks(_ptr(dst_key_cache), _ptr(dst_value_cache), NBd, _ptr(src_key_cache),
+                               _ptr(src_value_cache), NBs, _ptr(block_mapping), block_mapping.shape[0],
+                               Hkv, D, BS, _DT[dt], torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "pa_swap_blocks")
 
 
 def _decode_common(query, key_cache, value_cache, block_tables, context_lens, out, out_dtype):

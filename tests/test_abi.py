@@ -128,3 +128,17 @@ def test_copy_blocks_rejects_bad_arguments(lib):
     assert lib.pa_copy_blocks(p, None, p, 4, 8, 128, 16, 64, 0, None) == 1
     assert lib.pa_copy_blocks(p + 8, p, p, 4, 8, 128, 16, 64, 0, None) == 7
     assert lib.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 64, 0, None) == 0
+
+
+def test_swap_blocks_rejects_bad_arguments(lib):
+    p = 1 << 12
+    a = [p, p, 64, p, p, 32, p]  # dst pool, src pool, mapping
+    assert lib.pa_swap_blocks(*a, -1, 8, 128, 16, 0, None) == 2
+    assert lib.pa_swap_blocks(p, p, 0, p, p, 32, p, 4, 8, 128, 16, 0, None) == 2  # empty pool
+    assert lib.pa_swap_blocks(*a, 4, 8, 128, 16, 2, None) == 3                     # fp32
+    assert lib.pa_swap_blocks(p, None, 64, p, p, 32, p, 4, 8, 128, 16, 0, None) == 1
+    assert lib.pa_swap_blocks(p, p, 64, p + 8, p, 32, p, 4, 8, 128, 16, 0, None) == 7
+    # addresses no device can reach (here: plain integers) are refused before
+    # any launch
+    assert lib.pa_swap_blocks(*a, 4, 8, 128, 16, 0, None) == 4
+    assert lib.pa_swap_blocks(*a, 0, 8, 128, 16, 0, None) == 0

@@ -548,3 +548,63 @@ def test_copy_on_write_scenario_end_to_end():
                         np.array([parent], dtype=np.int32), np.array([n], dtype=np.int32),
                         1.0 / math.sqrt(D), "f16")
     _assert_close(got[:1].astype(np.float64), ref, "f32", "copy-on-write prompt")
+
+
+# ---- swapping blocks to pinned host memory and back ------------------------
+
+def test_swap_out_and_in_through_pinned_host_memory():
+    # "vLLM 核心…" §5: a request's blocks go to CPU memory and come back into
+    # other GPU blocks; both copies are bit-exact and the request attends to
+    # the same context afterwards
+    bs, Hkv, D, L = 16, 4, 128, 300
+    rng = np.random.default_rng(61)
+    gpu = W.BlockManager(rng.permutation(64), bs)
+    host = W.BlockManager(range(40), bs)
+    gpu.allocate("r", L)
+    gpu.allocate("other0", 100)
+    t0 = list(gpu.allocated["r"])
+    kc = torch.randn((64, bs, Hkv, D), generator=torch.Generator().manual_seed(1)).bfloat16().cuda()
+    vc = torch.randn((64, bs, Hkv, D), generator=torch.Generator().manual_seed(2)).bfloat16().cuda()
+    hk = torch.zeros((40, bs, Hkv, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    q = torch.randn((1, 8, D), generator=torch.Generator().manual_seed(3)).bfloat16().cuda()
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    before = palib.decode_split(q, kc, vc, torch.tensor([t0], dtype=torch.int32, device="cuda"),
+                                lens, 0.0883883, partition_size=128, out_dtype=torch.float32)
+    out_pairs = np.array(gpu.move_out("r", host), dtype=np.int64)
+    kc0, vc0 = to_host_bits(kc), to_host_bits(vc)
+    palib.swap_blocks(hk, hv, kc, vc, torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    rk, rv = oracle.swap_blocks(np.zeros((40, bs, Hkv, D), np.uint16), np.zeros((40, bs, Hkv, D), np.uint16),
+                                kc0, vc0, out_pairs)
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), rk)
+    assert np.array_equal(hv.view(torch.int16).numpy().view(np.uint16), rv)
+    gpu.allocate("other1", 16 * 10)            # the freed blocks are reused meanwhile
+    for b in gpu.allocated["other1"]:
+        kc[b] = 9.0
+        vc[b] = -9.0
+    in_pairs = np.array(host.move_out("r", gpu), dtype=np.int64)
+    kc1, vc1 = to_host_bits(kc), to_host_bits(vc)
+    # the mapping may live in pinned host memory as well
+    palib.swap_blocks(kc, vc, hk, hv, torch.from_numpy(in_pairs).pin_memory())
+    torch.cuda.synchronize()
+    rk2, rv2 = oracle.swap_blocks(kc1, vc1, rk, rv, in_pairs)
+    assert np.array_equal(to_host_bits(kc), rk2)
+    assert np.array_equal(to_host_bits(vc), rv2)
+    t1 = list(gpu.allocated["r"])
+    after = palib.decode_split(q, kc, vc, torch.tensor([t1], dtype=torch.int32, device="cuda"),
+                               lens, 0.0883883, partition_size=128, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(before, after)
+
+
+def test_swap_refuses_pageable_host_memory():
+    kc = torch.zeros((8, 16, 2, 64), dtype=torch.float16, device="cuda")
+    pageable = torch.zeros((8, 16, 2, 64), dtype=torch.float16)
+    mapping = torch.tensor([[0, 1]], dtype=torch.int64, device="cuda")
+    # the raw call: the binding itself already refuses CPU tensors that are not pinned
+    st = palib.load().pa_swap_blocks(pageable.data_ptr(), pageable.data_ptr(), 8, kc.data_ptr(),
+                                     kc.data_ptr(), 8, mapping.data_ptr(), 1, 2, 64, 16, 0, None)
+    assert st == 4
+    with pytest.raises(ValueError):
+        palib.swap_blocks(pageable, pageable, kc, kc, mapping)
