@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--path", choices=["auto", "decode", "split", "split_prefix"], default="auto")
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="re-block the workload (same tokens and cache bytes, other block size)")
     ap.add_argument("--unfused", action="store_true",
                     help="split path: run the scatter as its own launch instead of inside the "
                          "partition launch (pa_decode_split_append)")
@@ -102,6 +104,24 @@ def copy_calibration(mib):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def pick_workload(args):
+    """The named workload, with --lens and --block-size applied."""
+    import dataclasses
+    from paged_kv_cache_138_amd import workloads as W
+    w = W.WORKLOADS[args.workload]
+    if args.lens:
+        w = dataclasses.replace(w, lens=args.lens, name=w.name + "+lens=" + args.lens)
+    if args.block_size and args.block_size != w.block_size:
+        bs, old = args.block_size, w.block_size
+        tokens, per_seq = w.num_blocks * old, w.max_blocks_per_seq * old
+        if tokens % bs or per_seq % bs or w.shared_prefix_tokens % bs:
+            raise SystemExit("block size %d does not divide the workload's pool and tables" % bs)
+        w = dataclasses.replace(w, block_size=bs, num_blocks=tokens // bs,
+                                max_blocks_per_seq=per_seq // bs,
+                                name=w.name + "+bs=%d" % bs)
+    return w
 
 
 def default_path(workload):
@@ -187,10 +207,7 @@ def main():
     from paged_kv_cache_138_amd.pipeline import DeviceBatch, RotatedBatch
 
     palib.load()  # fails loudly if libpa.so is missing
-    w = W.WORKLOADS[args.workload]
-    if args.lens:
-        import dataclasses
-        w = dataclasses.replace(w, lens=args.lens, name=w.name + "+lens=" + args.lens)
+    w = pick_workload(args)
     path = default_path(w) if args.path == "auto" else args.path
     t_gen = time.perf_counter()
     batch = W.make_batch(w, seed=args.seed)
@@ -344,7 +361,7 @@ def bench_copy_blocks(args):
     import torch
     from paged_kv_cache_138_amd import lib as palib
     from paged_kv_cache_138_amd import workloads as W
-    w = W.WORKLOADS[args.workload]
+    w = pick_workload(args)
     NB, BS, Hkv, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     N = min(args.pairs, NB // 4)
@@ -407,7 +424,7 @@ def bench_swap_blocks(args):
     import torch
     from paged_kv_cache_138_amd import lib as palib
     from paged_kv_cache_138_amd import workloads as W
-    w = W.WORKLOADS[args.workload]
+    w = pick_workload(args)
     NB, BS, Hkv, D = w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     N = min(args.pairs, NB // 2)

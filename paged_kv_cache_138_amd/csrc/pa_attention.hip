@@ -71,12 +71,18 @@ __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_kernel(AttnArgs a) {
     constexpr int LPR = D / 8;          // lanes per cache row
     constexpr int RPI = 64 / LPR;       // rows per load instruction
-    constexpr int IPB = BS / RPI;       // load instructions per block
     constexpr int NI = LPR;             // load instructions per chunk
     constexpr int CHUNK = RPI * NI;     // tokens per chunk (64)
-    constexpr int BPC = CHUNK / BS;     // blocks per chunk
+    constexpr int RPB = BS < 32 ? BS : 32;  // rows one load descriptor covers
+    constexpr int IPB = RPB / RPI;      // load instructions per descriptor
+    constexpr int BPC = CHUNK / RPB;    // descriptors per chunk
+    // with more than 4 blocks per chunk the descriptors of two chunks would
+    // not fit the scalar registers: keep each block's offset and range and
+    // build its descriptor when its loads are issued
+    constexpr bool LAZY = BPC > 4;
     static_assert(CHUNK == 64, "one score per lane per chunk");
-    static_assert(BS % RPI == 0 && CHUNK % BS == 0, "block must tile the chunk");
+    static_assert(RPB % RPI == 0 && CHUNK % BS == 0 && BS % RPB == 0,
+                  "blocks tile the chunk, descriptors the block");
     static_assert(LPR == 8 || LPR == 16, "head_dim 64 or 128");
 
     __shared__ float sm_m[NW];
@@ -162,42 +168,68 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
-    // per-block load descriptors of the chunk starting at token cs: the
-    // range of each covers exactly the block's rows below `end`, so rows
-    // past the context and blocks past the table (or with an id outside the
-    // pool) read as zeros and are never fetched
-    struct ChunkIds {
+    // load descriptors of the chunk starting at token cs, one per RPB rows
+    // (a whole block, or a block's slice when blocks are longer): the range
+    // of each covers exactly its rows below `end`, so rows past the context
+    // and blocks past the table (or with an id outside the pool) read as
+    // zeros and are never fetched
+    struct IdsEager {
         __amdgpu_buffer_rsrc_t k[BPC], v[BPC];
         bool ok[BPC];
     };
+    struct IdsLazy {
+        int pid[BPC];        // block id (0 when absent)
+        uint32_t nrec[BPC];  // bytes in range; 0 when absent
+        uint32_t okm;        // bit b: block b present
+    };
+    using ChunkIds = std::conditional_t<LAZY, IdsLazy, IdsEager>;
     auto fetch_ids = [&](int cs, ChunkIds& ci) {
+        if constexpr (LAZY) ci.okm = 0;
 #pragma unroll
         for (int b = 0; b < BPC; ++b) {
-            const int lb = cs / BS + b;
+            // chunks start on block boundaries (a block is never longer
+            // than a chunk), so block and row offset are known per b
+            const int lb = cs / BS + (b * RPB) / BS;
             const int pid = lb < nb ? bt[lb] : -1;
-            const int rows = min(max(end_c - (cs + b * BS), 0), BS);
+            const int rows = min(max(end_c - (cs + b * RPB), 0), RPB);
             const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
             const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
-            const size_t boff = (size_t)(ok ? pid : 0) * block_bytes;
-            ci.k[b] = make_rsrc(kbase + boff, nrec);
-            ci.v[b] = make_rsrc(vbase + boff, nrec);
-            ci.ok[b] = ok;
+            if constexpr (LAZY) {
+                ci.pid[b] = __builtin_amdgcn_readfirstlane(ok ? pid : 0);
+                ci.nrec[b] = __builtin_amdgcn_readfirstlane(nrec);
+                ci.okm |= (uint32_t)ok << b;
+            } else {
+                const size_t boff =
+                    (size_t)(ok ? pid : 0) * block_bytes + ((b * RPB) % BS) * row_bytes;
+                ci.k[b] = make_rsrc(kbase + boff, nrec);
+                ci.v[b] = make_rsrc(vbase + boff, nrec);
+                ci.ok[b] = ok;
+            }
         }
     };
-    auto issue = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[NI]) {
+    auto issue = [&](const ChunkIds& ci, auto is_v, u32x4 (&buf)[NI]) {
         // recomputing the IPB offsets here (one add each) keeps them out of
         // the registers that live across the chunk loop
         uint32_t o = loff0;
         asm("" : "+v"(o));
 #pragma unroll
         for (int b = 0; b < BPC; ++b) {
+            __amdgpu_buffer_rsrc_t rs;
+            if constexpr (LAZY)
+                rs = make_rsrc((is_v ? vbase : kbase) + (size_t)ci.pid[b] * block_bytes +
+                                   ((b * RPB) % BS) * row_bytes,
+                               ci.nrec[b]);
+            else
+                rs = is_v ? ci.v[b] : ci.k[b];
 #pragma unroll
             for (int j = 0; j < IPB; ++j)
-                buf[b * IPB + j] = buffer_load16(rs[b], o + (uint32_t)(j * RPI * row_bytes));
+                buf[b * IPB + j] = buffer_load16(rs, o + (uint32_t)(j * RPI * row_bytes));
         }
     };
+    constexpr std::false_type kK{};
+    constexpr std::true_type kV{};
     // scores of the chunk's 64 tokens, one per lane (log2 units, -inf if absent)
-    auto scores = [&](const u32x4 (&kr)[NI], int cs, const bool (&pok)[BPC]) -> float {
+    auto scores = [&](const u32x4 (&kr)[NI], int cs, const ChunkIds& ci) -> float {
         float pd[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -212,11 +244,16 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         tr_step<2>(pd, c);
         tr_step<1>(pd, c);
         const int myb = c / IPB;
-        const int mytok = cs + myb * BS + (c % IPB) * RPI + r;
-        bool ok = pok[0];
+        const int mytok = cs + myb * RPB + (c % IPB) * RPI + r;
+        bool ok;
+        if constexpr (LAZY) {
+            ok = (__builtin_amdgcn_readfirstlane(ci.okm) >> myb) & 1u;
+        } else {
+            ok = ci.ok[0];
 #pragma unroll
-        for (int b = 1; b < BPC; ++b)
-            if (myb == b) ok = pok[b];
+            for (int b = 1; b < BPC; ++b)
+                if (myb == b) ok = ci.ok[b];
+        }
         ok = ok && mytok < end_c;
         return ok ? pd[0] * a.scale_log2 : -INFINITY;
     };
@@ -267,21 +304,21 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         ChunkIds cur;
         u32x4 kr[NI], vr[NI];
         fetch_ids(cs, cur);
-        issue(cur.k, kr);
-        issue(cur.v, vr);
+        issue(cur, kK, kr);
+        issue(cur, kV, vr);
         for (;;) {
             const int nx = cs + cstep;
             const bool more = nx < end_c;
             ChunkIds nxt;
             if (more) fetch_ids(nx, nxt);
-            const float pr = update(scores(kr, cs, cur.ok));
+            const float pr = update(scores(kr, cs, cur));
             if (!more) {
                 pv(vr, pr);
                 break;
             }
-            issue(nxt.k, kr);
+            issue(nxt, kK, kr);
             pv(vr, pr);
-            issue(nxt.v, vr);
+            issue(nxt, kV, vr);
             cur = nxt;
             cs = nx;
         }
@@ -416,8 +453,10 @@ typedef void (*merge_fn)(MergeArgs);
 template <class KV, class OUT, int D>
 attn_fn pick_attn_bs(int bs) {
     switch (bs) {
+        case 8: return attn_partition_kernel<KV, OUT, D, 8, kWaves>;
         case 16: return attn_partition_kernel<KV, OUT, D, 16, kWaves>;
         case 32: return attn_partition_kernel<KV, OUT, D, 32, kWaves>;
+        case 64: return attn_partition_kernel<KV, OUT, D, 64, kWaves>;
     }
     return nullptr;
 }
@@ -450,8 +489,10 @@ attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs) {
 template <class KV, class OUT, int D, bool PREFIX>
 attn_fn pick_gqa_bs(int bs) {
     switch (bs) {
+        case 8: return attn_gqa_kernel<KV, OUT, D, 8, kGqaWaves, PREFIX>;
         case 16: return attn_gqa_kernel<KV, OUT, D, 16, kGqaWaves, PREFIX>;
         case 32: return attn_gqa_kernel<KV, OUT, D, 32, kGqaWaves, PREFIX>;
+        case 64: return attn_gqa_kernel<KV, OUT, D, 64, kGqaWaves, PREFIX>;
     }
     return nullptr;
 }
@@ -593,8 +634,9 @@ pa_status validate_decode(void* out, pa_dtype out_dtype, const void* query, cons
     PA_REQUIRE(isfinite(scale), PA_ERR_SHAPE, "scale must be finite");
     PA_REQUIRE(s.head_dim == 64 || s.head_dim == 128, PA_ERR_UNSUPPORTED,
                "head_dim %d not in {64, 128}", s.head_dim);
-    PA_REQUIRE(s.block_size == 16 || s.block_size == 32, PA_ERR_UNSUPPORTED,
-               "block_size %d not in {16, 32}", s.block_size);
+    PA_REQUIRE(s.block_size == 8 || s.block_size == 16 || s.block_size == 32 ||
+                   s.block_size == 64,
+               PA_ERR_UNSUPPORTED, "block_size %d not in {8, 16, 32, 64}", s.block_size);
     if (s.num_seqs == 0) return PA_OK;
     PA_REQUIRE(out && query && kc && vc && bt && cl, PA_ERR_NULL, "null pointer argument");
     PA_REQUIRE(aligned16(out) && aligned16(query) && aligned16(kc) && aligned16(vc),

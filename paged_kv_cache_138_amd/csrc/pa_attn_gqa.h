@@ -108,11 +108,13 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     constexpr int LPR = D / 8;          // lanes per row in a coalesced V load
     constexpr int RPI = 64 / LPR;       // rows per coalesced V load
     constexpr int VL = CH / RPI;        // V loads per chunk
-    constexpr int BPC = CH / BS;        // blocks per chunk (BS = 16 or 32)
+    constexpr int RPB = BS < CH ? BS : CH;  // rows one load descriptor covers
+    constexpr int BPC = CH / RPB;       // descriptors per chunk (blocks, or one block's slice)
     constexpr int ROWB = D * 2 + 16;    // LDS bytes per K or V row (padding spreads banks)
     constexpr int TILE = CH * ROWB;     // LDS bytes of one chunk's K (then V) rows
     constexpr int OROW = D + 4;         // floats per row of the wave's partial output
-    static_assert(BS == 16 || BS == 32, "block size 16 or 32");
+    static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
+    static_assert(RPB % RPI == 0, "the rows of one coalesced load share a block");
     static_assert(CH == 32 || CH == 64, "chunk of 32 or 64 tokens");
     static_assert(16 * OROW * 4 <= TILE, "the wave's LDS tile also holds its partial output");
     static_assert(VL * RPI == CH, "coalesced loads tile the chunk");
@@ -232,30 +234,38 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     struct ChunkIds {
         __amdgpu_buffer_rsrc_t k[BPC], v[BPC];
         bool ok[BPC];
+        uint32_t okm;  // bit b = ok[b] (read per lane when blocks are shorter than 16)
     };
     auto fetch_ids = [&](int cs, ChunkIds& ci) {
+        ci.okm = 0;
 #pragma unroll
         for (int b = 0; b < BPC; ++b) {
-            const int lb = cs / BS + b;
+            // descriptor b covers the RPB rows from token tok0 on: a whole
+            // block when blocks are no longer than a chunk, else the chunk's
+            // slice of its (single) block
+            const int tok0 = cs + b * RPB;
+            const int lb = tok0 / BS;
             const int pid = lb < nb ? bt[lb] : -1;
-            const int blk_tok0 = lb * BS;
-            const int rows = min(max(end - blk_tok0, 0), BS);
+            const int rows = min(max(end - tok0, 0), RPB);
             const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
             const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
-            const size_t boff = (size_t)(ok ? pid : 0) * block_bytes;
+            const size_t boff =
+                ok ? (size_t)pid * block_bytes + (size_t)(tok0 - lb * BS) * row_bytes : 0;
             ci.k[b] = make_rsrc(kbase + boff, nrec);
             ci.v[b] = make_rsrc(vbase + boff, nrec);
             ci.ok[b] = ok;
+            ci.okm |= (uint32_t)ok << b;
         }
     };
-    // Chunks start on block boundaries (partitions are whole blocks). Load i
-    // of a chunk brings rows vr + RPI*i (the RPI rows of one load share a block).
+    // Chunks start on descriptor boundaries (partitions are whole blocks, and
+    // a block longer than a chunk holds a whole number of chunks). Load i of
+    // a chunk brings rows vr + RPI*i (the RPI rows of one load share a block).
     auto issue_rows = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[VL]) {
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
             const int t = vr + RPI * i;
-            const int b = (RPI * i) / BS;
-            const int row = t - b * BS;
+            const int b = (RPI * i) / RPB;
+            const int row = t - b * RPB;
             buf[i] = buffer_load16(rs[b], (uint32_t)(row * row_bytes + vc * 16));
         }
     };
@@ -288,11 +298,18 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         float sv[4 * NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const int b = (16 * s) / BS;
+            // descriptor of tokens 16s + 4g .. 16s + 4g + 3 (uniform unless
+            // a descriptor covers fewer than 16 rows)
+            bool bok;
+            if constexpr (RPB >= 16) {
+                bok = ci.ok[(16 * s) / RPB];
+            } else {
+                bok = (__builtin_amdgcn_readfirstlane(ci.okm) >> ((16 * s + 4 * g) / RPB)) & 1u;
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int tok = cs + 16 * s + 4 * g + k;
-                const bool ok = ci.ok[b] && tok < end;
+                const bool ok = bok && tok < end;
                 sv[4 * s + k] = ok ? sc[s][k] * a.scale_log2 : -INFINITY;
             }
         }

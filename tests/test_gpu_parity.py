@@ -165,8 +165,10 @@ def _selector_batch(dtype, D, BS, lens, G=1, seed=5):
     V rows hold distinct non-zero integers (seq, token, dim)."""
     Hkv = 2
     Hq = Hkv * G
+    need = [-(-L // BS) for L in lens]
     w = _small("sel", num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=D, dtype=dtype,
-               block_size=BS, num_blocks=256, max_blocks_per_seq=64, lens="fixed:1")
+               block_size=BS, num_blocks=max(256, sum(need) + 16),
+               max_blocks_per_seq=max(64, max(need)), lens="fixed:1")
     b = W.make_batch(w, seed=seed, lens=lens)
     rng = np.random.default_rng(seed)
     enc = lambda x: W.encode(np.asarray(x, np.float32), dtype)
@@ -193,7 +195,9 @@ def _selector_batch(dtype, D, BS, lens, G=1, seed=5):
 
 
 @pytest.mark.parametrize("dtype,D,BS,G", [("f16", 128, 16, 1), ("bf16", 64, 32, 1),
-                                          ("bf16", 128, 16, 8), ("f16", 64, 16, 4)])
+                                          ("bf16", 128, 16, 8), ("f16", 64, 16, 4),
+                                          ("f16", 128, 8, 1), ("bf16", 64, 64, 1),
+                                          ("bf16", 128, 8, 4), ("f16", 128, 64, 8)])
 def test_selector_pins_block_table_indexing_bit_exactly(dtype, D, BS, G):
     lens = [1, 5, BS, BS + 3, 100, 257, 700]
     b, winners = _selector_batch(dtype, D, BS, lens, G)
@@ -486,6 +490,65 @@ def test_two_heads_per_workgroup_on_a_sparse_rectangle(fused):
     _assert_close(to_host_f64(out), ref, "f32", "sparse rectangle fused=%s" % fused)
 
 
+# ---- block sizes 8 and 64 -----------------------------------------------------
+# An 8-token block puts eight blocks in a 64-token chunk of the one-head
+# kernel and four in a 32-token chunk of the grouped kernel; a 64-token block
+# is one chunk of the first and two chunks of the second, each of which then
+# starts inside the block.
+
+BS_HEADS = [
+    # (num_heads, num_kv_heads, head_dim, dtype)
+    (8, 8, 128, "f16"),
+    (4, 4, 64, "bf16"),
+    (16, 4, 128, "bf16"),
+    (8, 1, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("BS", [8, 64])
+@pytest.mark.parametrize("heads", range(len(BS_HEADS)))
+@pytest.mark.parametrize("path", ["single", "split64", "split192", "fused128"])
+def test_block_sizes_8_and_64(BS, heads, path):
+    Hq, Hkv, D, dt = BS_HEADS[heads]
+    lens = [1, BS - 1, BS, BS + 1, 63, 64, 65, 200, 511, 700]
+    need = sum(-(-L // BS) for L in lens)
+    w = _small("bs%d" % BS, num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+               dtype=dt, block_size=BS, num_blocks=need + 40, max_blocks_per_seq=-(-704 // BS),
+               lens="fixed:1")
+    b = W.make_batch(w, seed=BS + 10 * heads, lens=lens, unallocated="nan")
+    split = path != "single"
+    P = int(path[5:]) if path.startswith("split") else (128 if path == "fused128" else None)
+    if P is not None and P % BS:
+        P = BS * (-(-P // BS))
+    db = DeviceBatch(b, out_dtype=None, split=split, partition_size=P,
+                     fused=path.startswith("fused"))
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, dt, "BS=%d heads=%s %s" % (BS, BS_HEADS[heads], path))
+
+
+@pytest.mark.parametrize("BS", [8, 64])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_block_sizes_8_and_64_shared_prefix(BS, Hq, Hkv):
+    P = 128
+    prefix = 256
+    suf = [1, 2, BS, BS + 1, 100, 129, 7]
+    w = _small("pfxbs%d" % BS, num_seqs=len(suf), num_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+               dtype="bf16", block_size=BS, num_blocks=(prefix + 256 * len(suf)) // BS,
+               max_blocks_per_seq=(prefix + 256) // BS, lens="fixed:1",
+               shared_prefix_tokens=prefix, partition_size=P)
+    b = W.make_batch(w, seed=90 + BS, lens=suf, unallocated="nan")
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=P, shared_prefix=True)
+    assert db.prefix_tokens == prefix
+    out = db.step()
+    torch.cuda.synchronize()
+    _, _, ref = _oracle_step(b)
+    _assert_close(to_host_f64(out), ref, "f32", "prefix BS=%d" % BS)
+
+
 # ---- copy-on-write block copy ---------------------------------------------
 
 @pytest.mark.parametrize("dtype,NB,BS,Hkv,D,N", [
@@ -493,6 +556,8 @@ def test_two_heads_per_workgroup_on_a_sparse_rectangle(fused):
     ("bf16", 100, 32, 1, 64, 37),
     ("f16", 50, 16, 3, 64, 11),    # 6 KiB blocks: one partial 16 KiB slice
     ("bf16", 300, 16, 40, 128, 120),  # 160 KiB blocks: ten slices
+    ("f16", 80, 8, 2, 64, 30),     # 2 KiB blocks
+    ("bf16", 40, 64, 8, 128, 15),  # 128 KiB blocks
 ])
 def test_copy_blocks_bit_exact(dtype, NB, BS, Hkv, D, N):
     rng = np.random.default_rng(NB + N)
