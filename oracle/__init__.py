@@ -21,4 +21,5 @@ from .paged_attention import (  # noqa: F401
     decode_split,
     copy_blocks,
     swap_blocks,
+    prefill,
 )

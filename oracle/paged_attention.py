@@ -15,6 +15,12 @@ Sources (cited by page title and section):
   append into the current block or a new one), §2.3 (the three kernel steps:
   walk the block table, score every cached token and weight V, write out),
   §6 (ignore unfilled slots of a block; accumulate in fp32 or better).
+* [P3] also §3.2 (prefix-cache hits are whole blocks: a block's hash
+  depends on its tokens only, matched in order) and §3.4 (on a hit the
+  request's block table points at the cached blocks, prefill runs from the
+  first missing position, new blocks are taken as it goes, and decoding then
+  continues on the blocks); §1.1 (each generated token attends to itself and
+  every earlier token).
 * [P4] "优化大模型推理：PagedAttention 如何实现 GPU 显存高效管理":
   "按需分配" (35 tokens at block size 16 -> 3 blocks, 13 idle slots),
   Figure 2 (logical 0,1,2 -> physical 7,1,12), "写时复制" (copy-on-write:
@@ -26,7 +32,10 @@ design notes): query head h reads kv head h // (Hq/Hkv); a context length of 0
 gives a zero output; block-table entries past ceil(L/BS) are never read;
 slots with a negative slot_mapping entry are skipped; a split partition p
 covers logical tokens [p·P, (p+1)·P) and partitions are combined with the
-textbook log-sum-exp rule.
+textbook log-sum-exp rule. Prefill: the new tokens' K/V are stored into
+their slots before attention, and new token t of a sequence whose context
+(cached plus new) is L tokens, S of them new, sits at position L - S + t and
+attends to positions 0 .. L - S + t, itself included.
 
 Array conventions: fp16 data arrive as numpy float16; bf16 data arrive as
 their raw uint16 bit patterns (numpy has no bfloat16); fp32 as float32.
@@ -296,4 +305,54 @@ def swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, 
         kd[dst] = np.asarray(src_key_cache)[src]
         vd[dst] = np.asarray(src_value_cache)[src]
     return kd, vd
+
+
+# ---------------------------------------------------------------------------
+# Prefill over cached prefix blocks ([P3] §3.4 flow, §3.2 block-level hits,
+# §1.1 each token attends to itself and all earlier tokens; [P1] §二 formula)
+# ---------------------------------------------------------------------------
+
+
+def prefill(query, key_cache, value_cache, block_tables, context_lens, query_start,
+            scale, kv_dtype):
+    """Causal attention of every sequence's new tokens over its paged context.
+
+    query [T, Hq, D]: the new tokens of all sequences, packed in sequence
+    order; sequence i owns rows query_start[i] .. query_start[i+1] - 1
+    (query_start has B + 1 ascending entries, the first 0, the last T).
+    context_lens[i] = L_i counts the cached tokens plus the S_i new ones,
+    whose K/V are already in the caches at positions L_i - S_i .. L_i - 1.
+    Row t of sequence i (position p = L_i - S_i + t) attends to the cache
+    positions 0..p. Returns float64 [T, Hq, D]; a row with no position to
+    attend (p < 0, a caller error) is zero.
+    """
+    q64 = upcast(query, kv_dtype)
+    T, Hq, D = q64.shape
+    Hkv = key_cache.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("query heads must be a multiple of kv heads")
+    group = Hq // Hkv
+    block_size = key_cache.shape[1]
+    qs = [int(x) for x in query_start]
+    if qs[0] != 0 or qs[-1] != T or any(b < a for a, b in zip(qs, qs[1:])):
+        raise ValueError("query_start must ascend from 0 to the number of query rows")
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for i in range(len(qs) - 1):
+        S = qs[i + 1] - qs[i]
+        L = int(context_lens[i])
+        if S == 0 or L <= 0:
+            continue
+        K = upcast(gather_sequence(key_cache, block_tables[i], L, block_size), kv_dtype)
+        V = upcast(gather_sequence(value_cache, block_tables[i], L, block_size), kv_dtype)
+        for t in range(S):
+            p = L - S + t  # the token's position in its sequence
+            if p < 0:
+                continue
+            for h in range(Hq):
+                g = h // group
+                s = scale * (K[: p + 1, g, :] @ q64[qs[i] + t, h])  # logits of 0..p
+                w = np.exp(s - s.max())
+                w = w / w.sum()
+                out[qs[i] + t, h] = w @ V[: p + 1, g, :]
+    return out
 

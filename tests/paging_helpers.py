@@ -27,3 +27,15 @@ def paginate(logical, block_size, num_blocks, rng, fill=0.0):
         padded[:L] = seq
         cache[ids] = padded.reshape(nb, block_size, Hkv, D)
     return cache, tables
+
+
+def paginate_kv(ks, vs, block_size, num_blocks, rng, fill=0.0):
+    """K and V sequences placed into blocks through the same tables."""
+    kc, tables = paginate(ks, block_size, num_blocks, rng, fill)
+    vc = np.full_like(kc, fill)
+    for i, v in enumerate(vs):
+        nb = -(-v.shape[0] // block_size)
+        padded = np.full((nb * block_size,) + v.shape[1:], fill, dtype=v.dtype)
+        padded[:v.shape[0]] = v
+        vc[tables[i, :nb]] = padded.reshape((nb, block_size) + v.shape[1:])
+    return kc, vc, tables

@@ -555,3 +555,172 @@ def test_planted_swap_mistake_is_caught():
     g0 = _gather2(kc, vc, t0, L, bs)
     g1 = _gather2(kc3, vc3, t1, L, bs)
     assert not np.array_equal(g0[1].view(np.uint16), g1[1].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# Prefill over cached prefix blocks (lqnn.cn/news/170268 §3.2, §3.4, §1.1)
+# ---------------------------------------------------------------------------
+
+from tests.paging_helpers import paginate_kv  # noqa: E402
+
+
+def _causal_sdpa(q, k, v, scale, group):
+    """torch's causal scaled_dot_product_attention in float64 on one unpaged
+    sequence whose every token is a query: q [L, Hq, D], k, v [L, Hkv, D]."""
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(),
+                                                         is_causal=True, scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(4, 4, 16), (8, 2, 4), (6, 1, 32)])
+def test_prefill_from_scratch_matches_library_causal_attention(hq, hkv, bs):
+    # no cached prefix: every token of the sequence is new, so prefill is
+    # plain causal self-attention on the unpaged sequence
+    rng = np.random.default_rng(31)
+    d = 16
+    lens = [1, 3, bs, bs + 1, 2 * bs + 5, 40]
+    ks, vs = _random_logical(rng, lens, hkv, d)
+    qs = [rng.standard_normal((L, hq, d)).astype(np.float16) for L in lens]
+    kc, vc, bt = paginate_kv(ks, vs, bs, 64, rng, fill=np.float16(np.nan))
+    start = np.concatenate([[0], np.cumsum(lens)])
+    scale = 1.0 / math.sqrt(d)
+    got = oracle.prefill(np.concatenate(qs), kc, vc, bt, np.array(lens), start, scale, "f16")
+    ref = np.concatenate([_causal_sdpa(q, k, v, scale, hq // hkv) for q, k, v in zip(qs, ks, vs)])
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_of_one_new_token_is_decode():
+    # a decode step is a prefill of one token: the new token attends to the
+    # whole context, itself included
+    rng = np.random.default_rng(32)
+    hq, hkv, d, bs = 8, 2, 16, 8
+    lens = [1, 7, 8, 9, 30]
+    ks, vs = _random_logical(rng, lens, hkv, d)
+    kc, vc, bt = paginate_kv(ks, vs, bs, 40, rng, fill=np.float16(np.nan))
+    q = rng.standard_normal((len(lens), hq, d)).astype(np.float16)
+    got = oracle.prefill(q, kc, vc, bt, np.array(lens), np.arange(len(lens) + 1), 0.3, "f16")
+    ref = oracle.decode(q, kc, vc, bt, np.array(lens), 0.3, "f16")
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def _prefix_hit_scenario(rng, bs=8, hq=4, hkv=2, d=16, cached_blocks=3, suffixes=(1, 5, 9, 20)):
+    """Several requests share a system prompt whose whole blocks are cached
+    (same physical blocks in every table, [P3] §3.4); each then prefills the
+    prompt's tail plus its own question."""
+    C = cached_blocks * bs
+    prompt_k = rng.standard_normal((C, hkv, d)).astype(np.float16)
+    prompt_v = rng.standard_normal((C, hkv, d)).astype(np.float16)
+    tails = [(rng.standard_normal((S, hkv, d)).astype(np.float16),
+              rng.standard_normal((S, hkv, d)).astype(np.float16)) for S in suffixes]
+    ks = [np.concatenate([prompt_k, tk]) for tk, _ in tails]
+    vs = [np.concatenate([prompt_v, tv]) for _, tv in tails]
+    qs = [rng.standard_normal((C + S, hq, d)).astype(np.float16) for S in suffixes]
+    NB = cached_blocks + sum(-(-S // bs) for S in suffixes) + 4
+    kc = np.full((NB, bs, hkv, d), np.float16(np.nan), dtype=np.float16)
+    vc = np.full_like(kc, np.float16(np.nan))
+    perm = rng.permutation(NB)
+    shared = perm[:cached_blocks]
+    kc[shared] = prompt_k.reshape(cached_blocks, bs, hkv, d)
+    vc[shared] = prompt_v.reshape(cached_blocks, bs, hkv, d)
+    MB = cached_blocks + max(-(-S // bs) for S in suffixes)
+    bt = np.full((len(suffixes), MB), -1, dtype=np.int32)
+    nxt = cached_blocks
+    for i, (S, (tk, tv)) in enumerate(zip(suffixes, tails)):
+        nb = -(-S // bs)
+        ids = perm[nxt:nxt + nb]
+        nxt += nb
+        bt[i, :cached_blocks] = shared
+        bt[i, cached_blocks:cached_blocks + nb] = ids
+        pk = np.full((nb * bs, hkv, d), np.float16(np.nan), dtype=np.float16)
+        pv = pk.copy()
+        pk[:S], pv[:S] = tk, tv
+        kc[ids] = pk.reshape(nb, bs, hkv, d)
+        vc[ids] = pv.reshape(nb, bs, hkv, d)
+    return C, suffixes, ks, vs, qs, kc, vc, bt
+
+
+def test_prefix_hit_gives_the_rows_of_a_full_prefill():
+    # reusing the cached blocks skips their recomputation and changes no
+    # result: the tail rows equal those of attention over the whole prompt
+    rng = np.random.default_rng(33)
+    C, suffixes, ks, vs, qs, kc, vc, bt = _prefix_hit_scenario(rng)
+    lens = np.array([C + S for S in suffixes])
+    tail_q = np.concatenate([q[C:] for q in qs])
+    start = np.concatenate([[0], np.cumsum(suffixes)])
+    got = oracle.prefill(tail_q, kc, vc, bt, lens, start, 0.25, "f16")
+    ref = np.concatenate([_causal_sdpa(q, k, v, 0.25, 2)[C:] for q, k, v in zip(qs, ks, vs)])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_first_token_of_a_fresh_sequence_returns_its_value_row():
+    # position 0 attends to itself only: softmax of one logit is 1
+    rng = np.random.default_rng(34)
+    ks, vs = _random_logical(rng, [5, 12], 2, 16)
+    kc, vc, bt = paginate_kv(ks, vs, 4, 16, rng, fill=np.float16(np.nan))
+    q = rng.standard_normal((17, 4, 16)).astype(np.float16)
+    got = oracle.prefill(q, kc, vc, bt, np.array([5, 12]), np.array([0, 5, 17]), 0.5, "f16")
+    for i, (first, v) in enumerate(zip([0, 5], vs)):
+        for h in range(4):
+            assert np.array_equal(got[first, h], v[0, h // 2].astype(np.float64))
+
+
+def test_prefill_rejects_inconsistent_query_starts():
+    kc = np.zeros((4, 4, 1, 8), np.float16)
+    q = np.zeros((3, 1, 8), np.float16)
+    bt = np.zeros((2, 1), np.int32)
+    with pytest.raises(ValueError):
+        oracle.prefill(q, kc, kc, bt, np.array([2, 1]), np.array([0, 2, 2]), 1.0, "f16")
+    with pytest.raises(ValueError):
+        oracle.prefill(q, kc, kc, bt, np.array([2, 1]), np.array([0, 2, 1]), 1.0, "f16")
+
+
+ORIG_PREFILL = oracle.prefill
+
+
+def _prefill_mutants():
+    def make(limit_of):
+        # the oracle's loop with a different choice of attended positions
+        def mutant(query, kc, vc, bt, lens, start, scale, dt):
+            q64 = oracle.upcast(query, dt)
+            out = np.zeros(q64.shape)
+            G = q64.shape[1] // kc.shape[2]
+            for i in range(len(start) - 1):
+                S, L = int(start[i + 1] - start[i]), int(lens[i])
+                if S == 0:
+                    continue
+                K = oracle.upcast(oracle.gather_sequence(kc, bt[i], L, kc.shape[1]), dt)
+                V = oracle.upcast(oracle.gather_sequence(vc, bt[i], L, kc.shape[1]), dt)
+                for t in range(S):
+                    n = limit_of(S, L, t)
+                    if n <= 0:
+                        continue
+                    for h in range(q64.shape[1]):
+                        s = scale * (K[:n, h // G] @ q64[start[i] + t, h])
+                        w = np.exp(s - s.max())
+                        out[start[i] + t, h] = (w / w.sum()) @ V[:n, h // G]
+            return out
+        return mutant
+
+    return {
+        "excludes_itself": make(lambda S, L, t: L - S + t),
+        "ignores_cached_offset": make(lambda S, L, t: t + 1),
+        "no_causal_mask": make(lambda S, L, t: L),
+    }
+
+
+@pytest.mark.parametrize("name", ["excludes_itself", "ignores_cached_offset", "no_causal_mask"])
+def test_planted_prefill_mistakes_are_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "prefill", _prefill_mutants()[name])
+    caught = 0
+    for pin in (lambda: test_prefill_from_scratch_matches_library_causal_attention(8, 2, 4),
+                test_prefill_of_one_new_token_is_decode,
+                test_prefix_hit_gives_the_rows_of_a_full_prefill):
+        try:
+            pin()
+        except (AssertionError, FloatingPointError):
+            caught += 1
+    assert caught > 0, "no pin caught planted prefill mistake %s" % name
