@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of MI355X
 LLC_BYTES = 256 << 20
 
 
@@ -54,10 +55,12 @@ def parse():
                     help="override the context-length recipe (e.g. fixed:1094); not the headline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--op", choices=["decode", "copy_blocks", "swap_blocks"], default="decode",
+    ap.add_argument("--op", choices=["decode", "copy_blocks", "swap_blocks", "prefill"],
+                    default="decode",
                     help="decode: the decode step (default); copy_blocks: the copy-on-write "
                          "block copy on the workload's cache shape; swap_blocks: blocks to "
-                         "pinned host memory and back")
+                         "pinned host memory and back; prefill: the prefill after a prefix-cache "
+                         "hit (workloads prefix_prefill, prefix_prefill_gqa, prefill_tiny)")
     ap.add_argument("--pairs", type=int, default=1024, help="copy_blocks: block pairs per launch")
     ap.add_argument("--ceiling-gib", type=float, default=4.0,
                     help="buffer size of the streaming-read ceiling measurement (0 skips it)")
@@ -199,6 +202,9 @@ def main():
         return
     if args.op == "swap_blocks":
         bench_swap_blocks(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
     import numpy as np
     import torch
@@ -412,6 +418,110 @@ def bench_copy_blocks(args):
                                "unit": "GB/s", "cores": 1, "kind": "oracle",
                                "sample": "%d runs of %d pairs (whole-cache copies included)"
                                          % (reps, sample)}
+    print(json.dumps(res), flush=True)
+
+
+def bench_prefill(args):
+    """The prefill step after a prefix-cache hit: the new tokens' K/V stored
+    by pa_reshape_and_cache, then pa_prefill over the cached prompt blocks
+    and the new tokens. The attention is a matrix-core contraction: its
+    roofline is the dense fp16/bf16 MFMA peak, by the exact causal flop
+    count."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_138_amd import lib as palib
+    from paged_kv_cache_138_amd import workloads as W
+    from paged_kv_cache_138_amd.pipeline import DevicePrefill
+
+    palib.load()
+    name = args.workload if args.workload in W.PREFILL_WORKLOADS else "prefix_prefill"
+    w = W.PREFILL_WORKLOADS[name]
+    t_gen = time.perf_counter()
+    batch = W.make_prefill_batch(w, seed=args.seed)
+    t_gen = time.perf_counter() - t_gen
+    flops = W.prefill_flops(batch)
+    out_dtype = torch.float32 if args.out_dtype == "f32" else None
+    unique_bytes, request_bytes = W.prefill_bytes(batch, "f32" if out_dtype is not None else None)
+    stream = torch.cuda.Stream()
+    K = args.steps
+    with torch.cuda.stream(stream):
+        db = DevicePrefill(batch, out_dtype=out_dtype)
+        for _ in range(max(args.warmup, 1)):
+            db.step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(K):
+            db.step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / K
+        ms = e0.elapsed_time(e1) / K
+        # the attention launch alone, back to back
+        e0.record()
+        for _ in range(K):
+            db.attend()
+        e1.record()
+        torch.cuda.synchronize()
+        attn_ms = e0.elapsed_time(e1) / K
+    tflops = flops / (ms * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    T = int(batch.query_start[-1])
+    res = {
+        "metric": "paged prefill attn after a prefix-cache hit: TFLOP/s (causal flops)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "op": "prefill",
+                   "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "cached_tokens": w.cached_tokens,
+                   "new_tokens": T, "max_query_len": batch.max_query_len,
+                   "out_dtype": args.out_dtype, "seed": args.seed},
+        "step_wall_ms": round(wall, 5),
+        "new_tokens_per_s": round(T / (ms * 1e-3), 1),
+        "attention_flops": flops,
+        "attention_bytes": {"unique": unique_bytes, "per_request": request_bytes,
+                            "unique_GB_per_s": round(unique_bytes / (attn_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "pa_prefill: %d back-to-back launches between HIP events, "
+                               "avg %.2f us" % (K, attn_ms * 1e3)},
+        "host_data_generation_s": round(t_gen, 2),
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(limits=1)
+        except Exception:  # pragma: no cover
+            limiter = None
+        kc, vc = oracle.reshape_and_cache(batch.new_key, batch.new_value, batch.key_cache,
+                                          batch.value_cache, batch.slot_mapping)
+        qs = batch.query_start
+        t0 = time.perf_counter()
+        done_flops = 0
+        n = 0
+        while time.perf_counter() - t0 < args.cpu_seconds and n < len(batch.context_lens):
+            rows = np.arange(qs[n], qs[n + 1])
+            sub = W.PrefillBatch(w, batch.query[rows], None, None, batch.block_tables[n:n + 1],
+                                 batch.context_lens[n:n + 1],
+                                 np.array([0, len(rows)], dtype=np.int32), None, None, None,
+                                 batch.scale, batch.shared_blocks)
+            oracle.prefill(sub.query, kc, vc, sub.block_tables, sub.context_lens,
+                           sub.query_start, batch.scale, batch.dtype)
+            done_flops += W.prefill_flops(sub)
+            n += 1
+        el = time.perf_counter() - t0
+        if limiter is not None:
+            limiter.unregister()
+        res["cpu_baseline"] = {"value": round(done_flops / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "oracle.prefill (fp64, one thread) of the first %d "
+                                         "requests, %.1f s" % (n, el)}
     print(json.dumps(res), flush=True)
 
 

@@ -201,6 +201,43 @@ pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill - causal attention of each sequence's new tokens over its paged
+ * context, the prefill that follows a prefix-cache hit (lqnn.cn/news/170268
+ * §3.4: hit blocks enter the request's block table as they are, prefill
+ * runs from the first missing position and takes new blocks as it goes;
+ * §3.2: hits are whole blocks; §1.1: a token attends to itself and every
+ * earlier token).
+ *
+ *   out          [num_tokens, num_heads, head_dim] of out_dtype: row r of
+ *                query's attention result.
+ *   query        [num_tokens, num_heads, head_dim] in kv_dtype: the new
+ *                tokens of every sequence, packed in sequence order.
+ *   query_start  int32 [num_seqs + 1], ascending, query_start[0] = 0 and
+ *                query_start[num_seqs] = num_tokens: sequence i's new tokens
+ *                are rows query_start[i] .. query_start[i+1] - 1, S_i of
+ *                them, with S_i <= max_query_len.
+ *   context_lens int32 [num_seqs]: L_i = cached tokens + S_i. New token t of
+ *                sequence i sits at position L_i - S_i + t, and its K/V must
+ *                already be in the caches there (pa_reshape_and_cache with
+ *                the new tokens' slots, before this call).
+ *   key_cache, value_cache, block_tables, the shape arguments, scale and
+ *                kv_dtype: as for pa_decode; num_heads / num_kv_heads <= 16.
+ * Row t of sequence i is softmax(scale · K q) · V over positions
+ * 0 .. L_i - S_i + t. Rows of a sequence with S_i > L_i whose position is
+ * negative, and rows of a sequence with L_i = 0, are zero. Rows past
+ * max_query_len of a sequence (a caller error) are not written; the device
+ * data query_start and context_lens are not checked. Nothing is allocated;
+ * one launch of one workgroup per (sequence, kv head, 16 / G new tokens),
+ * each over the whole context on the matrix cores.
+ */
+pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
+                     const void* value_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                     int num_tokens, int max_query_len, int num_heads, int num_kv_heads,
+                     int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                     float scale, pa_dtype kv_dtype, void* stream);
+
+/*
  * pa_decode_split_append - one decode step's scatter and attention in the
  * launches of pa_decode_split ("vLLM PagedAttention深度解析与工程实践" §二:
  * each step appends the new token's K/V, then attends over the sequence).

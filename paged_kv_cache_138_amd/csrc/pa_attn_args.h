@@ -37,6 +37,11 @@ struct AttnArgs {
     const int64_t* slot_mapping;
     int64_t new_key_stride;    // elements between consecutive tokens of new_key
     int64_t new_value_stride;  // and of new_value
+    // Prefill: sequence i's new tokens are rows query_start[i] ..
+    // query_start[i+1] - 1 of query and out, the last positions of its
+    // context; the grid has num_q_tiles tiles of new tokens per sequence.
+    const int32_t* query_start;
+    int num_q_tiles;
 };
 
 }  // namespace pa

@@ -37,6 +37,7 @@
 
 #include "pa_attn_args.h"
 #include "pa_device.h"
+#include "pa_kernels.h"
 
 namespace pa {
 
@@ -90,16 +91,22 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 #define PA_GQA_CHUNK 32
 #endif
 
-// PREFIX = false: a workgroup serves the G query heads of one (sequence, kv
-// head) over one partition of that sequence's context.
-// PREFIX = true (shared-prefix mode): every sequence's first prefix_tokens
-// tokens are the same physical blocks (block_tables row 0). A workgroup then
-// serves 16 / G sequences x G heads of one kv head over one partition of the
-// shared prefix, so each prefix block is read once per 16 query rows instead
-// of once per (sequence, kv head).
-template <class KV, class OUT, int D, int BS, int NW, bool PREFIX>
+// MODE kModeDecode: a workgroup serves the G query heads of one (sequence,
+// kv head) over one partition of that sequence's context.
+// MODE kModePrefix (shared-prefix decode): every sequence's first
+// prefix_tokens tokens are the same physical blocks (block_tables row 0). A
+// workgroup then serves 16 / G sequences x G heads of one kv head over one
+// partition of the shared prefix, so each prefix block is read once per 16
+// query rows instead of once per (sequence, kv head).
+// MODE kModePrefill: a workgroup serves 16 / G consecutive new tokens x G
+// heads of one (sequence, kv head) over the whole context, each row masked
+// to the positions up to its own (causal); the tile of new tokens is
+// blockIdx's second coordinate.
+template <class KV, class OUT, int D, int BS, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(AttnArgs a) {
+    constexpr bool PREFIX = MODE == kModePrefix;
+    constexpr bool PREFILL = MODE == kModePrefill;
     constexpr int CH = PA_GQA_CHUNK;    // tokens per chunk (32 or 64)
     constexpr int NS = CH / 16;         // 16-token sub-blocks of a chunk
     constexpr int NH = CH / 32;         // 32-token halves (one p·v contraction each)
@@ -146,7 +153,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // are adjacent in a cache row, so their reads run side by side.
     constexpr int LOG_NW = NW == 4 ? 2 : (NW == 2 ? 1 : 0);
     static_assert((1 << LOG_NW) == NW, "NW must be 1, 2 or 4");
-    const int hl = PREFIX ? 0 : a.heads_log2;
+    const int hl = (PREFIX || PREFILL) ? 0 : a.heads_log2;
     const int nwh = NW >> hl;                 // waves per kv head
     const int hslot = wave >> (LOG_NW - hl);  // kv head within the workgroup
     const int sub = wave & (nwh - 1);         // wave within the kv head
@@ -156,8 +163,10 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     const int kvh = kvh0 + hslot;
     bid /= ngroups;
     // rows of every product: row r is query head r_head of sequence r_seq
-    const int R = PREFIX ? 16 / G : 1;  // sequences per workgroup
+    // (of new token r_seq in prefill mode)
+    const int R = (PREFIX || PREFILL) ? 16 / G : 1;  // sequences (new tokens) per workgroup
     int seq0, part, Lsrc, nparts = 0;
+    int q0 = 0, nq = 0, pos0 = 0;  // prefill: first new token of the tile, tokens in it, its position
     const int32_t* bt;
     if constexpr (PREFIX) {
         const int ntiles = (a.num_seqs + R - 1) / R;
@@ -165,6 +174,20 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         part = bid / ntiles + a.part_begin;
         Lsrc = a.prefix_tokens;
         bt = a.block_tables;  // the shared prefix, as row 0 lists it
+    } else if constexpr (PREFILL) {
+        const int tile = bid % a.num_q_tiles;
+        const int sq = bid / a.num_q_tiles;
+        const int qb0 = a.query_start[sq];
+        const int S = a.query_start[sq + 1] - qb0;  // new tokens of the sequence
+        if (tile * R >= S) return;                  // uniform over the workgroup
+        seq0 = sq;
+        part = 0;
+        Lsrc = ctx_len(sq);
+        q0 = qb0 + tile * R;
+        nq = min(R, S - tile * R);
+        pos0 = Lsrc - S + tile * R;  // new token t of the sequence sits at L - S + t
+        nparts = 1;
+        bt = a.block_tables + (size_t)sq * a.max_blocks_per_seq;
     } else {
         seq0 = bid % a.num_seqs;
         part = bid / a.num_seqs + a.part_begin;
@@ -184,7 +207,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // (A sequence with L = 0 has no token to attend; its row is still
     // stored, by the workgroups of its partition 0, as the scatter would.)
     bool has_new = false, store_new = false;
-    if constexpr (!PREFIX) {
+    if constexpr (MODE == kModeDecode) {
         if (a.new_key && part == max(nparts, 1) - 1) {
             const int64_t slot = a.slot_mapping[seq0];
             const bool slot_ok = slot >= 0 && slot < (int64_t)a.num_blocks * BS;
@@ -198,11 +221,20 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             }
         }
     }
-    const int end = has_new ? Lsrc - 1 : min(start + P, Lsrc);
+    // prefill: the tile's last row attends up to its own position
+    const int end = PREFILL ? max(min(pos0 + nq, Lsrc), 0)
+                            : (has_new ? Lsrc - 1 : min(start + P, Lsrc));
     const int nb = (Lsrc + BS - 1) / BS;
-    auto row_seq = [&](int r) { return seq0 + r / G; };
+    // row_seq is the query/output row's leading index: the sequence, or in
+    // prefill mode the new token's row of query and out
+    auto row_seq = [&](int r) { return PREFILL ? q0 + r / G : seq0 + r / G; };
     auto row_head = [&](int r) { return kvh * G + r % G; };
-    auto row_ok = [&](int r) { return r < R * G && row_seq(r) < a.num_seqs; };
+    auto row_ok = [&](int r) {
+        return r < R * G && (PREFILL ? r / G < nq : row_seq(r) < a.num_seqs);
+    };
+    // prefill: the last position row n (lane column n) attends to; -1 masks
+    // every position of a padding row
+    const int lim = PREFILL ? (row_ok(n) ? pos0 + n / G : -1) : 0;
 
     const size_t row_bytes = (size_t)Hkv * D * 2;
     const size_t block_bytes = row_bytes * BS;
@@ -309,7 +341,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int tok = cs + 16 * s + 4 * g + k;
-                const bool ok = bok && tok < end;
+                const bool ok = bok && tok < end && (!PREFILL || tok <= lim);
                 sv[4 * s + k] = ok ? sc[s][k] * a.scale_log2 : -INFINITY;
             }
         }
@@ -459,7 +491,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         }
         const float res = tot > 0.f ? o / tot : 0.f;
         const size_t sh = (size_t)row_seq(h) * Hq + (kvh0 + hs) * G + h % G;
-        const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : nparts;
+        const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : (PREFILL ? 1 : nparts);
         if (np <= 1) {
             OUT::store(a.out, sh * D + d, res);
         } else {
@@ -476,6 +508,43 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         *(u32x4*)((uint16_t*)a.key_cache + dst) = *(const u32x4*)&sm_new[wave][0][vc * 8];
         *(u32x4*)((uint16_t*)a.value_cache + dst) = *(const u32x4*)&sm_new[wave][1][vc * 8];
     }
+}
+
+// Instances of one mode: 1 <= num_heads / num_kv_heads <= 16 (2 <= ... for
+// plain decode, where a single head takes the one-head kernel).
+template <class KV, class OUT, int D, int MODE>
+attn_fn pick_gqa_bs(int bs) {
+    switch (bs) {
+        case 8: return attn_gqa_kernel<KV, OUT, D, 8, kGqaWaves, MODE>;
+        case 16: return attn_gqa_kernel<KV, OUT, D, 16, kGqaWaves, MODE>;
+        case 32: return attn_gqa_kernel<KV, OUT, D, 32, kGqaWaves, MODE>;
+        case 64: return attn_gqa_kernel<KV, OUT, D, 64, kGqaWaves, MODE>;
+    }
+    return nullptr;
+}
+
+template <class KV, class OUT, int MODE>
+attn_fn pick_gqa_d(int d, int bs) {
+    switch (d) {
+        case 64: return pick_gqa_bs<KV, OUT, 64, MODE>(bs);
+        case 128: return pick_gqa_bs<KV, OUT, 128, MODE>(bs);
+    }
+    return nullptr;
+}
+
+template <class KV, int MODE>
+attn_fn pick_gqa_out(pa_dtype out, pa_dtype kv, int d, int bs) {
+    if (out == PA_F32) return pick_gqa_d<KV, OutF32, MODE>(d, bs);
+    if (out != kv) return nullptr;
+    if (kv == PA_F16) return pick_gqa_d<KV, OutF16, MODE>(d, bs);
+    return pick_gqa_d<KV, OutBF16, MODE>(d, bs);
+}
+
+template <int MODE>
+attn_fn pick_gqa_mode(pa_dtype kv, pa_dtype out, int d, int bs) {
+    if (kv == PA_F16) return pick_gqa_out<KvF16, MODE>(out, kv, d, bs);
+    if (kv == PA_BF16) return pick_gqa_out<KvBF16, MODE>(out, kv, d, bs);
+    return nullptr;
 }
 
 }  // namespace pa

@@ -1,0 +1,11 @@
+// Instances of the matrix-core kernel for grouped-query decode.
+#include "pa_attn_gqa.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+attn_fn pick_gqa(pa_dtype kv, pa_dtype out, int d, int bs) {
+    return pick_gqa_mode<kModeDecode>(kv, out, d, bs);
+}
+
+}  // namespace pa

@@ -1,0 +1,36 @@
+// The attention kernels' instances, as the host code reaches them. Each
+// picker returns the kernel instance for an element type, output type,
+// head_dim and block size, or null when there is none; each is defined in
+// its own pa_inst_*.hip file so that the instances compile in parallel.
+#pragma once
+
+#include "pa.h"
+#include "pa_attn_args.h"
+
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
+
+namespace pa {
+
+constexpr int kWaves = PA_WAVES;         // wavefronts per workgroup, one-head kernel
+constexpr int kGqaWaves = PA_GQA_WAVES;  // and matrix-core kernel
+
+// what a matrix-core kernel instance computes
+enum GqaMode {
+    kModeDecode = 0,   // decode: one sequence's query heads of a kv head per workgroup
+    kModePrefix = 1,   // decode over a shared prefix: several sequences per workgroup
+    kModePrefill = 2,  // prefill: several new tokens of one sequence per workgroup
+};
+
+typedef void (*attn_fn)(AttnArgs);
+
+attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs);            // pa_inst_mha.hip
+attn_fn pick_gqa(pa_dtype kv, pa_dtype out, int d, int bs);             // pa_inst_gqa.hip
+attn_fn pick_prefix_kernel(pa_dtype kv, pa_dtype out, int d, int bs);   // pa_inst_prefix.hip
+attn_fn pick_prefill_kernel(pa_dtype kv, pa_dtype out, int d, int bs);  // pa_inst_prefill.hip
+
+}  // namespace pa

@@ -51,6 +51,9 @@ def load():
     lib.pa_reshape_and_cache.restype = i32
     dec = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32]
     lib.pa_decode.argtypes = dec + [vp]
+    lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                               i32, i32, f32, i32, vp]
+    lib.pa_prefill.restype = i32
     lib.pa_decode.restype = i32
     lib.pa_decode_split.argtypes = dec + [i32, vp, sz, vp]
     lib.pa_decode_split.restype = i32
@@ -218,6 +221,40 @@ def decode(query, key_cache, value_cache, block_tables, context_lens, scale, out
                           _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, BS, MB, NB,
                           float(scale), _DT[key_cache.dtype], _stream(query))
     _check(st, "pa_decode")
+    return out
+
+
+def prefill(query, key_cache, value_cache, block_tables, context_lens, query_start, scale,
+            max_query_len, out=None, out_dtype=None):
+    """Causal attention of the new tokens query [T, Hq, D] (sequence i owns
+    rows query_start[i] .. query_start[i+1] - 1, the last positions of its
+    context_lens[i] tokens, whose K/V are already cached) over each
+    sequence's paged context; returns out [T, Hq, D]. max_query_len bounds
+    every sequence's new-token count; see pa_prefill."""
+    _on_gpu(query, key_cache, value_cache, block_tables, context_lens, query_start)
+    _kv_checks(query, key_cache, value_cache)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.is_contiguous(),
+          "block_tables must be a contiguous int32 [num_seqs, max_blocks_per_seq] tensor")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1 and context_lens.is_contiguous(),
+          "context_lens must be a contiguous int32 vector")
+    B = context_lens.shape[0]
+    _need(query_start.dtype == torch.int32 and query_start.dim() == 1 and query_start.is_contiguous()
+          and query_start.shape[0] == B + 1, "query_start must be a contiguous int32 [num_seqs + 1] vector")
+    _need(block_tables.shape[0] == B, "batch sizes differ")
+    T, Hq, D = query.shape
+    NB, BS, Hkv, D2 = key_cache.shape
+    _need(D == D2, "head_dim of query and caches differ")
+    if out is None:
+        od = out_dtype if out_dtype is not None else query.dtype
+        out = torch.empty((T, Hq, D), dtype=od, device=query.device)
+    _on_gpu(query, out)
+    _need(out.shape == (T, Hq, D) and out.is_contiguous(), "out must be a contiguous [T, Hq, D] tensor")
+    _need(out.dtype in _DT, "unsupported out dtype")
+    st = load().pa_prefill(_ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                           _ptr(block_tables), _ptr(context_lens), _ptr(query_start), B, T,
+                           int(max_query_len), Hq, Hkv, D, BS, block_tables.shape[1], NB,
+                           float(scale), _DT[key_cache.dtype], _stream(query))
+    _check(st, "pa_prefill")
     return out
 
 

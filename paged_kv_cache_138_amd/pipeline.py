@@ -166,3 +166,41 @@ class RotatedBatch(DeviceBatch):
         self.slot_mapping = torch.where(sm >= 0, remap[blk] * BS + sm.clamp(min=0) % BS, sm)
         self.out = torch.empty_like(src.out)
         self.workspace = None if src.workspace is None else torch.empty_like(src.workspace)
+
+
+class DevicePrefill:
+    """GPU copies of a workloads.PrefillBatch. A step stores the new tokens'
+    K/V into their slots (pa_reshape_and_cache), then runs pa_prefill: the
+    new tokens attend over the cached prompt blocks and themselves, causally
+    (lqnn.cn/news/170268 §3.4: prefill from the first missing position on
+    top of the hit blocks)."""
+
+    def __init__(self, batch, device="cuda", out_dtype=None):
+        dt = batch.workload.dtype
+        self.batch = batch
+        self.query = to_device_tensor(batch.query, dt, device)
+        self.key_cache = to_device_tensor(batch.key_cache, dt, device)
+        self.value_cache = to_device_tensor(batch.value_cache, dt, device)
+        self.new_key = to_device_tensor(batch.new_key, dt, device)
+        self.new_value = to_device_tensor(batch.new_value, dt, device)
+        self.block_tables = torch.from_numpy(batch.block_tables).to(device)
+        self.context_lens = torch.from_numpy(batch.context_lens).to(device)
+        self.query_start = torch.from_numpy(batch.query_start).to(device)
+        self.slot_mapping = torch.from_numpy(batch.slot_mapping).to(device)
+        self.scale = batch.scale
+        self.max_query_len = batch.max_query_len
+        od = out_dtype if out_dtype is not None else self.query.dtype
+        self.out = torch.empty(tuple(self.query.shape), dtype=od, device=device)
+
+    def write_cache(self):
+        palib.reshape_and_cache(self.new_key, self.new_value, self.key_cache, self.value_cache,
+                                self.slot_mapping)
+
+    def attend(self):
+        return palib.prefill(self.query, self.key_cache, self.value_cache, self.block_tables,
+                             self.context_lens, self.query_start, self.scale, self.max_query_len,
+                             out=self.out)
+
+    def step(self):
+        self.write_cache()
+        return self.attend()

@@ -439,6 +439,162 @@ def _grow(mgr, seq_id):
     return b
 
 
+# ---------------------------------------------------------------------------
+# Prefill after a prefix-cache hit (lqnn.cn/news/170268 §3.4, §4.3)
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    cached_tokens: int    # whole blocks of a shared prompt found in the prefix cache
+    new_lens: str         # new tokens per request, a draw_context_lens recipe
+    description: str = ""
+
+
+PREFILL_WORKLOADS = {
+    "prefill_tiny": PrefillWorkload(
+        "prefill_tiny", 4, 8, 8, 64, "f16", 16, 64, 12, 64, "uniform:1:64",
+        description="4 requests share 64 cached prompt tokens, then 1..64 new tokens each; "
+                    "8 MHA heads, head_dim 64, fp16, block 16"),
+    "prefix_prefill": PrefillWorkload(
+        "prefix_prefill", 100, 32, 32, 128, "f16", 16, 2048, 128, 1488, "uniform:16:80",
+        description="100 requests share a ~1500-token system prompt whose 93 whole blocks "
+                    "(1488 tokens) hit the prefix cache; each prefills the prompt's tail and "
+                    "its question, 16..80 new tokens; 32 heads, head_dim 128, fp16, block 16, "
+                    "2048-block shuffled free list"),
+    "prefix_prefill_gqa": PrefillWorkload(
+        "prefix_prefill_gqa", 100, 28, 4, 128, "bf16", 16, 2048, 128, 1488, "uniform:16:80",
+        description="the same requests on a 28-query / 4-kv-head model, head_dim 128, bf16, "
+                    "block 16"),
+}
+
+PREFILL_ORDER = ["prefill_tiny", "prefix_prefill", "prefix_prefill_gqa"]
+
+
+@dataclass
+class PrefillBatch:
+    workload: PrefillWorkload
+    query: np.ndarray          # [T, Hq, D], the new tokens of every request in order
+    key_cache: np.ndarray      # [NB, BS, Hkv, D]: cached prompt blocks; new slots poisoned
+    value_cache: np.ndarray
+    block_tables: np.ndarray   # int32 [B, MB]
+    context_lens: np.ndarray   # int32 [B]: cached + new tokens
+    query_start: np.ndarray    # int32 [B + 1]
+    new_key: np.ndarray        # [T, Hkv, D], K/V of the new tokens, stored by the scatter
+    new_value: np.ndarray
+    slot_mapping: np.ndarray   # int64 [T]
+    scale: float
+    shared_blocks: np.ndarray  # the cached prompt's blocks, in every table
+
+    @property
+    def dtype(self):
+        return self.workload.dtype
+
+    @property
+    def max_query_len(self):
+        return int(np.diff(self.query_start).max(initial=0))
+
+
+def make_prefill_batch(workload, seed=0, lens=None, unallocated="nan"):
+    """Seeded prefill batch: every request's table starts with the cached
+    prompt's blocks (the same physical blocks, shared), then the blocks its
+    new tokens need, taken from a shuffled free list. The new tokens' slots
+    hold NaN until the scatter stores their K/V. lens overrides the drawn
+    new-token counts."""
+    w = workload
+    rng = np.random.default_rng(seed)
+    BS, B = w.block_size, w.num_seqs
+    if w.cached_tokens % BS:
+        raise ValueError("cached prompt tokens must be whole blocks")
+    S = (draw_context_lens(rng, w.new_lens, B) if lens is None
+         else np.asarray(lens, dtype=np.int64))
+    if len(S) != B:
+        raise ValueError("expected %d lengths" % B)
+    ctx = w.cached_tokens + S
+    if ctx.max(initial=0) > w.max_blocks_per_seq * BS:
+        raise ValueError("context longer than max_blocks_per_seq * block_size")
+    mgr = BlockManager(rng.permutation(w.num_blocks), BS)
+    shared = []
+    if w.cached_tokens:
+        mgr.allocate("prompt", w.cached_tokens)
+        shared = list(mgr.allocated["prompt"])
+    bt = np.full((B, w.max_blocks_per_seq), -1, dtype=np.int32)
+    for i in range(B):
+        if shared:
+            mgr.share(i, shared)
+        mgr.allocate(i, int(ctx[i]))
+        blocks = mgr.allocated.get(i, [])
+        bt[i, :len(blocks)] = blocks
+    if shared:
+        mgr.free("prompt")
+    qs = np.concatenate([[0], np.cumsum(S)]).astype(np.int32)
+    T = int(qs[-1])
+    slots = np.empty(T, dtype=np.int64)
+    for i in range(B):
+        for t in range(int(S[i])):
+            p = w.cached_tokens + t
+            slots[qs[i] + t] = int(bt[i, p // BS]) * BS + p % BS
+    D, Hq, Hkv = w.head_dim, w.num_heads, w.num_kv_heads
+    pool = (w.num_blocks, BS, Hkv, D)
+    fill = nan_bits(w.dtype) if unallocated == "nan" else np.uint16(0)
+    key_cache = np.full(pool, fill, dtype=np.uint16)
+    value_cache = np.full(pool, fill, dtype=np.uint16)
+    if shared:
+        ids = np.asarray(shared, dtype=np.int64)
+        _fill_blocks(seed, STREAM_K, key_cache, ids, w.dtype)
+        _fill_blocks(seed, STREAM_V, value_cache, ids, w.dtype)
+    # every slot of the new tokens' blocks is NaN until written
+    for i in range(B):
+        for j in range(w.cached_tokens // BS, -(-int(ctx[i]) // BS)):
+            key_cache[bt[i, j]] = nan_bits(w.dtype)
+            value_cache[bt[i, j]] = nan_bits(w.dtype)
+    q = _bits(encode(_normal(seed, STREAM_Q, 0, (T, Hq, D)), w.dtype))
+    nk = _bits(encode(_normal(seed, STREAM_NEW_K, 0, (T, Hkv, D)), w.dtype))
+    nv = _bits(encode(_normal(seed, STREAM_NEW_V, 0, (T, Hkv, D)), w.dtype))
+    edt = element_numpy_dtype(w.dtype)
+    q, key_cache, value_cache, nk, nv = (a.view(edt) for a in (q, key_cache, value_cache, nk, nv))
+    return PrefillBatch(w, q, key_cache, value_cache, bt, ctx.astype(np.int32), qs, nk, nv, slots,
+                        1.0 / math.sqrt(D), np.asarray(shared, dtype=np.int64))
+
+
+def prefill_flops(batch):
+    """Algorithmic flops of the attention of a prefill batch: new token t of
+    request i attends to L_i - S_i + t + 1 positions, each costing a q·k and
+    a p·v multiply-add per head_dim element and query head (4 flops)."""
+    w = batch.workload
+    n = 0
+    for i in range(len(batch.context_lens)):
+        S = int(batch.query_start[i + 1] - batch.query_start[i])
+        L = int(batch.context_lens[i])
+        n += sum(max(L - S + t + 1, 0) for t in range(S))
+    return 4 * n * w.num_heads * w.head_dim
+
+
+def prefill_bytes(batch, out_dtype=None):
+    """Algorithmic HBM bytes of the attention: each request's K/V rows once
+    per kv head (a shared prompt block once for the whole batch), plus q and
+    the output. Returns (unique, per_request)."""
+    w = batch.workload
+    e = element_bytes(w.dtype)
+    eo = element_bytes(out_dtype or w.dtype)
+    per_tok = 2 * w.num_kv_heads * w.head_dim * e
+    T = int(batch.query_start[-1])
+    qo = T * w.num_heads * w.head_dim * (e + eo)
+    L = batch.context_lens.astype(np.int64)
+    per_request = int(L.sum()) * per_tok + qo
+    unique = (int(L.sum()) - (len(L) - 1) * w.cached_tokens) * per_tok + qo if len(L) else qo
+    return unique, per_request
+
+
 def custom_workload(name="custom", **kw):
     base = dict(num_seqs=2, num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16",
                 block_size=16, num_blocks=64, max_blocks_per_seq=8,

@@ -142,3 +142,27 @@ def test_swap_blocks_rejects_bad_arguments(lib):
     # any launch
     assert lib.pa_swap_blocks(*a, 4, 8, 128, 16, 0, None) == 4
     assert lib.pa_swap_blocks(*a, 0, 8, 128, 16, 0, None) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(out=1 << 12, out_dtype=2, query=1 << 12, kc=1 << 12, vc=1 << 12, bt=1 << 12, cl=1 << 12,
+             qs=1 << 12, B=2, T=5, maxq=4, Hq=8, Hkv=8, D=128, BS=16, MB=8, NB=64, scale=0.1, kvdt=0)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["out_dtype"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"],
+                          a["qs"], a["B"], a["T"], a["maxq"], a["Hq"], a["Hkv"], a["D"], a["BS"],
+                          a["MB"], a["NB"], a["scale"], a["kvdt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=34, Hkv=2), 4), (dict(D=96), 4), (dict(T=-1), 2), (dict(maxq=-2), 2),
+    (dict(maxq=8 * 16 + 1), 2), (dict(qs=None), 1), (dict(query=None), 1), (dict(kvdt=2), 3),
+    (dict(kc=(1 << 12) + 2), 7),
+])
+def test_prefill_rejects_bad_arguments_without_launching(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_prefill_without_new_tokens_is_a_no_op(lib):
+    assert _prefill(lib, T=0, maxq=0, qs=None) == 0
+    assert _prefill(lib, B=0, T=0, maxq=0, qs=None) == 0
