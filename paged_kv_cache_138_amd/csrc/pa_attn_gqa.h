@@ -63,6 +63,17 @@ struct Mma<KvBF16> {
         *back = __uint_as_float(b << 16);
         return b;
     }
+    // (x0, x1) as packed hi halves, and what is left of each, packed
+    static __device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi,
+                                                  uint32_t* lo) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, b2));
+        const float r0 = x0 - __uint_as_float(h << 16);
+        const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
+        *hi = h;
+        *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, b2));
+    }
 };
 
 template <>
@@ -75,6 +86,15 @@ struct Mma<KvF16> {
         const _Float16 h = (_Float16)x;
         *back = (float)h;
         return (uint32_t)__builtin_bit_cast(uint16_t, h);
+    }
+    static __device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi,
+                                                  uint32_t* lo) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const h2 h = __builtin_convertvector(f2{x0, x1}, h2);
+        const f2 r = f2{x0, x1} - __builtin_convertvector(h, f2);
+        *hi = __builtin_bit_cast(uint32_t, h);
+        *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, h2));
     }
 };
 
@@ -98,15 +118,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // workgroup then serves 16 / G sequences x G heads of one kv head over one
 // partition of the shared prefix, so each prefix block is read once per 16
 // query rows instead of once per (sequence, kv head).
-// MODE kModePrefill: a workgroup serves 16 / G consecutive new tokens x G
-// heads of one (sequence, kv head) over the whole context, each row masked
-// to the positions up to its own (causal); the tile of new tokens is
-// blockIdx's second coordinate.
 template <class KV, class OUT, int D, int BS, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(AttnArgs a) {
     constexpr bool PREFIX = MODE == kModePrefix;
-    constexpr bool PREFILL = MODE == kModePrefill;
+    static_assert(MODE == kModeDecode || MODE == kModePrefix, "decode modes");
     constexpr int CH = PA_GQA_CHUNK;    // tokens per chunk (32 or 64)
     constexpr int NS = CH / 16;         // 16-token sub-blocks of a chunk
     constexpr int NH = CH / 32;         // 32-token halves (one p·v contraction each)
@@ -153,7 +169,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // are adjacent in a cache row, so their reads run side by side.
     constexpr int LOG_NW = NW == 4 ? 2 : (NW == 2 ? 1 : 0);
     static_assert((1 << LOG_NW) == NW, "NW must be 1, 2 or 4");
-    const int hl = (PREFIX || PREFILL) ? 0 : a.heads_log2;
+    const int hl = PREFIX ? 0 : a.heads_log2;
     const int nwh = NW >> hl;                 // waves per kv head
     const int hslot = wave >> (LOG_NW - hl);  // kv head within the workgroup
     const int sub = wave & (nwh - 1);         // wave within the kv head
@@ -163,10 +179,8 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     const int kvh = kvh0 + hslot;
     bid /= ngroups;
     // rows of every product: row r is query head r_head of sequence r_seq
-    // (of new token r_seq in prefill mode)
-    const int R = (PREFIX || PREFILL) ? 16 / G : 1;  // sequences (new tokens) per workgroup
+    const int R = PREFIX ? 16 / G : 1;  // sequences per workgroup
     int seq0, part, Lsrc, nparts = 0;
-    int q0 = 0, nq = 0, pos0 = 0;  // prefill: first new token of the tile, tokens in it, its position
     const int32_t* bt;
     if constexpr (PREFIX) {
         const int ntiles = (a.num_seqs + R - 1) / R;
@@ -174,20 +188,6 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         part = bid / ntiles + a.part_begin;
         Lsrc = a.prefix_tokens;
         bt = a.block_tables;  // the shared prefix, as row 0 lists it
-    } else if constexpr (PREFILL) {
-        const int tile = bid % a.num_q_tiles;
-        const int sq = bid / a.num_q_tiles;
-        const int qb0 = a.query_start[sq];
-        const int S = a.query_start[sq + 1] - qb0;  // new tokens of the sequence
-        if (tile * R >= S) return;                  // uniform over the workgroup
-        seq0 = sq;
-        part = 0;
-        Lsrc = ctx_len(sq);
-        q0 = qb0 + tile * R;
-        nq = min(R, S - tile * R);
-        pos0 = Lsrc - S + tile * R;  // new token t of the sequence sits at L - S + t
-        nparts = 1;
-        bt = a.block_tables + (size_t)sq * a.max_blocks_per_seq;
     } else {
         seq0 = bid % a.num_seqs;
         part = bid / a.num_seqs + a.part_begin;
@@ -221,20 +221,11 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             }
         }
     }
-    // prefill: the tile's last row attends up to its own position
-    const int end = PREFILL ? max(min(pos0 + nq, Lsrc), 0)
-                            : (has_new ? Lsrc - 1 : min(start + P, Lsrc));
+    const int end = has_new ? Lsrc - 1 : min(start + P, Lsrc);
     const int nb = (Lsrc + BS - 1) / BS;
-    // row_seq is the query/output row's leading index: the sequence, or in
-    // prefill mode the new token's row of query and out
-    auto row_seq = [&](int r) { return PREFILL ? q0 + r / G : seq0 + r / G; };
+    auto row_seq = [&](int r) { return seq0 + r / G; };
     auto row_head = [&](int r) { return kvh * G + r % G; };
-    auto row_ok = [&](int r) {
-        return r < R * G && (PREFILL ? r / G < nq : row_seq(r) < a.num_seqs);
-    };
-    // prefill: the last position row n (lane column n) attends to; -1 masks
-    // every position of a padding row
-    const int lim = PREFILL ? (row_ok(n) ? pos0 + n / G : -1) : 0;
+    auto row_ok = [&](int r) { return r < R * G && row_seq(r) < a.num_seqs; };
 
     const size_t row_bytes = (size_t)Hkv * D * 2;
     const size_t block_bytes = row_bytes * BS;
@@ -341,7 +332,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int tok = cs + 16 * s + 4 * g + k;
-                const bool ok = bok && tok < end && (!PREFILL || tok <= lim);
+                const bool ok = bok && tok < end;
                 sv[4 * s + k] = ok ? sc[s][k] * a.scale_log2 : -INFINITY;
             }
         }
@@ -491,7 +482,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         }
         const float res = tot > 0.f ? o / tot : 0.f;
         const size_t sh = (size_t)row_seq(h) * Hq + (kvh0 + hs) * G + h % G;
-        const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : (PREFILL ? 1 : nparts);
+        const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : nparts;
         if (np <= 1) {
             OUT::store(a.out, sh * D + d, res);
         } else {

@@ -1,0 +1,338 @@
+// Prefill over cached prefix blocks on the matrix cores (gfx950).
+//
+// What is computed (lqnn.cn/news/170268 §3.4 and §1.1): new token t of
+// sequence i, at position L_i - S_i + t, attends to the positions 0 ..
+// L_i - S_i + t of its paged context: the cached prompt blocks its table
+// starts with, then the new tokens themselves (already stored in the cache).
+//
+// Work decomposition: one workgroup = one (sequence, kv head, tile of
+// NW * TR * 16/G consecutive new tokens). Wave w owns TR tiles of 16 rows,
+// each 16/G new tokens x the G query heads of the kv head, and keeps their
+// online softmax and output in registers for the whole context; there is
+// no cross-wave merge. (The instances built use TR = 1: two tiles per wave
+// halve the LDS reads per product but measured slower, with fewer waves
+// resident.)
+// The workgroup walks the context in 32-token chunks, and all its waves
+// read each chunk's K and V rows from LDS, so a row of the cache comes from
+// memory once per NW * 16 rows rather than once per 16 (the 16-row
+// grouped-query kernel's reuse). Chunks are double-buffered in LDS: the
+// global loads of chunk c + 1 are in flight while chunk c is computed, and
+// one barrier per chunk orders the buffer swap.
+//
+// Per chunk and tile, the products are those of the grouped-query decode
+// kernel: Sᵀ[16 tokens x 16 rows] = K · Qᵀ on v_mfma_f32_16x16x32, the
+// online softmax lane-local per row (lane (g, n) holds row n; the max and
+// sum over a row's four lanes use the gfx950 lane swaps), and
+// Oᵀ[16 d x 16 rows] += Vᵀ · Pᵀ with Vᵀ read by ds_read_b64_tr_b16 and P
+// split into hi + lo 16-bit halves. Each row is masked to positions up to
+// its own; a wave whose rows all sit before a chunk skips its products (it
+// still loads and waits at the barrier).
+#pragma once
+
+#include "pa_attn_gqa.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+// Max and sum over the four lanes n, n + 16, n + 32, n + 48 (the row
+// groups of an MFMA output) with the gfx950 lane swaps, on the VALU.
+__device__ __forceinline__ float max_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <class KV, class OUT, int D, int BS, int NW, int TR>
+__global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
+    constexpr int CH = 32;         // tokens per chunk
+    constexpr int NS = CH / 16;    // 16-token sub-blocks of a chunk
+    constexpr int NJ = D / 32;     // q·k products per 16-token sub-block
+    constexpr int NT = D / 16;     // 16-wide output tiles of head_dim
+    constexpr int LPR = D / 8;     // lanes per row of a 16-byte load
+    constexpr int RPW = 64 / LPR;  // rows one wave loads per instruction (4 or 8)
+    constexpr int RPL = NW * RPW;  // rows the workgroup loads per instruction
+    constexpr int LPC = CH / RPL;  // load instructions per chunk, of K and of V
+    constexpr int ROWB = D * 2 + 16;  // LDS bytes per row (padding spreads banks)
+    constexpr int TILE = CH * ROWB;
+    constexpr int BSC = BS < CH ? BS : CH;  // tokens of a chunk in one block
+    constexpr uint32_t kBlockBits = BSC == 32 ? 0xffffffffu : (1u << BSC) - 1u;
+    static_assert(LPC >= 1 && LPC * RPL == CH, "the workgroup's loads tile the chunk");
+    static_assert(BS % RPW == 0, "the rows of one wave's load share a block");
+    static_assert(NS == 2, "one p·v contraction (32 tokens) per chunk");
+
+    __shared__ __attribute__((aligned(16))) char sm_k[2][TILE];
+    __shared__ __attribute__((aligned(16))) char sm_v[2][TILE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;      // lane group
+    const int n = lane & 15;      // row of a tile (column of every product)
+    const int lr = lane / LPR;    // row of a wave's load
+    const int lc = lane % LPR;    // 16-byte slice of that row
+
+    const int Hq = a.num_heads;
+    const int Hkv = a.num_kv_heads;
+    const int G = Hq / Hkv;
+    const int R = 16 / G;  // new tokens per 16-row tile
+    const int Lmax = a.max_blocks_per_seq * BS;
+
+    int bid = blockIdx.x;  // kv head fastest, then token tile, then sequence
+    const int kvh = bid % Hkv;
+    bid /= Hkv;
+    const int tile = bid % a.num_q_tiles;
+    const int seq = bid / a.num_q_tiles;
+    const int qb0 = a.query_start[seq];
+    const int S = a.query_start[seq + 1] - qb0;
+    const int t0 = tile * NW * TR * R;  // the workgroup's first new token
+    if (t0 >= S) return;                // uniform over the workgroup
+    int L = a.context_lens[seq];
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    // positions the workgroup reads: up to its last row's own position
+    const int end = max(min(L, L - S + t0 + min(NW * TR * R, S - t0)), 0);
+    // this wave's tiles: tile u holds new tokens tw + u*R .. + R - 1
+    const int tw = t0 + wave * TR * R;
+    const int wend = max(min(L, L - S + tw + max(min(TR * R, S - tw), 0)), 0);  // 0: no rows
+    const int first_pos = L - S + tw;  // position of the wave's first row
+    const int head = kvh * G + n % G;
+    bool rowv[TR];
+    int lim[TR];       // last position row n of tile u attends to (-1: padding row)
+    size_t orow[TR];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+        const int tok = tw + u * R + n / G;  // the new token of row n
+        rowv[u] = n < R * G && tok < S;
+        lim[u] = rowv[u] ? L - S + tok : -1;
+        orow[u] = ((size_t)(qb0 + (rowv[u] ? tok : 0)) * Hq + head) * D;
+    }
+
+    const size_t row_bytes = (size_t)Hkv * D * 2;
+    const size_t block_bytes = row_bytes * BS;
+    const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
+    const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    const int nb = (L + BS - 1) / BS;
+    const uint32_t loff = (uint32_t)(lr * row_bytes + lc * 16);
+
+    // Qᵀ operands: lane (g, n) holds row n's q[32j + 8g .. +7]; padding rows are 0
+    u32x4 qb[TR][NJ];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            qb[u][j] = u32x4{0u, 0u, 0u, 0u};
+            if (rowv[u]) qb[u][j] = *(const u32x4*)(a.query + orow[u] + 32 * j + 8 * g);
+        }
+    }
+
+    // reference max of row n's scores (log2 units): a finite sentinel below
+    // any score, so that exp2(s - m) of a masked score (-inf) is 0 before
+    // the first real score arrives
+    float m[TR], lsum[TR];  // lsum: this lane's share of row n's Σ exp2(s - m)
+    f32x4 oacc[TR][NT];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+        m[u] = -1e30f;
+        lsum[u] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) oacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- loads: instruction j of a chunk brings rows j*RPL + wave*RPW + lr,
+    // through a descriptor whose range ends at the wave's last valid row (an
+    // absent block, or rows at or past `end`, read as zeros) ---------------
+    u32x4 kr[LPC], vr[LPC];
+    auto issue = [&](int cs) {
+#pragma unroll
+        for (int j = 0; j < LPC; ++j) {
+            const int tok0 = cs + j * RPL + wave * RPW;
+            const int lb = tok0 / BS;
+            const int pid = lb < nb ? bt[lb] : -1;
+            // (a uniform value the compiler would clamp with a vector med3,
+            // which then makes every descriptor a per-lane one)
+            const int rows = __builtin_amdgcn_readfirstlane(min(max(end - tok0, 0), RPW));
+            const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
+            const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
+            const size_t boff =
+                ok ? (size_t)pid * block_bytes + (size_t)(tok0 - lb * BS) * row_bytes : 0;
+            kr[j] = buffer_load16(make_rsrc(kbase + boff, nrec), loff);
+            vr[j] = buffer_load16(make_rsrc(vbase + boff, nrec), loff);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < LPC; ++j) {
+            const int row = j * RPL + wave * RPW + lr;
+            *(u32x4*)(sm_k[buf] + row * ROWB + lc * 16) = kr[j];
+            *(u32x4*)(sm_v[buf] + row * ROWB + lc * 16) = vr[j];
+        }
+    };
+    // bit e: position cs + e is below `end` and its block is in the pool
+    auto present = [&](int cs) -> uint32_t {
+        uint32_t okm = 0;
+#pragma unroll
+        for (int b = 0; b < CH / BSC; ++b) {
+            const int lb = (cs + b * BSC) / BS;
+            const int pid = lb < nb ? bt[lb] : -1;
+            if (pid >= 0 && pid < a.num_blocks) okm |= kBlockBits << (b * BSC);
+        }
+        const int rest = end - cs;
+        return rest >= CH ? okm : okm & ((1u << rest) - 1u);
+    };
+
+    auto compute = [&](int cs, const char* kt, const char* vt) {
+        const uint32_t okm = __builtin_amdgcn_readfirstlane(present(cs));
+        // a chunk wholly present and at or before every row's own position
+        // needs no mask (most chunks of a long cached prefix)
+        const bool inside = okm == 0xffffffffu && cs + CH - 1 <= first_pos;
+        // ---- scores Sᵀ: lane (g, n) gets row n, tokens 16s + 4g + k; each
+        // K operand read from LDS serves every tile of the wave ------------
+        f32x4 sc[TR][NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int u = 0; u < TR; ++u) sc[u][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const char* krow = kt + (16 * s + n) * ROWB + 16 * g;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const u32x4 kv = *(const u32x4*)(krow + 64 * j);
+#pragma unroll
+                for (int u = 0; u < TR; ++u) sc[u][s] = Mma<KV>::mma(kv, qb[u][j], sc[u][s]);
+            }
+        }
+        u32x4 phi[TR], plo[TR];
+#pragma unroll
+        for (int u = 0; u < TR; ++u) {
+            float sv[4 * NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e = 16 * s + 4 * g + k;
+                    const bool ok = inside || (((okm >> e) & 1u) && cs + e <= lim[u]);
+                    sv[4 * s + k] = ok ? sc[u][s][k] * a.scale_log2 : -INFINITY;
+                }
+            }
+            // ---- online softmax of row n ---------------------------------
+            // The reference m moves only when the chunk's max passes it by
+            // more than 8 (log2 units), and then for every row of the tile:
+            // the result is the same for any reference, the weights stay
+            // below 2^8, and most chunks skip rescaling the accumulators.
+            float cm = sv[0];
+#pragma unroll
+            for (int e = 1; e < 4 * NS; ++e) cm = fmaxf(cm, sv[e]);
+            cm = max_over_groups(cm);
+            if (__builtin_amdgcn_ballot_w64(cm > m[u] + 8.f) != 0) {
+                const float mn = fmaxf(m[u], cm);
+                const float alpha = fast_exp2(m[u] - mn);  // 0 while m is the sentinel
+                m[u] = mn;
+                lsum[u] *= alpha;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) oacc[u][t] *= alpha;
+            }
+            float pr[4 * NS];
+#pragma unroll
+            for (int e = 0; e < 4 * NS; ++e) {
+                pr[e] = fast_exp2(sv[e] - m[u]);
+                lsum[u] += pr[e];
+            }
+            // Pᵀ operand in hi + lo halves
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Mma<KV>::split2(pr[2 * e], pr[2 * e + 1], &hw[e], &lw[e]);
+            phi[u] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            plo[u] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        }
+        // ---- Oᵀ += Vᵀ · Pᵀ: tokens 4g + e (e < 4) and 16 + 4g + e - 4; each
+        // Vᵀ operand serves every tile ------------------------------------
+        const int e4 = n >> 2, q4 = n & 3;
+        const char* r0 = vt + (4 * g + e4) * ROWB + q4 * 8;
+        const char* r1 = r0 + 16 * ROWB;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const u32x2 lo = lds_read_tr16(r0 + 32 * t);
+            const u32x2 hi = lds_read_tr16(r1 + 32 * t);
+            const u32x4 av = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+            for (int u = 0; u < TR; ++u) {
+                oacc[u][t] = Mma<KV>::mma(av, phi[u], oacc[u][t]);
+                oacc[u][t] = Mma<KV>::mma(av, plo[u], oacc[u][t]);
+            }
+        }
+    };
+
+    // ---- the context, chunk by chunk; every wave takes every iteration
+    // (the barrier), a wave computes only chunks that hold a position one
+    // of its rows attends to. The loads and stores run on every pass, also
+    // past the last chunk, where their descriptors have no range (zeros, no
+    // memory traffic): a load issued on some paths only would make the wait
+    // counts of every path assume it absent, and the first product of a
+    // chunk would then wait for the next chunk's loads. ---------------------
+    const int nch = (end + CH - 1) / CH;
+    issue(0);
+    stash(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int cs = c * CH;
+        issue(cs + CH);
+        if (cs < wend) compute(cs, sm_k[c & 1], sm_v[c & 1]);
+        stash((c + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ ---------------
+#pragma unroll
+    for (int u = 0; u < TR; ++u) {
+        const float tot = sum_over_groups(lsum[u]);
+        if (rowv[u]) {
+            const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const size_t o = orow[u] + 16 * t + 4 * g;
+                OUT::store2(a.out, o, oacc[u][t][0] * inv, oacc[u][t][1] * inv);
+                OUT::store2(a.out, o + 2, oacc[u][t][2] * inv, oacc[u][t][3] * inv);
+            }
+        }
+    }
+}
+
+template <class KV, class OUT, int D, int NW, int TR>
+attn_fn pick_prefill_bs(int bs) {
+    switch (bs) {
+        case 8: return attn_prefill_kernel<KV, OUT, D, 8, NW, TR>;
+        case 16: return attn_prefill_kernel<KV, OUT, D, 16, NW, TR>;
+        case 32: return attn_prefill_kernel<KV, OUT, D, 32, NW, TR>;
+        case 64: return attn_prefill_kernel<KV, OUT, D, 64, NW, TR>;
+    }
+    return nullptr;
+}
+
+template <class KV, class OUT, int NW, int TR>
+attn_fn pick_prefill_d(int d, int bs) {
+    if (d == 128) return pick_prefill_bs<KV, OUT, 128, NW, TR>(bs);
+    // head_dim 64: 8 rows per wave-load, at most 4 waves for a 32-token chunk
+    if constexpr (NW <= 4) {
+        if (d == 64) return pick_prefill_bs<KV, OUT, 64, NW, TR>(bs);
+    }
+    return nullptr;
+}
+
+template <class KV, int NW, int TR>
+attn_fn pick_prefill_out(pa_dtype out, pa_dtype kv, int d, int bs) {
+    if (out == PA_F32) return pick_prefill_d<KV, OutF32, NW, TR>(d, bs);
+    if (out != kv) return nullptr;
+    if (kv == PA_F16) return pick_prefill_d<KV, OutF16, NW, TR>(d, bs);
+    return pick_prefill_d<KV, OutBF16, NW, TR>(d, bs);
+}
+
+}  // namespace pa

@@ -1,11 +1,22 @@
-// Instances of the matrix-core kernel for prefill.
-#include "pa_attn_gqa.h"
+// Instances of the prefill kernel.
+#include "pa_attn_prefill.h"
 #include "pa_kernels.h"
 
 namespace pa {
 
-attn_fn pick_prefill_kernel(pa_dtype kv, pa_dtype out, int d, int bs) {
-    return pick_gqa_mode<kModePrefill>(kv, out, d, bs);
+namespace {
+template <int NW>
+attn_fn pick_cfg(pa_dtype kv, pa_dtype out, int d, int bs) {
+    if (kv == PA_F16) return pick_prefill_out<KvF16, NW, 1>(out, kv, d, bs);
+    if (kv == PA_BF16) return pick_prefill_out<KvBF16, NW, 1>(out, kv, d, bs);
+    return nullptr;
+}
+}  // namespace
+
+attn_fn pick_prefill_kernel(pa_dtype kv, pa_dtype out, int d, int bs, int waves) {
+    if (waves == 4) return pick_cfg<4>(kv, out, d, bs);
+    if (waves == 8) return pick_cfg<8>(kv, out, d, bs);
+    return nullptr;
 }
 
 }  // namespace pa

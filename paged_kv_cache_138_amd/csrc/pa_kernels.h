@@ -19,11 +19,10 @@ namespace pa {
 constexpr int kWaves = PA_WAVES;         // wavefronts per workgroup, one-head kernel
 constexpr int kGqaWaves = PA_GQA_WAVES;  // and matrix-core kernel
 
-// what a matrix-core kernel instance computes
+// what a grouped-query decode kernel instance computes
 enum GqaMode {
-    kModeDecode = 0,   // decode: one sequence's query heads of a kv head per workgroup
-    kModePrefix = 1,   // decode over a shared prefix: several sequences per workgroup
-    kModePrefill = 2,  // prefill: several new tokens of one sequence per workgroup
+    kModeDecode = 0,  // one sequence's query heads of a kv head per workgroup
+    kModePrefix = 1,  // over a shared prefix: several sequences per workgroup
 };
 
 typedef void (*attn_fn)(AttnArgs);
@@ -31,6 +30,8 @@ typedef void (*attn_fn)(AttnArgs);
 attn_fn pick_attn(pa_dtype kv, pa_dtype out, int d, int bs);            // pa_inst_mha.hip
 attn_fn pick_gqa(pa_dtype kv, pa_dtype out, int d, int bs);             // pa_inst_gqa.hip
 attn_fn pick_prefix_kernel(pa_dtype kv, pa_dtype out, int d, int bs);   // pa_inst_prefix.hip
-attn_fn pick_prefill_kernel(pa_dtype kv, pa_dtype out, int d, int bs);  // pa_inst_prefill.hip
+// prefill kernel with `waves` (4 or 8) wavefronts of 16 rows per workgroup
+attn_fn pick_prefill_kernel(pa_dtype kv, pa_dtype out, int d, int bs,
+                            int waves);  // pa_inst_prefill.hip
 
 }  // namespace pa

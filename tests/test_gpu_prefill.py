@@ -62,6 +62,7 @@ CASES = [
     (16, 1, 64, "bf16", 8, 40, [5, 17]),                 # 16 heads per kv head: one token
     (6, 2, 64, "f16", 64, 128, [1, 64, 65, 130]),        # block 64, 3 heads: 5 tokens, 15 rows
     (4, 4, 128, "f16", 8, 24, [3, 0, 5, 0, 70]),         # requests without new tokens
+    (4, 4, 128, "bf16", 32, 64, [1, 130, 64, 17]),       # 8 waves of 16 new tokens
 ]
 
 
