@@ -487,7 +487,8 @@ def bench_prefill(args):
                             "unique_GB_per_s": round(unique_bytes / (attn_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic("%s/prefill" % w.name),
                      "kernel": "pa_prefill: %d back-to-back launches between HIP events, "
                                "avg %.2f us" % (K, attn_ms * 1e3)},
         "host_data_generation_s": round(t_gen, 2),
