@@ -210,16 +210,20 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
                 for (int u = 0; u < TR; ++u) sc[u][s] = Mma<KV>::mma(kv, qb[u][j], sc[u][s]);
             }
         }
+        const uint32_t okl = inside ? 0xffffffffu : okm;
         u32x4 phi[TR], plo[TR];
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
+            // (selects and bitwise ands, no short-circuit: the compiler
+            // would branch on a uniform operand of || and &&)
+            const int limx = inside ? 0x7fffffff : lim[u];
             float sv[4 * NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int e = 16 * s + 4 * g + k;
-                    const bool ok = inside || (((okm >> e) & 1u) && cs + e <= lim[u]);
+                    const bool ok = (((okl >> e) & 1u) != 0u) & (cs + e <= limx);
                     sv[4 * s + k] = ok ? sc[u][s][k] * a.scale_log2 : -INFINITY;
                 }
             }
