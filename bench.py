@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--block-size", type=int, default=None,
                     help="re-block the workload (same tokens and cache bytes, other block size)")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="the workload with another head_dim (same tokens and heads)")
     ap.add_argument("--unfused", action="store_true",
                     help="split path: run the scatter as its own launch instead of inside the "
                          "partition launch (pa_decode_split_append)")
@@ -110,7 +112,7 @@ def copy_calibration(mib):
 
 
 def pick_workload(args):
-    """The named workload, with --lens and --block-size applied."""
+    """The named workload, with --lens, --block-size and --head-dim applied."""
     import dataclasses
     from paged_kv_cache_138_amd import workloads as W
     w = W.WORKLOADS[args.workload]
@@ -124,6 +126,8 @@ def pick_workload(args):
         w = dataclasses.replace(w, block_size=bs, num_blocks=tokens // bs,
                                 max_blocks_per_seq=per_seq // bs,
                                 name=w.name + "+bs=%d" % bs)
+    if args.head_dim and args.head_dim != w.head_dim:
+        w = dataclasses.replace(w, head_dim=args.head_dim, name=w.name + "+d=%d" % args.head_dim)
     return w
 
 

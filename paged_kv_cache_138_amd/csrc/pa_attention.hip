@@ -59,6 +59,29 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     OUT::store(a.out, (size_t)row * D + d, o);
 }
 
+// head_dim 80 and 96: one row per wavefront, each lane merging the
+// elements lane and lane + 64 of it.
+template <class OUT, int D>
+__global__ __launch_bounds__(256) void lse_merge_wave_kernel(MergeArgs a) {
+    static_assert(D <= 128, "two elements per lane at most");
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    if (row >= a.num_seqs * a.num_heads) return;
+    const int seq = row / a.num_heads;
+    int L = a.context_lens[seq];
+    if (L < 0) L = 0;
+    int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
+    if (np > a.max_partitions) np = a.max_partitions;
+    if (np <= 1) return;
+    const size_t r = (size_t)row * a.max_partitions;
+#pragma unroll
+    for (int d = lane; d < D; d += 64) {
+        const float o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d,
+                                          np, D);
+        OUT::store(a.out, (size_t)row * D + d, o);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
@@ -138,6 +161,8 @@ template <class OUT>
 merge_fn pick_merge_d(int d) {
     switch (d) {
         case 64: return lse_merge_kernel<OUT, 64>;
+        case 80: return lse_merge_wave_kernel<OUT, 80>;
+        case 96: return lse_merge_wave_kernel<OUT, 96>;
         case 128: return lse_merge_kernel<OUT, 128>;
     }
     return nullptr;
@@ -175,8 +200,12 @@ pa_status validate_decode(void* out, pa_dtype out_dtype, const void* query, cons
     PA_REQUIRE(out_dtype == PA_F32 || out_dtype == kv_dtype, PA_ERR_DTYPE,
                "out dtype must be PA_F32 or the kv dtype");
     PA_REQUIRE(isfinite(scale), PA_ERR_SHAPE, "scale must be finite");
-    PA_REQUIRE(s.head_dim == 64 || s.head_dim == 128, PA_ERR_UNSUPPORTED,
-               "head_dim %d not in {64, 128}", s.head_dim);
+    PA_REQUIRE(s.head_dim == 64 || s.head_dim == 80 || s.head_dim == 96 || s.head_dim == 128,
+               PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128}", s.head_dim);
+    // lanes of missing 16-byte slices (head_dim 80, 96) read past a block's
+    // range with a fixed offset, which must stay past every block
+    PA_REQUIRE((int64_t)s.block_size * s.num_kv_heads * s.head_dim * 2 < ((int64_t)1 << 27),
+               PA_ERR_SHAPE, "a block of more than 128 MiB");
     PA_REQUIRE(s.block_size == 8 || s.block_size == 16 || s.block_size == 32 ||
                    s.block_size == 64,
                PA_ERR_UNSUPPORTED, "block_size %d not in {8, 16, 32, 64}", s.block_size);
@@ -380,7 +409,7 @@ pa_status launch_merge(void* out, pa_dtype out_dtype, const float* part_out,
     MergeArgs m{out, part_out, part_max, part_sum, context_lens,
                 num_seqs, num_heads, max_partitions, partition_size};
     const int64_t rows = (int64_t)num_seqs * num_heads;
-    const int64_t rpw = 256 / head_dim;
+    const int64_t rpw = head_dim % 64 == 0 ? 256 / head_dim : 4;  // rows per workgroup
     const int64_t grid = (rows + rpw - 1) / rpw;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     hipLaunchKernelGGL(mfn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, m);
@@ -549,8 +578,8 @@ extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* pa
     clear_error();
     PA_REQUIRE(num_seqs >= 0 && num_heads > 0 && max_partitions > 0 && partition_size > 0,
                PA_ERR_SHAPE, "invalid sizes");
-    PA_REQUIRE(head_dim == 64 || head_dim == 128, PA_ERR_UNSUPPORTED,
-               "head_dim %d not in {64, 128}", head_dim);
+    PA_REQUIRE(head_dim == 64 || head_dim == 80 || head_dim == 96 || head_dim == 128,
+               PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128}", head_dim);
     PA_REQUIRE(out_dtype == PA_F32 || out_dtype == PA_F16 || out_dtype == PA_BF16,
                PA_ERR_DTYPE, "invalid out dtype");
     if (num_seqs == 0) return PA_OK;

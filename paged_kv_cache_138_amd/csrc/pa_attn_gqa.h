@@ -126,16 +126,19 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     constexpr int CH = PA_GQA_CHUNK;    // tokens per chunk (32 or 64)
     constexpr int NS = CH / 16;         // 16-token sub-blocks of a chunk
     constexpr int NH = CH / 32;         // 32-token halves (one p·v contraction each)
-    constexpr int NJ = D / 32;          // q·k products per 16-token sub-block
-    constexpr int NT = D / 16;          // 16-wide output tiles of head_dim
-    constexpr int LPR = D / 8;          // lanes per row in a coalesced V load
+    // head_dim 80 and 96 are laid out as 128: the missing slices read as
+    // zeros, so they add nothing to q·k and give output columns never stored
+    constexpr int DP = D <= 64 ? 64 : 128;
+    constexpr int NJ = DP / 32;         // q·k products per 16-token sub-block
+    constexpr int NT = DP / 16;         // 16-wide output tiles of head_dim
+    constexpr int LPR = DP / 8;         // lanes per row in a coalesced V load
     constexpr int RPI = 64 / LPR;       // rows per coalesced V load
     constexpr int VL = CH / RPI;        // V loads per chunk
     constexpr int RPB = BS < CH ? BS : CH;  // rows one load descriptor covers
     constexpr int BPC = CH / RPB;       // descriptors per chunk (blocks, or one block's slice)
-    constexpr int ROWB = D * 2 + 16;    // LDS bytes per K or V row (padding spreads banks)
+    constexpr int ROWB = DP * 2 + 16;   // LDS bytes per K or V row (padding spreads banks)
     constexpr int TILE = CH * ROWB;     // LDS bytes of one chunk's K (then V) rows
-    constexpr int OROW = D + 4;         // floats per row of the wave's partial output
+    constexpr int OROW = DP + 4;        // floats per row of the wave's partial output
     static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
     static_assert(RPB % RPI == 0, "the rows of one coalesced load share a block");
     static_assert(CH == 32 || CH == 64, "chunk of 32 or 64 tokens");
@@ -145,7 +148,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     __shared__ __attribute__((aligned(16))) char sm_v[NW][TILE];
     __shared__ float sm_m[NW][16];
     __shared__ float sm_l[NW][16];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_new[NW][2][D];  // fused append: new K, V rows
+    __shared__ __attribute__((aligned(16))) uint16_t sm_new[NW][2][DP];  // fused append: new K, V rows
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -153,6 +156,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     const int n = lane & 15;   // head inside the group (column of every product)
     const int vr = lane / LPR; // row of a coalesced V load
     const int vc = lane % LPR; // 16-byte slice of that row
+    const bool vcv = vc * 8 < D;  // the slice exists (head_dim 80, 96: not all do)
 
     const int Hq = a.num_heads;
     const int Hkv = a.num_kv_heads;
@@ -214,10 +218,14 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             has_new = slot_ok && Lsrc > 0;
             store_new = slot_ok && sub == 0 && vr == 0;
             if (store_new) {
-                *(u32x4*)&sm_new[wave][0][vc * 8] =
-                    *(const u32x4*)(a.new_key + seq0 * a.new_key_stride + kvh * D + vc * 8);
-                *(u32x4*)&sm_new[wave][1][vc * 8] =
-                    *(const u32x4*)(a.new_value + seq0 * a.new_value_stride + kvh * D + vc * 8);
+                u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = nk;
+                if (vcv) {
+                    nk = *(const u32x4*)(a.new_key + seq0 * a.new_key_stride + kvh * D + vc * 8);
+                    nv = *(const u32x4*)(a.new_value + seq0 * a.new_value_stride + kvh * D +
+                                         vc * 8);
+                }
+                *(u32x4*)&sm_new[wave][0][vc * 8] = nk;
+                *(u32x4*)&sm_new[wave][1][vc * 8] = nv;
             }
         }
     }
@@ -244,7 +252,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             qb[j] = u32x4{0u, 0u, 0u, 0u};
-            if (real) qb[j] = *(const u32x4*)(qrow + 32 * j + 8 * g);
+            if (real && 32 * j + 8 * g < D) qb[j] = *(const u32x4*)(qrow + 32 * j + 8 * g);
         }
     }
 
@@ -283,13 +291,14 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // Chunks start on descriptor boundaries (partitions are whole blocks, and
     // a block longer than a chunk holds a whole number of chunks). Load i of
     // a chunk brings rows vr + RPI*i (the RPI rows of one load share a block).
+    const uint32_t voff = vcv ? (uint32_t)(vc * 16) : kNoSlice;
     auto issue_rows = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[VL]) {
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
             const int t = vr + RPI * i;
             const int b = (RPI * i) / RPB;
             const int row = t - b * RPB;
-            buf[i] = buffer_load16(rs[b], (uint32_t)(row * row_bytes + vc * 16));
+            buf[i] = buffer_load16(rs[b], (uint32_t)(row * row_bytes) + voff);
         }
     };
     auto issue_k = [&](const ChunkIds& ci, u32x4 (&kb)[VL]) { issue_rows(ci.k, kb); };
@@ -494,7 +503,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             }
         }
     }
-    if (store_new) {
+    if (store_new && vcv) {
         const size_t dst = (size_t)a.slot_mapping[seq0] * (Hkv * D) + kvh * D + vc * 8;
         *(u32x4*)((uint16_t*)a.key_cache + dst) = *(const u32x4*)&sm_new[wave][0][vc * 8];
         *(u32x4*)((uint16_t*)a.value_cache + dst) = *(const u32x4*)&sm_new[wave][1][vc * 8];
@@ -518,6 +527,8 @@ template <class KV, class OUT, int MODE>
 attn_fn pick_gqa_d(int d, int bs) {
     switch (d) {
         case 64: return pick_gqa_bs<KV, OUT, 64, MODE>(bs);
+        case 80: return pick_gqa_bs<KV, OUT, 80, MODE>(bs);
+        case 96: return pick_gqa_bs<KV, OUT, 96, MODE>(bs);
         case 128: return pick_gqa_bs<KV, OUT, 128, MODE>(bs);
     }
     return nullptr;

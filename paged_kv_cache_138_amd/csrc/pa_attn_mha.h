@@ -46,7 +46,11 @@ __device__ __forceinline__ void tr_step(float (&pd)[N], int c) {
 template <class KV, class OUT, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_kernel(AttnArgs a) {
-    constexpr int LPR = D / 8;          // lanes per cache row
+    // head_dim 80 and 96 are laid out as 128: the lanes of the missing
+    // slices load nothing (an offset past every range reads zeros) and
+    // store nothing, so every product and sum is the real one
+    constexpr int DP = D <= 64 ? 64 : 128;
+    constexpr int LPR = DP / 8;         // lanes per cache row
     constexpr int RPI = 64 / LPR;       // rows per load instruction
     constexpr int NI = LPR;             // load instructions per chunk
     constexpr int CHUNK = RPI * NI;     // tokens per chunk (64)
@@ -60,12 +64,13 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     static_assert(CHUNK == 64, "one score per lane per chunk");
     static_assert(RPB % RPI == 0 && CHUNK % BS == 0 && BS % RPB == 0,
                   "blocks tile the chunk, descriptors the block");
-    static_assert(LPR == 8 || LPR == 16, "head_dim 64 or 128");
+    static_assert(LPR == 8 || LPR == 16, "head_dim laid out as 64 or 128");
+    static_assert(D % 16 == 0 && D <= DP, "head_dim a multiple of 16, at most the layout");
 
     __shared__ float sm_m[NW];
     __shared__ float sm_l[NW];
-    __shared__ float sm_acc[NW][D];
-    __shared__ __attribute__((aligned(16))) uint16_t sm_new[NW][2][D];  // fused append: new K, V rows
+    __shared__ float sm_acc[NW][DP];
+    __shared__ __attribute__((aligned(16))) uint16_t sm_new[NW][2][DP];  // fused append: new K, V rows
 
     // the wave index is uniform inside a wavefront; saying so keeps every
     // chunk, block-table and address computation in scalar registers
@@ -93,6 +98,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     const int lane = threadIdx.x & 63;
     const int r = lane / LPR;  // row within a load instruction
     const int c = lane % LPR;  // 8-element slice of the row
+    const bool cv = c * 8 < D;  // the slice exists (head_dim 80, 96: not all do)
 
     const int Lmax = a.max_blocks_per_seq * BS;
     int L = a.context_lens[seq];
@@ -112,9 +118,10 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
     // byte offset, inside a block, of the first row this lane reads; load j
     // of a block reads RPI * j rows further
-    const uint32_t loff0 = (uint32_t)(r * row_bytes + c * 16);
+    const uint32_t loff0 = (uint32_t)(r * row_bytes) + (cv ? (uint32_t)(c * 16) : kNoSlice);
 
-    const u32x4 q = *(const u32x4*)(a.query + ((size_t)seq * Hq + head) * D + c * 8);
+    u32x4 q = u32x4{0u, 0u, 0u, 0u};
+    if (cv) q = *(const u32x4*)(a.query + ((size_t)seq * Hq + head) * D + c * 8);
 
     // Fused append: position L - 1 of the partition that holds it is the new
     // token, whose rows come from new_key / new_value instead of the cache.
@@ -132,10 +139,13 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     const bool has_new = slot_ok && L > 0;  // every wave of the head
     const bool app = has_new && sub == 0;   // the wave that folds it in
     if (slot_ok && sub == 0 && r == 0) {
-        *(u32x4*)&sm_new[hslot][0][c * 8] =
-            *(const u32x4*)(a.new_key + seq * a.new_key_stride + kvh * D + c * 8);
-        *(u32x4*)&sm_new[hslot][1][c * 8] =
-            *(const u32x4*)(a.new_value + seq * a.new_value_stride + kvh * D + c * 8);
+        u32x4 nk = u32x4{0u, 0u, 0u, 0u}, nv = nk;
+        if (cv) {
+            nk = *(const u32x4*)(a.new_key + seq * a.new_key_stride + kvh * D + c * 8);
+            nv = *(const u32x4*)(a.new_value + seq * a.new_value_stride + kvh * D + c * 8);
+        }
+        *(u32x4*)&sm_new[hslot][0][c * 8] = nk;
+        *(u32x4*)&sm_new[hslot][1][c * 8] = nv;
     }
     const int end_c = has_new ? L - 1 : end;  // end of the tokens read from the cache
 
@@ -380,7 +390,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         a.part_max[pidx] = M * kLn2;  // natural-log units
         a.part_sum[pidx] = tot;
     }
-    if (slot_ok && sub == 0 && r == 0 && head % (Hq / a.num_kv_heads) == 0) {
+    if (slot_ok && sub == 0 && r == 0 && cv && head % (Hq / a.num_kv_heads) == 0) {
         const size_t dst = (size_t)a.slot_mapping[seq] * (a.num_kv_heads * D) + kvh * D + c * 8;
         *(u32x4*)((uint16_t*)a.key_cache + dst) = *(const u32x4*)&sm_new[hslot][0][c * 8];
         *(u32x4*)((uint16_t*)a.value_cache + dst) = *(const u32x4*)&sm_new[hslot][1][c * 8];

@@ -57,13 +57,16 @@ template <class KV, class OUT, int D, int BS, int NW, int TR>
 __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
     constexpr int CH = 32;         // tokens per chunk
     constexpr int NS = CH / 16;    // 16-token sub-blocks of a chunk
-    constexpr int NJ = D / 32;     // q·k products per 16-token sub-block
-    constexpr int NT = D / 16;     // 16-wide output tiles of head_dim
-    constexpr int LPR = D / 8;     // lanes per row of a 16-byte load
+    // head_dim 80 and 96 are laid out as 128: the missing slices read as
+    // zeros, so they add nothing to q·k and give output columns never stored
+    constexpr int DP = D <= 64 ? 64 : 128;
+    constexpr int NJ = DP / 32;    // q·k products per 16-token sub-block
+    constexpr int NT = DP / 16;    // 16-wide output tiles of head_dim
+    constexpr int LPR = DP / 8;    // lanes per row of a 16-byte load
     constexpr int RPW = 64 / LPR;  // rows one wave loads per instruction (4 or 8)
     constexpr int RPL = NW * RPW;  // rows the workgroup loads per instruction
     constexpr int LPC = CH / RPL;  // load instructions per chunk, of K and of V
-    constexpr int ROWB = D * 2 + 16;  // LDS bytes per row (padding spreads banks)
+    constexpr int ROWB = DP * 2 + 16;  // LDS bytes per row (padding spreads banks)
     constexpr int TILE = CH * ROWB;
     constexpr int BSC = BS < CH ? BS : CH;  // tokens of a chunk in one block
     constexpr uint32_t kBlockBits = BSC == 32 ? 0xffffffffu : (1u << BSC) - 1u;
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
     const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
     const int nb = (L + BS - 1) / BS;
-    const uint32_t loff = (uint32_t)(lr * row_bytes + lc * 16);
+    const uint32_t loff = (uint32_t)(lr * row_bytes) + (lc * 8 < D ? (uint32_t)(lc * 16) : kNoSlice);
 
     // Qᵀ operands: lane (g, n) holds row n's q[32j + 8g .. +7]; padding rows are 0
     u32x4 qb[TR][NJ];
@@ -131,7 +134,8 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             qb[u][j] = u32x4{0u, 0u, 0u, 0u};
-            if (rowv[u]) qb[u][j] = *(const u32x4*)(a.query + orow[u] + 32 * j + 8 * g);
+            if (rowv[u] && 32 * j + 8 * g < D)
+                qb[u][j] = *(const u32x4*)(a.query + orow[u] + 32 * j + 8 * g);
         }
     }
 
@@ -302,6 +306,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
             const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
+                if (16 * t >= D) break;  // columns of the layout only
                 const size_t o = orow[u] + 16 * t + 4 * g;
                 OUT::store2(a.out, o, oacc[u][t][0] * inv, oacc[u][t][1] * inv);
                 OUT::store2(a.out, o + 2, oacc[u][t][2] * inv, oacc[u][t][3] * inv);
@@ -324,6 +329,8 @@ attn_fn pick_prefill_bs(int bs) {
 template <class KV, class OUT, int NW, int TR>
 attn_fn pick_prefill_d(int d, int bs) {
     if (d == 128) return pick_prefill_bs<KV, OUT, 128, NW, TR>(bs);
+    if (d == 96) return pick_prefill_bs<KV, OUT, 96, NW, TR>(bs);
+    if (d == 80) return pick_prefill_bs<KV, OUT, 80, NW, TR>(bs);
     // head_dim 64: 8 rows per wave-load, at most 4 waves for a 32-token chunk
     if constexpr (NW <= 4) {
         if (d == 64) return pick_prefill_bs<KV, OUT, 64, NW, TR>(bs);

@@ -182,6 +182,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 #define PA_LOAD_AUX 2
 #endif
 
+// Added to the in-block offset of a lane whose 16-byte slice of the row
+// does not exist (head_dim laid out wider than it is): past every range a
+// descriptor has (at most a block, and the host requires blocks below
+// 2^27 bytes), so the load reads zeros without touching memory.
+constexpr uint32_t kNoSlice = 1u << 27;
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, PA_LOAD_AUX);
 }

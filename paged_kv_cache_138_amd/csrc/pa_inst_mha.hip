@@ -20,6 +20,8 @@ template <class KV, class OUT>
 attn_fn pick_attn_d(int d, int bs) {
     switch (d) {
         case 64: return pick_attn_bs<KV, OUT, 64>(bs);
+        case 80: return pick_attn_bs<KV, OUT, 80>(bs);
+        case 96: return pick_attn_bs<KV, OUT, 96>(bs);
         case 128: return pick_attn_bs<KV, OUT, 128>(bs);
     }
     return nullptr;

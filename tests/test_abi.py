@@ -61,7 +61,7 @@ def _decode(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=96), 4), (dict(BS=24), 4), (dict(BS=128), 4), (dict(Hq=6, Hkv=4), 2), (dict(kvdt=2), 3),
+    (dict(D=112), 4), (dict(D=256), 4), (dict(BS=24), 4), (dict(BS=128), 4), (dict(Hq=6, Hkv=4), 2), (dict(kvdt=2), 3),
     (dict(out_dtype=1), 3), (dict(query=None), 1), (dict(kc=(1 << 12) + 4), 7),
     (dict(B=-1), 2), (dict(scale=float("inf")), 2), (dict(NB=0), 2),
 ])
@@ -154,7 +154,7 @@ def _prefill(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(Hq=34, Hkv=2), 4), (dict(D=96), 4), (dict(T=-1), 2), (dict(maxq=-2), 2),
+    (dict(Hq=34, Hkv=2), 4), (dict(D=72), 4), (dict(T=-1), 2), (dict(maxq=-2), 2),
     (dict(maxq=8 * 16 + 1), 2), (dict(qs=None), 1), (dict(query=None), 1), (dict(kvdt=2), 3),
     (dict(kc=(1 << 12) + 2), 7),
 ])

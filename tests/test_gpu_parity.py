@@ -549,6 +549,59 @@ def test_block_sizes_8_and_64_shared_prefix(BS, Hq, Hkv):
     _assert_close(to_host_f64(out), ref, "f32", "prefix BS=%d" % BS)
 
 
+# ---- head_dim 80 and 96 ------------------------------------------------------
+# Laid out as 128 by every kernel: the missing 16-byte slices of a row read
+# as zeros and are never stored.
+
+HD_HEADS = [
+    # (num_heads, num_kv_heads, dtype, block_size)
+    (8, 8, "f16", 16),    # one-head kernel
+    (6, 6, "bf16", 32),
+    (16, 4, "bf16", 16),  # grouped-query kernel
+    (8, 1, "f16", 8),
+]
+
+
+@pytest.mark.parametrize("D", [80, 96])
+@pytest.mark.parametrize("heads", range(len(HD_HEADS)))
+@pytest.mark.parametrize("path", ["single", "split64", "fused128"])
+def test_head_dims_80_and_96(D, heads, path):
+    Hq, Hkv, dt, BS = HD_HEADS[heads]
+    lens = [1, BS, BS + 1, 63, 64, 65, 200, 511, 700]
+    need = sum(-(-L // BS) for L in lens)
+    w = _small("hd%d" % D, num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+               dtype=dt, block_size=BS, num_blocks=need + 40, max_blocks_per_seq=-(-704 // BS),
+               lens="fixed:1")
+    b = W.make_batch(w, seed=D + 7 * heads, lens=lens, unallocated="nan")
+    split = path != "single"
+    P = int(path[5:]) if path.startswith("split") else (128 if path == "fused128" else None)
+    for od in (torch.float32, None):
+        db = DeviceBatch(b, out_dtype=od, split=split, partition_size=P,
+                         fused=path.startswith("fused"))
+        out = db.step()
+        torch.cuda.synchronize()
+        kc, vc, ref = _oracle_step(b)
+        assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+        assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+        _assert_close(to_host_f64(out), ref, "f32" if od is not None else dt,
+                      "D=%d heads=%s %s" % (D, HD_HEADS[heads], path))
+
+
+@pytest.mark.parametrize("D", [80, 96])
+def test_head_dims_80_and_96_shared_prefix(D):
+    P, prefix, suf = 64, 128, [1, 2, 16, 17, 100, 7]
+    w = _small("pfxhd%d" % D, num_seqs=len(suf), num_heads=8, num_kv_heads=2, head_dim=D,
+               dtype="f16", block_size=16, num_blocks=(prefix + 128 * len(suf)) // 16,
+               max_blocks_per_seq=(prefix + 128) // 16, lens="fixed:1",
+               shared_prefix_tokens=prefix, partition_size=P)
+    b = W.make_batch(w, seed=D, lens=suf, unallocated="nan")
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=P, shared_prefix=True)
+    out = db.step()
+    torch.cuda.synchronize()
+    _, _, ref = _oracle_step(b)
+    _assert_close(to_host_f64(out), ref, "f32", "prefix D=%d" % D)
+
+
 # ---- copy-on-write block copy ---------------------------------------------
 
 @pytest.mark.parametrize("dtype,NB,BS,Hkv,D,N", [

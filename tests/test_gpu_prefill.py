@@ -63,6 +63,8 @@ CASES = [
     (6, 2, 64, "f16", 64, 128, [1, 64, 65, 130]),        # block 64, 3 heads: 5 tokens, 15 rows
     (4, 4, 128, "f16", 8, 24, [3, 0, 5, 0, 70]),         # requests without new tokens
     (4, 4, 128, "bf16", 32, 64, [1, 130, 64, 17]),       # 8 waves of 16 new tokens
+    (8, 8, 80, "f16", 16, 32, [1, 16, 17, 40]),          # head_dim 80, laid out as 128
+    (14, 2, 96, "bf16", 16, 48, [3, 20, 9]),             # head_dim 96, 7 heads per kv head
 ]
 
 
