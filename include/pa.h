@@ -41,10 +41,15 @@
  *     even from fp32) or PA_F32. All accumulation is fp32
  *     (lqnn.cn/news/170268 §6: half-precision accumulation of the scores
  *     degrades long sequences).
- *   - Supported shapes: head_dim in {64, 80, 96, 128}; block_size in {8, 16, 32, 64};
- *     num_heads a multiple of num_kv_heads (query head h reads kv head
- *     h / (num_heads / num_kv_heads)); one block of a cache (block_size *
- *     num_kv_heads * head_dim elements) below 128 MiB.
+ *   - Supported shapes: head_dim in {64, 80, 96, 128, 256}; block_size in
+ *     {8, 16, 32, 64}; num_heads a multiple of num_kv_heads (query head h
+ *     reads kv head h / (num_heads / num_kv_heads)), at most 16 query heads
+ *     per kv head at head_dim 256; one block of a cache (block_size *
+ *     num_kv_heads * head_dim elements) below 128 MiB. At head_dim 256 the
+ *     decode calls run on the prefill kernel (one new token per sequence):
+ *     the fused-append calls then launch the scatter first, and the
+ *     shared-prefix calls read the prefix per sequence; the results are
+ *     those of the other widths' paths.
  */
 #ifndef PA_H
 #define PA_H

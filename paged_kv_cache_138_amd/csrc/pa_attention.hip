@@ -164,6 +164,7 @@ merge_fn pick_merge_d(int d) {
         case 80: return lse_merge_wave_kernel<OUT, 80>;
         case 96: return lse_merge_wave_kernel<OUT, 96>;
         case 128: return lse_merge_kernel<OUT, 128>;
+        case 256: return lse_merge_kernel<OUT, 256>;
     }
     return nullptr;
 }
@@ -200,8 +201,12 @@ pa_status validate_decode(void* out, pa_dtype out_dtype, const void* query, cons
     PA_REQUIRE(out_dtype == PA_F32 || out_dtype == kv_dtype, PA_ERR_DTYPE,
                "out dtype must be PA_F32 or the kv dtype");
     PA_REQUIRE(isfinite(scale), PA_ERR_SHAPE, "scale must be finite");
-    PA_REQUIRE(s.head_dim == 64 || s.head_dim == 80 || s.head_dim == 96 || s.head_dim == 128,
-               PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128}", s.head_dim);
+    PA_REQUIRE(s.head_dim == 64 || s.head_dim == 80 || s.head_dim == 96 || s.head_dim == 128 ||
+                   s.head_dim == 256,
+               PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128, 256}", s.head_dim);
+    PA_REQUIRE(s.head_dim != 256 || s.num_heads / s.num_kv_heads <= kMaxGroupMfma,
+               PA_ERR_UNSUPPORTED, "head_dim 256 takes at most %d query heads per kv head",
+               kMaxGroupMfma);
     // lanes of missing 16-byte slices (head_dim 80, 96) read past a block's
     // range with a fixed offset, which must stay past every block
     PA_REQUIRE((int64_t)s.block_size * s.num_kv_heads * s.head_dim * 2 < ((int64_t)1 << 27),
@@ -232,6 +237,23 @@ AttnArgs make_args(void* out, const void* query, const void* kc, const void* vc,
     a.num_blocks = s.num_blocks;
     a.scale_log2 = scale * kLog2e;
     return a;
+}
+
+// head_dim 256: the decode paths run on the prefill kernel in its decode
+// mode (one new token per sequence, `nparts` partitions of
+// a.partition_size), whose registers stretch to that width; the one-head
+// and grouped-query decode kernels stop at 128.
+pa_status launch_wide(AttnArgs a, const DecodeShape& s, pa_dtype kv_dtype, pa_dtype out_dtype,
+                      int nparts, void* stream, const char* what) {
+    attn_fn fn = pick_prefill_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, 4);
+    PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    a.query_start = nullptr;  // decode mode
+    a.num_q_tiles = nparts;
+    const int64_t grid = (int64_t)s.num_seqs * nparts * s.num_kv_heads;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    if (grid == 0) return PA_OK;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(4 * 64), 0, (hipStream_t)stream, a);
+    return check_launch(what);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -277,6 +299,13 @@ extern "C" pa_status pa_decode(void* out, pa_dtype out_dtype, const void* query,
     pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
                                    context_lens, s, scale, kv_dtype);
     if (st != PA_OK || num_seqs == 0) return st;
+    if (head_dim == 256) {
+        AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
+                               scale);
+        a.partition_size = max_blocks_per_seq * block_size;  // one partition per sequence
+        a.max_partitions = 1;
+        return launch_wide(a, s, kv_dtype, out_dtype, 1, stream, "pa_decode");
+    }
     int per_seq = 0, threads = 0;
     const int hl = 0;  // one head per workgroup: its waves share the whole context
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, head_dim, block_size, num_heads, num_kv_heads,
@@ -344,6 +373,26 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
                "workspace must be 256-byte aligned");
     PA_REQUIRE(workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
                "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+    char* ws = (char*)workspace;
+    if (s.head_dim == 256) {
+        // the step's scatter first, then every partition of every context
+        // (a shared prefix is read per sequence: same results)
+        if (app) {
+            st = pa_reshape_and_cache(app->new_key, app->new_value, (void*)key_cache,
+                                      (void*)value_cache, app->slot_mapping, s.num_seqs,
+                                      app->key_stride, app->value_stride, s.num_kv_heads,
+                                      s.head_dim, s.num_blocks, s.block_size, kv_dtype, stream);
+            if (st != PA_OK) return st;
+        }
+        AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
+                               scale);
+        a.part_max = (float*)(ws + lay.off_max);
+        a.part_sum = (float*)(ws + lay.off_sum);
+        a.part_out = (float*)(ws + lay.off_out);
+        a.partition_size = partition_size;
+        a.max_partitions = lay.np;
+        return launch_wide(a, s, kv_dtype, out_dtype, lay.np, stream, what);
+    }
     const int prefix_parts = prefix_tokens / partition_size;
     int per_seq = 0, threads = 0;
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, s.num_heads,
@@ -363,7 +412,6 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
                                     : nullptr;
     PA_REQUIRE(fn && (prefix_tokens == 0 || pfn), PA_ERR_UNSUPPORTED,
                "no kernel instance for this dtype/shape");
-    char* ws = (char*)workspace;
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
                            scale);
     a.part_max = (float*)(ws + lay.off_max);
@@ -578,8 +626,9 @@ extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* pa
     clear_error();
     PA_REQUIRE(num_seqs >= 0 && num_heads > 0 && max_partitions > 0 && partition_size > 0,
                PA_ERR_SHAPE, "invalid sizes");
-    PA_REQUIRE(head_dim == 64 || head_dim == 80 || head_dim == 96 || head_dim == 128,
-               PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128}", head_dim);
+    PA_REQUIRE(head_dim == 64 || head_dim == 80 || head_dim == 96 || head_dim == 128 ||
+                   head_dim == 256,
+               PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128, 256}", head_dim);
     PA_REQUIRE(out_dtype == PA_F32 || out_dtype == PA_F16 || out_dtype == PA_BF16,
                PA_ERR_DTYPE, "invalid out dtype");
     if (num_seqs == 0) return PA_OK;

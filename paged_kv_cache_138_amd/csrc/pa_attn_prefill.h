@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
     constexpr int NS = CH / 16;    // 16-token sub-blocks of a chunk
     // head_dim 80 and 96 are laid out as 128: the missing slices read as
     // zeros, so they add nothing to q·k and give output columns never stored
-    constexpr int DP = D <= 64 ? 64 : 128;
+    constexpr int DP = D <= 64 ? 64 : (D <= 128 ? 128 : 256);
     constexpr int NJ = DP / 32;    // q·k products per 16-token sub-block
     constexpr int NT = DP / 16;    // 16-wide output tiles of head_dim
     constexpr int LPR = DP / 8;    // lanes per row of a 16-byte load
@@ -90,22 +90,35 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
     const int R = 16 / G;  // new tokens per 16-row tile
     const int Lmax = a.max_blocks_per_seq * BS;
 
-    int bid = blockIdx.x;  // kv head fastest, then token tile, then sequence
+    // Decode mode (no query_start): one new token per sequence, query and
+    // out rows indexed by sequence, the context split into partitions of
+    // partition_size whose (max, sum, normalised output) go to the split
+    // workspace when a sequence has several; the grid's second coordinate
+    // is then the partition instead of the tile of new tokens.
+    const bool dec = a.query_start == nullptr;
+    int bid = blockIdx.x;  // kv head fastest, then token tile (partition), then sequence
     const int kvh = bid % Hkv;
     bid /= Hkv;
-    const int tile = bid % a.num_q_tiles;
+    const int tile = dec ? 0 : bid % a.num_q_tiles;
+    const int part = dec ? bid % a.num_q_tiles : 0;
     const int seq = bid / a.num_q_tiles;
-    const int qb0 = a.query_start[seq];
-    const int S = a.query_start[seq + 1] - qb0;
+    const int qb0 = dec ? seq : a.query_start[seq];
+    const int S = dec ? 1 : a.query_start[seq + 1] - qb0;
     const int t0 = tile * NW * TR * R;  // the workgroup's first new token
     if (t0 >= S) return;                // uniform over the workgroup
     int L = a.context_lens[seq];
     L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int P = a.partition_size;
+    const int nparts = dec ? (L + P - 1) / P : 1;
+    if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+    const int start = part * P;
     // positions the workgroup reads: up to its last row's own position
-    const int end = max(min(L, L - S + t0 + min(NW * TR * R, S - t0)), 0);
+    const int end = min(max(min(L, L - S + t0 + min(NW * TR * R, S - t0)), 0),
+                        dec ? start + P : L);
     // this wave's tiles: tile u holds new tokens tw + u*R .. + R - 1
     const int tw = t0 + wave * TR * R;
-    const int wend = max(min(L, L - S + tw + max(min(TR * R, S - tw), 0)), 0);  // 0: no rows
+    const int nq = max(min(TR * R, S - tw), 0);  // new tokens of the wave
+    const int wend = nq > 0 ? max(min(L, L - S + tw + nq), 0) : 0;  // 0: no rows
     const int first_pos = L - S + tw;  // position of the wave's first row
     const int head = kvh * G + n % G;
     bool rowv[TR];
@@ -143,6 +156,9 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
     // any score, so that exp2(s - m) of a masked score (-inf) is 0 before
     // the first real score arrives
     float m[TR], lsum[TR];  // lsum: this lane's share of row n's Σ exp2(s - m)
+    // how far a chunk's max may pass the reference before it moves (log2
+    // units); 0 in decode mode, whose partitions report their exact max
+    const float thr = dec ? 0.f : 8.f;
     f32x4 oacc[TR][NT];
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
@@ -240,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 1; e < 4 * NS; ++e) cm = fmaxf(cm, sv[e]);
             cm = max_over_groups(cm);
-            if (__builtin_amdgcn_ballot_w64(cm > m[u] + 8.f) != 0) {
+            if (__builtin_amdgcn_ballot_w64(cm > m[u] + thr) != 0) {
                 const float mn = fmaxf(m[u], cm);
                 const float alpha = fast_exp2(m[u] - mn);  // 0 while m is the sentinel
                 m[u] = mn;
@@ -286,30 +302,43 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
     // memory traffic): a load issued on some paths only would make the wait
     // counts of every path assume it absent, and the first product of a
     // chunk would then wait for the next chunk's loads. ---------------------
-    const int nch = (end + CH - 1) / CH;
-    issue(0);
+    const int nch = (max(end - start, 0) + CH - 1) / CH;
+    issue(start);
     stash(0);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        const int cs = c * CH;
+        const int cs = start + c * CH;
         issue(cs + CH);
         if (cs < wend) compute(cs, sm_k[c & 1], sm_v[c & 1]);
         stash((c + 1) & 1);
         __syncthreads();
     }
 
-    // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ ---------------
+    // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ; in decode
+    // mode with several partitions, the partition's row of the workspace --
+    const bool partial = dec && nparts > 1;
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
         const float tot = sum_over_groups(lsum[u]);
         if (rowv[u]) {
             const float inv = tot > 0.f ? 1.f / tot : 0.f;
+            const size_t pidx = ((size_t)seq * Hq + head) * a.max_partitions + part;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if (16 * t >= D) break;  // columns of the layout only
-                const size_t o = orow[u] + 16 * t + 4 * g;
-                OUT::store2(a.out, o, oacc[u][t][0] * inv, oacc[u][t][1] * inv);
-                OUT::store2(a.out, o + 2, oacc[u][t][2] * inv, oacc[u][t][3] * inv);
+                if (partial) {
+                    float* po = a.part_out + pidx * D + 16 * t + 4 * g;
+                    *(f32x4*)po = f32x4{oacc[u][t][0] * inv, oacc[u][t][1] * inv,
+                                        oacc[u][t][2] * inv, oacc[u][t][3] * inv};
+                } else {
+                    const size_t o = orow[u] + 16 * t + 4 * g;
+                    OUT::store2(a.out, o, oacc[u][t][0] * inv, oacc[u][t][1] * inv);
+                    OUT::store2(a.out, o + 2, oacc[u][t][2] * inv, oacc[u][t][3] * inv);
+                }
+            }
+            if (partial && g == 0) {
+                a.part_max[pidx] = m[u] * kLn2;  // natural-log units
+                a.part_sum[pidx] = tot;
             }
         }
     }
@@ -329,6 +358,9 @@ attn_fn pick_prefill_bs(int bs) {
 template <class KV, class OUT, int NW, int TR>
 attn_fn pick_prefill_d(int d, int bs) {
     if (d == 128) return pick_prefill_bs<KV, OUT, 128, NW, TR>(bs);
+    if constexpr (NW == 4) {
+        if (d == 256) return pick_prefill_bs<KV, OUT, 256, NW, TR>(bs);
+    }
     if (d == 96) return pick_prefill_bs<KV, OUT, 96, NW, TR>(bs);
     if (d == 80) return pick_prefill_bs<KV, OUT, 80, NW, TR>(bs);
     // head_dim 64: 8 rows per wave-load, at most 4 waves for a 32-token chunk

@@ -61,7 +61,7 @@ def _decode(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=112), 4), (dict(D=256), 4), (dict(BS=24), 4), (dict(BS=128), 4), (dict(Hq=6, Hkv=4), 2), (dict(kvdt=2), 3),
+    (dict(D=112), 4), (dict(D=512), 4), (dict(D=256, Hq=34, Hkv=1), 4), (dict(BS=24), 4), (dict(BS=128), 4), (dict(Hq=6, Hkv=4), 2), (dict(kvdt=2), 3),
     (dict(out_dtype=1), 3), (dict(query=None), 1), (dict(kc=(1 << 12) + 4), 7),
     (dict(B=-1), 2), (dict(scale=float("inf")), 2), (dict(NB=0), 2),
 ])

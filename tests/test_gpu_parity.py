@@ -549,9 +549,11 @@ def test_block_sizes_8_and_64_shared_prefix(BS, Hq, Hkv):
     _assert_close(to_host_f64(out), ref, "f32", "prefix BS=%d" % BS)
 
 
-# ---- head_dim 80 and 96 ------------------------------------------------------
-# Laid out as 128 by every kernel: the missing 16-byte slices of a row read
-# as zeros and are never stored.
+# ---- head_dim 80, 96 and 256 ---------------------------------------------------
+# 80 and 96 are laid out as 128 by every kernel: the missing 16-byte slices
+# of a row read as zeros and are never stored. 256 runs the decode paths on
+# the prefill kernel (one new token per sequence, partitions for the split
+# path).
 
 HD_HEADS = [
     # (num_heads, num_kv_heads, dtype, block_size)
@@ -562,10 +564,10 @@ HD_HEADS = [
 ]
 
 
-@pytest.mark.parametrize("D", [80, 96])
+@pytest.mark.parametrize("D", [80, 96, 256])
 @pytest.mark.parametrize("heads", range(len(HD_HEADS)))
 @pytest.mark.parametrize("path", ["single", "split64", "fused128"])
-def test_head_dims_80_and_96(D, heads, path):
+def test_head_dims_80_96_256(D, heads, path):
     Hq, Hkv, dt, BS = HD_HEADS[heads]
     lens = [1, BS, BS + 1, 63, 64, 65, 200, 511, 700]
     need = sum(-(-L // BS) for L in lens)
@@ -587,8 +589,8 @@ def test_head_dims_80_and_96(D, heads, path):
                       "D=%d heads=%s %s" % (D, HD_HEADS[heads], path))
 
 
-@pytest.mark.parametrize("D", [80, 96])
-def test_head_dims_80_and_96_shared_prefix(D):
+@pytest.mark.parametrize("D", [80, 96, 256])
+def test_head_dims_80_96_256_shared_prefix(D):
     P, prefix, suf = 64, 128, [1, 2, 16, 17, 100, 7]
     w = _small("pfxhd%d" % D, num_seqs=len(suf), num_heads=8, num_kv_heads=2, head_dim=D,
                dtype="f16", block_size=16, num_blocks=(prefix + 128 * len(suf)) // 16,

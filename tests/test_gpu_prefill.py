@@ -65,6 +65,8 @@ CASES = [
     (4, 4, 128, "bf16", 32, 64, [1, 130, 64, 17]),       # 8 waves of 16 new tokens
     (8, 8, 80, "f16", 16, 32, [1, 16, 17, 40]),          # head_dim 80, laid out as 128
     (14, 2, 96, "bf16", 16, 48, [3, 20, 9]),             # head_dim 96, 7 heads per kv head
+    (8, 2, 256, "bf16", 16, 64, [1, 17, 70]),            # head_dim 256
+    (4, 4, 256, "f16", 64, 128, [2, 33]),
 ]
 
 
