@@ -192,3 +192,67 @@ def test_swap_out_and_back_keeps_the_table_order():
     gpu.fork("b", "b2")
     with pytest.raises(ValueError):
         gpu.move_out("b2", host)
+
+
+# ---------------------------------------------------------------------------
+# Prefill batches after a prefix-cache hit (lqnn.cn/news/170268 §3.2, §3.4)
+# ---------------------------------------------------------------------------
+
+
+def test_prefill_batch_shares_the_cached_prompt_and_places_new_tokens():
+    w = W.PrefillWorkload("pt", 5, 4, 2, 64, "bf16", 8, 80, 12, 24, "fixed:1")
+    lens = [1, 7, 8, 9, 0]
+    b = W.make_prefill_batch(w, seed=3, lens=lens)
+    C = w.cached_tokens
+    # contexts, query rows and their starts
+    assert list(b.context_lens) == [C + S for S in lens]
+    assert list(b.query_start) == [0, 1, 8, 16, 25, 25]
+    assert b.query.shape == (25, 4, 64) and b.max_query_len == 9
+    # the cached prompt's 3 blocks start every table, the same physical blocks
+    shared = list(b.shared_blocks)
+    assert len(shared) == C // w.block_size
+    for i in range(5):
+        assert list(b.block_tables[i, :3]) == shared
+    # private blocks are distinct across requests and from the prompt's
+    private = [int(x) for i in range(5) for x in b.block_tables[i, 3:] if x >= 0]
+    assert len(private) == len(set(private)) and not set(private) & set(shared)
+    # new token t of request i goes to position C + t of its table
+    for i, S in enumerate(lens):
+        for t in range(S):
+            s = b.slot_mapping[b.query_start[i] + t]
+            assert s == oracle.slot_of_token(b.block_tables[i], C + t, w.block_size)
+    # slots of new tokens hold NaN until written; the prompt holds data
+    kb = b.key_cache.view(np.uint16)
+    for s in b.slot_mapping:
+        assert np.all(kb[s // 8, s % 8] == W.nan_bits("bf16"))
+    assert not np.any(kb[shared] == W.nan_bits("bf16"))
+
+
+def test_prefill_flops_count_the_causal_triangle():
+    w = W.PrefillWorkload("pf", 2, 2, 1, 16, "f16", 4, 16, 8, 8, "fixed:1")
+    b = W.make_prefill_batch(w, seed=0, lens=[1, 3])
+    # request 0: one token at position 8 attends to 9 positions; request 1:
+    # positions 8, 9, 10 attend to 9, 10, 11; 4 flops per head_dim element
+    # and query head
+    assert W.prefill_flops(b) == 4 * (9 + 9 + 10 + 11) * 2 * 16
+    unique, per_request = W.prefill_bytes(b)
+    per_tok = 2 * 1 * 16 * 2
+    qo = 4 * 2 * 16 * (2 + 2)
+    assert per_request == (9 + 11) * per_tok + qo
+    assert unique == (9 + 11 - 8) * per_tok + qo
+
+
+def test_prefill_batch_without_a_cache_hit_has_no_shared_blocks():
+    w = W.PrefillWorkload("pf0", 3, 4, 4, 32, "f16", 16, 16, 4, 0, "fixed:1")
+    b = W.make_prefill_batch(w, seed=1, lens=[5, 16, 17])
+    assert len(b.shared_blocks) == 0
+    assert list(b.context_lens) == [5, 16, 17]
+    used = [int(x) for x in b.block_tables.ravel() if x >= 0]
+    assert len(used) == len(set(used)) == 1 + 1 + 2
+
+
+def test_prefill_workloads_follow_the_page_scenario():
+    for name in ("prefix_prefill", "prefix_prefill_gqa"):
+        w = W.PREFILL_WORKLOADS[name]
+        assert w.num_seqs == 100 and w.cached_tokens == 1488 and w.cached_tokens % w.block_size == 0
+        assert 1488 // w.block_size == 93 and 1500 - 1488 < w.block_size
