@@ -53,8 +53,16 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Waves per SIMD the registers are budgeted for (measured on MI355X: 4
+// rather than the 3 the compiler picks by itself took the 32-head prefill
+// from 487 to 438 µs; 5, for 8-wave workgroups, was slower again).
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU 4
+#endif
+
 template <class KV, class OUT, int D, int BS, int NW, int TR>
-__global__ __launch_bounds__(NW * 64) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_kernel(AttnArgs a) {
     constexpr int CH = 32;         // tokens per chunk
     constexpr int NS = CH / 16;    // 16-token sub-blocks of a chunk
     // head_dim 80 and 96 are laid out as 128: the missing slices read as
