@@ -233,8 +233,9 @@ pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
  * negative, and rows of a sequence with L_i = 0, are zero. Rows past
  * max_query_len of a sequence (a caller error) are not written; the device
  * data query_start and context_lens are not checked. Nothing is allocated;
- * one launch of one workgroup per (sequence, kv head, 16 / G new tokens),
- * each over the whole context on the matrix cores.
+ * one launch, one workgroup per (sequence, kv head, 4 or 8 x 16/G new
+ * tokens) over the whole context on the matrix cores (G = num_heads /
+ * num_kv_heads).
  */
 pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
                      const void* value_cache, const int32_t* block_tables,
