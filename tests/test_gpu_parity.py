@@ -285,8 +285,9 @@ def test_nan_poisoned_tails_do_not_change_bits():
     assert np.array_equal(outs[0], outs[1])
 
 
-def test_exported_lse_merge_matches_oracle_merge():
-    w = _small("merge", num_seqs=4, num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16",
+@pytest.mark.parametrize("D", [64, 80, 96, 128, 256])
+def test_exported_lse_merge_matches_oracle_merge(D):
+    w = _small("merge", num_seqs=4, num_heads=4, num_kv_heads=4, head_dim=D, dtype="f16",
                block_size=16, num_blocks=200, max_blocks_per_seq=48, lens="uniform:1:768")
     b = W.make_batch(w, seed=2, lens=[0, 100, 513, 768])
     kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
@@ -295,7 +296,7 @@ def test_exported_lse_merge_matches_oracle_merge():
                                        "f16", 128, max_partitions=6)
     ref = oracle.lse_merge(m, l, o, b.context_lens, 128)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
-    out = torch.full((4, 4, 64), -7.0, device="cuda")
+    out = torch.full((4, 4, D), -7.0, device="cuda")
     palib.lse_merge(dev(o), dev(m), dev(l), torch.from_numpy(b.context_lens).cuda(), 128, out=out)
     got = out.cpu().numpy().astype(np.float64)
     # sequences with <= 1 partition are left untouched by the merge
