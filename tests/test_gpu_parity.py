@@ -614,6 +614,8 @@ def test_head_dims_80_96_256_shared_prefix(D):
     ("bf16", 300, 16, 40, 128, 120),  # 160 KiB blocks: ten slices
     ("f16", 80, 8, 2, 64, 30),     # 2 KiB blocks
     ("bf16", 40, 64, 8, 128, 15),  # 128 KiB blocks
+    ("f16", 30, 16, 2, 256, 10),   # head_dim 256
+    ("bf16", 30, 32, 3, 80, 12),   # head_dim 80: 15 KiB blocks
 ])
 def test_copy_blocks_bit_exact(dtype, NB, BS, Hkv, D, N):
     rng = np.random.default_rng(NB + N)
