@@ -25,8 +25,13 @@
 // sum over a row's four lanes use the gfx950 lane swaps), and
 // Oᵀ[16 d x 16 rows] += Vᵀ · Pᵀ with Vᵀ read by ds_read_b64_tr_b16 and P
 // split into hi + lo 16-bit halves. Each row is masked to positions up to
-// its own; a wave whose rows all sit before a chunk skips its products (it
-// still loads and waits at the barrier).
+// its own; a wave whose rows all sit before a chunk, or that has no rows,
+// skips its products (it still loads and waits at the barrier).
+//
+// The same kernel has a decode mode (no query_start): one new token per
+// sequence and context partitions with the split path's workspace rows.
+// The decode calls use it at head_dim 256, where it has the registers the
+// head_dim-128 decode kernels lack.
 #pragma once
 
 #include "pa_attn_gqa.h"
@@ -65,8 +70,9 @@ __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_kernel(AttnArgs a) {
     constexpr int CH = 32;         // tokens per chunk
     constexpr int NS = CH / 16;    // 16-token sub-blocks of a chunk
-    // head_dim 80 and 96 are laid out as 128: the missing slices read as
-    // zeros, so they add nothing to q·k and give output columns never stored
+    // head_dim 80 and 96 are laid out as 128 (the missing slices read as
+    // zeros, so they add nothing to q·k and give output columns never
+    // stored); 64, 128 and 256 as themselves
     constexpr int DP = D <= 64 ? 64 : (D <= 128 ? 128 : 256);
     constexpr int NJ = DP / 32;    // q·k products per 16-token sub-block
     constexpr int NT = DP / 16;    // 16-wide output tiles of head_dim
