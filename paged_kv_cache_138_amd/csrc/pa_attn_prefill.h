@@ -185,20 +185,36 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // ---- loads: instruction j of a chunk brings rows j*RPL + wave*RPW + lr,
     // through a descriptor whose range ends at the wave's last valid row (an
     // absent block, or rows at or past `end`, read as zeros) ---------------
+    // The scalar unit issues as much per chunk as the vector units, so the
+    // per-chunk address work is kept to unsigned shifts and 32-bit products
+    // (blocks are below 2^27 bytes) and the table is read unconditionally
+    // at a clamped index.
+    constexpr int LOG_BS = BS == 8 ? 3 : (BS == 16 ? 4 : (BS == 32 ? 5 : 6));
+    static_assert((1 << LOG_BS) == BS, "block size a power of two");
+    const uint32_t nbu = (uint32_t)nb;
+    const uint32_t nb_last = nbu > 0 ? nbu - 1 : 0;  // a table entry that exists
+    const uint32_t row32 = (uint32_t)row_bytes;
+    const uint32_t block32 = (uint32_t)block_bytes;
+    // physical block of logical block lb, or ~0 when absent (past the table
+    // or an id outside the pool)
+    // (bitwise & rather than &&: a short-circuit would make the table read
+    // conditional, a branch)
+    auto block_of = [&](uint32_t lb) -> uint32_t {
+        const uint32_t pid = (uint32_t)bt[lb < nb_last ? lb : nb_last];
+        return ((lb < nbu) & (pid < (uint32_t)a.num_blocks)) ? pid : 0xffffffffu;
+    };
     u32x4 kr[LPC], vr[LPC];
     auto issue = [&](int cs) {
 #pragma unroll
         for (int j = 0; j < LPC; ++j) {
-            const int tok0 = cs + j * RPL + wave * RPW;
-            const int lb = tok0 / BS;
-            const int pid = lb < nb ? bt[lb] : -1;
-            // (a uniform value the compiler would clamp with a vector med3,
-            // which then makes every descriptor a per-lane one)
-            const int rows = __builtin_amdgcn_readfirstlane(min(max(end - tok0, 0), RPW));
-            const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
-            const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
-            const size_t boff =
-                ok ? (size_t)pid * block_bytes + (size_t)(tok0 - lb * BS) * row_bytes : 0;
+            const uint32_t tok0 = (uint32_t)(cs + j * RPL + wave * RPW);
+            const uint32_t pid = block_of(tok0 >> LOG_BS);
+            const int left = end - (int)tok0;  // rows of the wave's load below `end`
+            // no range (and so no access, whatever the base) unless the
+            // block exists and some rows are below `end`
+            const uint32_t keep = 0u - ((uint32_t)(pid != 0xffffffffu) & (uint32_t)(left > 0));
+            const uint32_t nrec = ((uint32_t)(min(left, RPW) - 1) * row32 + D * 2) & keep;
+            const size_t boff = (size_t)pid * block32 + (tok0 & (BS - 1)) * row32;
             kr[j] = buffer_load16(make_rsrc(kbase + boff, nrec), loff);
             vr[j] = buffer_load16(make_rsrc(vbase + boff, nrec), loff);
         }
@@ -216,9 +232,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         uint32_t okm = 0;
 #pragma unroll
         for (int b = 0; b < CH / BSC; ++b) {
-            const int lb = (cs + b * BSC) / BS;
-            const int pid = lb < nb ? bt[lb] : -1;
-            if (pid >= 0 && pid < a.num_blocks) okm |= kBlockBits << (b * BSC);
+            if (block_of((uint32_t)(cs + b * BSC) >> LOG_BS) != 0xffffffffu)
+                okm |= kBlockBits << (b * BSC);
         }
         const int rest = end - cs;
         return rest >= CH ? okm : okm & ((1u << rest) - 1u);
@@ -244,21 +259,24 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                 for (int u = 0; u < TR; ++u) sc[u][s] = Mma<KV>::mma(kv, qb[u][j], sc[u][s]);
             }
         }
-        const uint32_t okl = inside ? 0xffffffffu : okm;
         u32x4 phi[TR], plo[TR];
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
-            // (selects and bitwise ands, no short-circuit: the compiler
-            // would branch on a uniform operand of || and &&)
-            const int limx = inside ? 0x7fffffff : lim[u];
             float sv[4 * NS];
+            if (inside) {  // uniform: no mask at all
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
+                for (int e = 0; e < 4 * NS; ++e) sv[e] = sc[u][e / 4][e % 4] * a.scale_log2;
+            } else {
+                // (selects and bitwise ands, no short-circuit: the compiler
+                // would branch on a uniform operand of || and &&)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int e = 16 * s + 4 * g + k;
-                    const bool ok = (((okl >> e) & 1u) != 0u) & (cs + e <= limx);
-                    sv[4 * s + k] = ok ? sc[u][s][k] * a.scale_log2 : -INFINITY;
+                for (int s = 0; s < NS; ++s) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = 16 * s + 4 * g + k;
+                        const bool ok = (((okm >> e) & 1u) != 0u) & (cs + e <= lim[u]);
+                        sv[4 * s + k] = ok ? sc[u][s][k] * a.scale_log2 : -INFINITY;
+                    }
                 }
             }
             // ---- online softmax of row n ---------------------------------
