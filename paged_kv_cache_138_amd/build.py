@@ -30,6 +30,13 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source flags. The prefill instances assume no NaN operands: their max
+# operations then need no quieting of signalling NaNs (two instructions per
+# max of values the compiler cannot prove canonical); infinities, which the
+# masks use, are still honoured.
+FILE_FLAGS = {"pa_inst_prefill.hip": ["-fno-honor-nans"]}
+
+
 def hipcc():
     h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(h):
@@ -63,7 +70,8 @@ def build(verbose=False, jobs=None, extra_flags=(), out=None):
     for s in srcs:
         o = os.path.join(objdir, os.path.basename(s) + ".o")
         objs.append(o)
-        cmds.append([cc] + DEVICE_FLAGS + list(extra_flags) +
+        cmds.append([cc] + DEVICE_FLAGS + FILE_FLAGS.get(os.path.basename(s), []) +
+                    list(extra_flags) +
                     ["-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o])
     jobs = jobs or min(8, len(cmds))
     with ThreadPoolExecutor(jobs) as ex:

@@ -28,7 +28,7 @@
 //
 // K and V rows reach LDS through the same coalesced loads as the
 // head-per-workgroup kernel (head_dim/8 lanes per row, whole 128-byte lines
-// per request). LDS rows are padded to 2*head_dim + 16 bytes, which spreads
+// per request). LDS rows are padded to 2*head_dim + 32 bytes, which spreads
 // the 16-byte reads of K and the transpose reads of V over the banks. The
 // work decomposition (1 or 2 adjacent kv heads per workgroup), masking by
 // buffer ranges, partitions, the cross-wave merge and the fused append
@@ -63,15 +63,23 @@ struct Mma<KvBF16> {
         *back = __uint_as_float(b << 16);
         return b;
     }
-    // (x0, x1) as packed hi halves, and what is left of each, packed
+    // (x0, x1) as packed hi halves, and what is left of each, packed. The
+    // remainders x - hi are exact in fp32 (hi is x rounded to 8 bits), so
+    // the dot2 form x + (-1)·hi + (-0)·other computes them with no rounding,
+    // one instruction each. (The pairs are (-1, -0) rather than (-1, 0):
+    // the compiler encodes a bf16 pair (-1, 0) as the inline constant -1.0,
+    // which the hardware reads as the fp32 bit pattern, -1 in the upper
+    // half; (-1, -0) is a literal.)
     static __device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi,
                                                   uint32_t* lo) {
         typedef __bf16 b2 __attribute__((ext_vector_type(2)));
         typedef float f2 __attribute__((ext_vector_type(2)));
-        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, b2));
-        const float r0 = x0 - __uint_as_float(h << 16);
-        const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
-        *hi = h;
+        const b2 h = __builtin_convertvector(f2{x0, x1}, b2);
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, b2{(__bf16)-1.0f, (__bf16)-0.0f}, x0,
+                                                         false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, b2{(__bf16)-0.0f, (__bf16)-1.0f}, x1,
+                                                         false);
+        *hi = __builtin_bit_cast(uint32_t, h);
         *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, b2));
     }
 };
@@ -87,14 +95,18 @@ struct Mma<KvF16> {
         *back = (float)h;
         return (uint32_t)__builtin_bit_cast(uint16_t, h);
     }
+    // as for bf16: the remainders are exact, taken by dot2 with (-1, -0)
     static __device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi,
                                                   uint32_t* lo) {
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         typedef float f2 __attribute__((ext_vector_type(2)));
         const h2 h = __builtin_convertvector(f2{x0, x1}, h2);
-        const f2 r = f2{x0, x1} - __builtin_convertvector(h, f2);
+        const float r0 =
+            __builtin_amdgcn_fdot2(h, h2{(_Float16)-1.0f, (_Float16)-0.0f}, x0, false);
+        const float r1 =
+            __builtin_amdgcn_fdot2(h, h2{(_Float16)-0.0f, (_Float16)-1.0f}, x1, false);
         *hi = __builtin_bit_cast(uint32_t, h);
-        *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, h2));
+        *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, h2));
     }
 };
 
@@ -136,7 +148,10 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     constexpr int VL = CH / RPI;        // V loads per chunk
     constexpr int RPB = BS < CH ? BS : CH;  // rows one load descriptor covers
     constexpr int BPC = CH / RPB;       // descriptors per chunk (blocks, or one block's slice)
-    constexpr int ROWB = DP * 2 + 16;   // LDS bytes per K or V row (padding spreads banks)
+    // LDS bytes per K or V row: a 32-byte pad keeps the 16-byte K reads and
+    // the transposed V reads free of bank conflicts (a 16-byte pad left both
+    // 2-way on MI355X)
+    constexpr int ROWB = DP * 2 + 32;
     constexpr int TILE = CH * ROWB;     // LDS bytes of one chunk's K (then V) rows
     constexpr int OROW = DP + 4;        // floats per row of the wave's partial output
     static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");

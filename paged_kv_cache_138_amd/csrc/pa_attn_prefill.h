@@ -65,6 +65,20 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #define PA_PREFILL_WAVES_PER_EU 4
 #endif
 
+// Cache policy of the prefill's K/V loads (0: default, 2: non-temporal).
+// Unlike decode, prefill re-reads a cached prompt shared by many requests
+// (each kv head's prompt blocks by every request's workgroups), and the
+// default policy keeps it in L2: measured on MI355X, the 32-head workload
+// ran 406 µs with non-temporal loads and 321 µs with the default.
+#ifndef PA_PREFILL_LOAD_AUX
+#define PA_PREFILL_LOAD_AUX 0
+#endif
+
+// Chunks of K/V in flight per wave: 1 (one register set) or 2.
+#ifndef PA_PREFILL_DEPTH
+#define PA_PREFILL_DEPTH 2
+#endif
+
 template <class KV, class OUT, int D, int BS, int NW, int TR>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_kernel(AttnArgs a) {
@@ -80,7 +94,11 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     constexpr int RPW = 64 / LPR;  // rows one wave loads per instruction (4 or 8)
     constexpr int RPL = NW * RPW;  // rows the workgroup loads per instruction
     constexpr int LPC = CH / RPL;  // load instructions per chunk, of K and of V
-    constexpr int ROWB = DP * 2 + 16;  // LDS bytes per row (padding spreads banks)
+    // LDS bytes per row: 32 bytes of padding make the 16-byte K reads and
+    // the transposed V reads free of bank conflicts (measured on MI355X,
+    // 16 waves on a CU: 4.4 and 2.6 cycles per instruction; a 16-byte pad
+    // left both 2-way, 8.1 and 4.1)
+    constexpr int ROWB = DP * 2 + 32;
     constexpr int TILE = CH * ROWB;
     constexpr int BSC = BS < CH ? BS : CH;  // tokens of a chunk in one block
     constexpr uint32_t kBlockBits = BSC == 32 ? 0xffffffffu : (1u << BSC) - 1u;
@@ -182,44 +200,100 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         for (int t = 0; t < NT; ++t) oacc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // ---- the scale: scores are kept unscaled and the scale enters the
+    // exponent, exp2(s·c - m) by one fma. c = |scale·log2 e| > 0 (a zero
+    // scale as the smallest normal float: every weight then rounds to
+    // exactly 1, the uniform average a zero scale means); a negative scale
+    // negates q instead, which is exact ----------------------------------
+    const float sl = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+    if (a.scale_log2 < 0.f) {
+#pragma unroll
+        for (int u = 0; u < TR; ++u) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) qb[u][j] ^= 0x80008000u;
+        }
+    }
+
     // ---- loads: instruction j of a chunk brings rows j*RPL + wave*RPW + lr,
     // through a descriptor whose range ends at the wave's last valid row (an
     // absent block, or rows at or past `end`, read as zeros) ---------------
     // The scalar unit issues as much per chunk as the vector units, so the
-    // per-chunk address work is kept to unsigned shifts and 32-bit products
-    // (blocks are below 2^27 bytes) and the table is read unconditionally
-    // at a clamped index.
+    // per-chunk address work is kept small: a chunk's table entries are read
+    // once, together, at clamped indices (chunk starts are multiples of BSC,
+    // partitions being multiples of the block size, so a chunk covers blocks
+    // lb0 .. lb0 + NBC - 1), block offsets use 32-bit products (blocks are
+    // below 2^27 bytes), and what depends only on the wave is computed once.
     constexpr int LOG_BS = BS == 8 ? 3 : (BS == 16 ? 4 : (BS == 32 ? 5 : 6));
     static_assert((1 << LOG_BS) == BS, "block size a power of two");
+    constexpr int NBC = CH / BSC;  // blocks of a chunk
     const uint32_t nbu = (uint32_t)nb;
     const uint32_t nb_last = nbu > 0 ? nbu - 1 : 0;  // a table entry that exists
+    const uint32_t nblk = (uint32_t)a.num_blocks;
     const uint32_t row32 = (uint32_t)row_bytes;
     const uint32_t block32 = (uint32_t)block_bytes;
-    // physical block of logical block lb, or ~0 when absent (past the table
-    // or an id outside the pool)
-    // (bitwise & rather than &&: a short-circuit would make the table read
-    // conditional, a branch)
-    auto block_of = [&](uint32_t lb) -> uint32_t {
-        const uint32_t pid = (uint32_t)bt[lb < nb_last ? lb : nb_last];
-        return ((lb < nbu) & (pid < (uint32_t)a.num_blocks)) ? pid : 0xffffffffu;
-    };
-    u32x4 kr[LPC], vr[LPC];
-    auto issue = [&](int cs) {
+    const int pad = (int)row32 - D * 2;  // bytes from a row's head slice to the next row
+    // per load j: the wave's first row of the chunk, x_j = j*RPL + wave*RPW,
+    // and the bases of its row within a block (for BS = 64 a chunk starts
+    // at row 0 or 32 of its block, added per chunk)
+    const char* kb_j[LPC];
+    const char* vb_j[LPC];
+#pragma unroll
+    for (int j = 0; j < LPC; ++j) {
+        const uint32_t x = (uint32_t)(j * RPL + wave * RPW);
+        const size_t o = (size_t)((BS < CH ? x & (BS - 1) : x) * row32);
+        kb_j[j] = kbase + o;
+        vb_j[j] = vbase + o;
+    }
+    typedef u32x4 Stage[LPC];  // one chunk's rows of this lane, K or V
+    // Issues chunk cs's loads into (kr, vr); returns bit e set when position cs + e lies
+    // in a block of the pool (in decode mode also below `end`, the
+    // partition's end). Rows below `end` lie in blocks below nb (end <= L),
+    // so a block's place in the table needs no test of its own: the row
+    // counts cover it, and in prefill every row's limit is below `end`.
+    // Each select depends on one comparison (the compiler turns a
+    // combination of comparisons into lane masks and several instructions).
+    auto issue = [&](int cs, Stage& kr, Stage& vr) -> uint32_t {
+        const uint32_t lb0 = (uint32_t)cs >> LOG_BS;
+        uint32_t pid[NBC];
+#pragma unroll
+        for (int b = 0; b < NBC; ++b) {
+            const uint32_t lb = lb0 + b;
+            pid[b] = (uint32_t)bt[lb < nb_last ? lb : nb_last];
+        }
+        uint32_t okm = 0;
+#pragma unroll
+        for (int b = 0; b < NBC; ++b) okm |= pid[b] < nblk ? kBlockBits << (b * BSC) : 0u;
+        const int rest = end - cs;  // rows of the chunk below `end`
+        if (dec) okm &= rest >= CH ? 0xffffffffu : (rest > 0 ? (1u << rest) - 1u : 0u);
+        const size_t coff = BS > CH ? (size_t)(((uint32_t)cs & (BS - 1)) * row32) : 0;
 #pragma unroll
         for (int j = 0; j < LPC; ++j) {
-            const uint32_t tok0 = (uint32_t)(cs + j * RPL + wave * RPW);
-            const uint32_t pid = block_of(tok0 >> LOG_BS);
-            const int left = end - (int)tok0;  // rows of the wave's load below `end`
-            // no range (and so no access, whatever the base) unless the
-            // block exists and some rows are below `end`
-            const uint32_t keep = 0u - ((uint32_t)(pid != 0xffffffffu) & (uint32_t)(left > 0));
-            const uint32_t nrec = ((uint32_t)(min(left, RPW) - 1) * row32 + D * 2) & keep;
-            const size_t boff = (size_t)pid * block32 + (tok0 & (BS - 1)) * row32;
-            kr[j] = buffer_load16(make_rsrc(kbase + boff, nrec), loff);
-            vr[j] = buffer_load16(make_rsrc(vbase + boff, nrec), loff);
+            // the load's block within the chunk: fixed when a load's rows
+            // never straddle blocks (BS a multiple of RPL)
+            uint32_t p = pid[0];
+            if constexpr (BS < CH) {
+                if constexpr (BS % RPL == 0) {
+                    p = pid[(j * RPL) >> LOG_BS];
+                } else {
+                    const int bi = (j * RPL + wave * RPW) >> LOG_BS;
+#pragma unroll
+                    for (int b = 1; b < NBC; ++b) p = bi == b ? pid[b] : p;
+                }
+            }
+            // bytes of the wave's rows below `end`, up to the last row's
+            // head slice (none: 0, whatever the base)
+            // (readfirstlane: the compiler would keep it per lane, and a
+            // per-lane range makes it loop over the lanes' values)
+            const int rr = min(rest - (j * RPL + wave * RPW), RPW);
+            const int bytes = max(rr * (int)row32 - pad, 0);
+            const uint32_t nrec = __builtin_amdgcn_readfirstlane(p < nblk ? (uint32_t)bytes : 0u);
+            const size_t boff = (size_t)p * block32 + coff;
+            kr[j] = buffer_load16<PA_PREFILL_LOAD_AUX>(make_rsrc(kb_j[j] + boff, nrec), loff);
+            vr[j] = buffer_load16<PA_PREFILL_LOAD_AUX>(make_rsrc(vb_j[j] + boff, nrec), loff);
         }
+        return okm;
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, const Stage& kr, const Stage& vr) {
 #pragma unroll
         for (int j = 0; j < LPC; ++j) {
             const int row = j * RPL + wave * RPW + lr;
@@ -227,23 +301,19 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             *(u32x4*)(sm_v[buf] + row * ROWB + lc * 16) = vr[j];
         }
     };
-    // bit e: position cs + e is below `end` and its block is in the pool
-    auto present = [&](int cs) -> uint32_t {
-        uint32_t okm = 0;
-#pragma unroll
-        for (int b = 0; b < CH / BSC; ++b) {
-            if (block_of((uint32_t)(cs + b * BSC) >> LOG_BS) != 0xffffffffu)
-                okm |= kBlockBits << (b * BSC);
-        }
-        const int rest = end - cs;
-        return rest >= CH ? okm : okm & ((1u << rest) - 1u);
-    };
 
-    auto compute = [&](int cs, const char* kt, const char* vt) {
-        const uint32_t okm = __builtin_amdgcn_readfirstlane(present(cs));
+    // lane (g, n) holds tokens 16s + 4g + k of row n; dl: row n's limit
+    // less 4g, so that token 16s + k of chunk cs is visible when
+    // 16s + k <= dl - cs
+    int dl[TR];
+#pragma unroll
+    for (int u = 0; u < TR; ++u) dl[u] = lim[u] - 4 * g;
+
+    auto compute = [&](int cs, uint32_t okm, const char* kt, const char* vt) {
+        const bool all = okm == 0xffffffffu;
         // a chunk wholly present and at or before every row's own position
         // needs no mask (most chunks of a long cached prefix)
-        const bool inside = okm == 0xffffffffu && cs + CH - 1 <= first_pos;
+        const bool inside = all & (cs + CH - 1 <= first_pos);
         // ---- scores Sᵀ: lane (g, n) gets row n, tokens 16s + 4g + k; each
         // K operand read from LDS serves every tile of the wave ------------
         f32x4 sc[TR][NS];
@@ -262,32 +332,39 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         u32x4 phi[TR], plo[TR];
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
+            // unscaled scores, -inf where masked (the branches are uniform;
+            // the masks are selects, no short-circuit)
+            // (masked in place, so that every path leaves them in the same
+            // registers)
             float sv[4 * NS];
-            if (inside) {  // uniform: no mask at all
 #pragma unroll
-                for (int e = 0; e < 4 * NS; ++e) sv[e] = sc[u][e / 4][e % 4] * a.scale_log2;
-            } else {
-                // (selects and bitwise ands, no short-circuit: the compiler
-                // would branch on a uniform operand of || and &&)
+            for (int e = 0; e < 4 * NS; ++e) sv[e] = sc[u][e / 4][e % 4];
+            if (!inside) {
+                const int d = dl[u] - cs;
+                if (all) {  // every block present: the row limit alone
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
+                    for (int e = 0; e < 4 * NS; ++e)
+                        sv[e] = (e / 4) * 16 + e % 4 <= d ? sv[e] : -INFINITY;
+                } else {
+                    const uint32_t lm = okm >> (4 * g);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int e = 16 * s + 4 * g + k;
-                        const bool ok = (((okm >> e) & 1u) != 0u) & (cs + e <= lim[u]);
-                        sv[4 * s + k] = ok ? sc[u][s][k] * a.scale_log2 : -INFINITY;
+                    for (int e = 0; e < 4 * NS; ++e) {
+                        const int t = (e / 4) * 16 + e % 4;
+                        const bool ok = (((lm >> t) & 1u) != 0u) & (t <= d);
+                        sv[e] = ok ? sv[e] : -INFINITY;
                     }
                 }
             }
             // ---- online softmax of row n ---------------------------------
             // The reference m moves only when the chunk's max passes it by
-            // more than 8 (log2 units), and then for every row of the tile:
-            // the result is the same for any reference, the weights stay
-            // below 2^8, and most chunks skip rescaling the accumulators.
-            float cm = sv[0];
+            // more than thr (log2 units), and then for every row of the
+            // tile: the result is the same for any reference, the weights
+            // stay below 2^thr, and most chunks skip rescaling the
+            // accumulators.
+            float cr = sv[0];
 #pragma unroll
-            for (int e = 1; e < 4 * NS; ++e) cm = fmaxf(cm, sv[e]);
-            cm = max_over_groups(cm);
+            for (int e = 1; e < 4 * NS; ++e) cr = fmaxf(cr, sv[e]);
+            const float cm = max_over_groups(cr) * sl;
             if (__builtin_amdgcn_ballot_w64(cm > m[u] + thr) != 0) {
                 const float mn = fmaxf(m[u], cm);
                 const float alpha = fast_exp2(m[u] - mn);  // 0 while m is the sentinel
@@ -296,12 +373,12 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
 #pragma unroll
                 for (int t = 0; t < NT; ++t) oacc[u][t] *= alpha;
             }
+            const float nm = -m[u];
             float pr[4 * NS];
 #pragma unroll
-            for (int e = 0; e < 4 * NS; ++e) {
-                pr[e] = fast_exp2(sv[e] - m[u]);
-                lsum[u] += pr[e];
-            }
+            for (int e = 0; e < 4 * NS; ++e) pr[e] = fast_exp2(fmaf(sv[e], sl, nm));
+            static_assert(4 * NS == 8, "the sum below adds eight weights");
+            lsum[u] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
             // Pᵀ operand in hi + lo halves
             uint32_t hw[4], lw[4];
 #pragma unroll
@@ -333,18 +410,55 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // past the last chunk, where their descriptors have no range (zeros, no
     // memory traffic): a load issued on some paths only would make the wait
     // counts of every path assume it absent, and the first product of a
-    // chunk would then wait for the next chunk's loads. ---------------------
+    // chunk would then wait for the next chunk's loads. The table reads of
+    // chunk c + 1 come with its loads, before chunk c's LDS reads, whose
+    // wait counter they share. ---------------------------------------------
     const int nch = (max(end - start, 0) + CH - 1) / CH;
-    issue(start);
-    stash(0);
+#if PA_PREFILL_DEPTH == 1
+    Stage kr, vr;
+    uint32_t okm = issue(start, kr, vr);
+    stash(0, kr, vr);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const int cs = start + c * CH;
-        issue(cs + CH);
-        if (cs < wend) compute(cs, sm_k[c & 1], sm_v[c & 1]);
-        stash((c + 1) & 1);
+        const uint32_t okm_next = issue(cs + CH, kr, vr);
+        if (cs < wend) compute(cs, okm, sm_k[c & 1], sm_v[c & 1]);
+        stash((c + 1) & 1, kr, vr);
         __syncthreads();
+        okm = okm_next;
     }
+#else
+    // Two chunks in flight: register set 0 stages the even chunks, set 1
+    // the odd ones, and the loop is unrolled by two so that both sets and
+    // both LDS buffers are fixed in each half. In step c the loads of chunk
+    // c + 2 are issued, chunk c is computed from LDS, and chunk c + 1
+    // (issued a step earlier) is stored to the other buffer; its wait
+    // leaves chunk c + 2's loads in flight.
+    Stage k0, v0, k1, v1;
+    uint32_t okm0 = issue(start, k0, v0);
+    uint32_t okm1 = issue(start + CH, k1, v1);
+    stash(0, k0, v0);
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+        {
+            const int cs = start + c * CH;
+            const uint32_t okm2 = issue(cs + 2 * CH, k0, v0);
+            if (cs < wend) compute(cs, okm0, sm_k[0], sm_v[0]);
+            stash(1, k1, v1);
+            __syncthreads();
+            okm0 = okm2;
+        }
+        if (c + 1 >= nch) break;
+        {
+            const int cs = start + (c + 1) * CH;
+            const uint32_t okm3 = issue(cs + 2 * CH, k1, v1);
+            if (cs < wend) compute(cs, okm1, sm_k[1], sm_v[1]);
+            stash(0, k0, v0);
+            __syncthreads();
+            okm1 = okm3;
+        }
+    }
+#endif
 
     // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ; in decode
     // mode with several partitions, the partition's row of the workspace --

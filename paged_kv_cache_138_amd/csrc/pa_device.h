@@ -188,8 +188,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 // 2^27 bytes), so the load reads zeros without touching memory.
 constexpr uint32_t kNoSlice = 1u << 27;
 
+template <int AUX = PA_LOAD_AUX>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, PA_LOAD_AUX);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).

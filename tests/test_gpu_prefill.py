@@ -85,6 +85,20 @@ def test_prefill_matches_oracle(case, out_kind):
     _assert_close(to_host_f64(out), ref, "f32" if out_kind == "f32" else dt, "case %d" % case)
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_prefill_negative_and_zero_scale(scale):
+    # the kernel keeps scores unscaled and applies |scale| in the exponent,
+    # negating q for a negative scale; a zero scale gives the plain average
+    lens = [1, 20, 33]
+    b = W.make_prefill_batch(_workload(8, 2, 128, "f16", 16, 48, lens), seed=13, lens=lens)
+    b.scale = scale
+    db = DevicePrefill(b, out_dtype=torch.float32)
+    out = db.step()
+    torch.cuda.synchronize()
+    _, _, ref = _oracle(b)
+    _assert_close(to_host_f64(out), ref, "f32", "scale %g" % scale)
+
+
 def test_prefill_grid_wider_than_the_longest_request():
     # max_query_len may exceed every request's count: the extra tiles exit
     b = W.make_prefill_batch(_workload(8, 2, 128, "bf16", 16, 32, [3, 9]), seed=7, lens=[3, 9])
