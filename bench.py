@@ -63,6 +63,9 @@ def parse():
                          "block copy on the workload's cache shape; swap_blocks: blocks to "
                          "pinned host memory and back; prefill: the prefill after a prefix-cache "
                          "hit (workloads prefix_prefill, prefix_prefill_gqa, prefill_tiny)")
+    ap.add_argument("--prefill-entry", choices=["auto", "shared", "plain"], default="auto",
+                    help="prefill: pa_prefill_shared_prefix over the cached prompt every request "
+                         "shares (auto: when the workload has one) or plain pa_prefill")
     ap.add_argument("--pairs", type=int, default=1024, help="copy_blocks: block pairs per launch")
     ap.add_argument("--ceiling-gib", type=float, default=4.0,
                     help="buffer size of the streaming-read ceiling measurement (0 skips it)")
@@ -427,10 +430,12 @@ def bench_copy_blocks(args):
 
 def bench_prefill(args):
     """The prefill step after a prefix-cache hit: the new tokens' K/V stored
-    by pa_reshape_and_cache, then pa_prefill over the cached prompt blocks
-    and the new tokens. The attention is a matrix-core contraction: its
-    roofline is the dense fp16/bf16 MFMA peak, by the exact causal flop
-    count."""
+    by pa_reshape_and_cache, then the attention over the cached prompt
+    blocks and the new tokens: pa_prefill_shared_prefix when every request's
+    table starts with the same cached prompt blocks (the workload's shared
+    system prompt, declared as shared_prefix_tokens), else pa_prefill. The
+    attention is a matrix-core contraction: its roofline is the dense
+    fp16/bf16 MFMA peak, by the exact causal flop count."""
     import numpy as np
     import torch
     from paged_kv_cache_138_amd import lib as palib
@@ -446,10 +451,14 @@ def bench_prefill(args):
     flops = W.prefill_flops(batch)
     out_dtype = torch.float32 if args.out_dtype == "f32" else None
     unique_bytes, request_bytes = W.prefill_bytes(batch, "f32" if out_dtype is not None else None)
+    shared = (args.prefill_entry == "shared" or
+              (args.prefill_entry == "auto" and w.cached_tokens > 0))
+    ps = w.cached_tokens if shared else None
+    entry = "pa_prefill_shared_prefix" if shared else "pa_prefill"
     stream = torch.cuda.Stream()
     K = args.steps
     with torch.cuda.stream(stream):
-        db = DevicePrefill(batch, out_dtype=out_dtype)
+        db = DevicePrefill(batch, out_dtype=out_dtype, shared_prefix_tokens=ps)
         for _ in range(max(args.warmup, 1)):
             db.step()
         torch.cuda.synchronize()
@@ -483,6 +492,7 @@ def bench_prefill(args):
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "cached_tokens": w.cached_tokens,
                    "new_tokens": T, "max_query_len": batch.max_query_len,
+                   "entry": entry, "shared_prefix_tokens": ps or 0,
                    "out_dtype": args.out_dtype, "seed": args.seed},
         "step_wall_ms": round(wall, 5),
         "new_tokens_per_s": round(T / (ms * 1e-3), 1),
@@ -492,9 +502,10 @@ def bench_prefill(args):
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic("%s/prefill" % w.name),
-                     "kernel": "pa_prefill: %d back-to-back launches between HIP events, "
-                               "avg %.2f us" % (K, attn_ms * 1e3)},
+                     "traffic": stored_traffic("%s/%s" % (w.name, "prefill_shared" if shared
+                                                          else "prefill")),
+                     "kernel": "%s: %d back-to-back launches between HIP events, "
+                               "avg %.2f us" % (entry, K, attn_ms * 1e3)},
         "host_data_generation_s": round(t_gen, 2),
     }
     if args.cpu_seconds > 0:

@@ -245,6 +245,38 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query, const voi
                      float scale, pa_dtype kv_dtype, void* stream);
 
 /*
+ * pa_prefill_shared_prefix - pa_prefill for sequences whose contexts start
+ * with the same cached blocks, e.g. requests that share a system prompt
+ * (lqnn.cn/news/170268 §3.4 and §4.3: many requests hit the same cached
+ * prompt blocks, the shared blocks counted once).
+ *
+ * Same arguments and result as pa_prefill (up to rounding order), plus:
+ *   shared_prefix_tokens  positions every sequence shares, a multiple of
+ *                     block_size and at most max_blocks_per_seq * block_size;
+ *                     0 is allowed (nothing shared).
+ * The new tokens of all sequences form one list of rows; a workgroup takes
+ * 4 or 8 x 16/G consecutive rows, whichever sequences they belong to, reads
+ * the shared positions once for all of them (through row 0 of
+ * block_tables), then each of its sequences' own positions past the prefix
+ * for that sequence's rows. Without sharing the shared blocks are read once
+ * per sequence and kv head instead, and a sequence whose new tokens do not
+ * fill its workgroups leaves waves idle.
+ * Caller contract (not checked on the device): for every sequence i,
+ * block_tables[i][j] == block_tables[0][j] for
+ * j < shared_prefix_tokens / block_size, and context_lens[i] >=
+ * shared_prefix_tokens. max_query_len is not used for the grid (num_tokens
+ * is). One launch; nothing is allocated.
+ */
+pa_status pa_prefill_shared_prefix(void* out, pa_dtype out_dtype, const void* query,
+                                   const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* query_start, int num_seqs, int num_tokens,
+                                   int max_query_len, int num_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int max_blocks_per_seq,
+                                   int num_blocks, float scale, pa_dtype kv_dtype,
+                                   int shared_prefix_tokens, void* stream);
+
+/*
  * pa_decode_split_append - one decode step's scatter and attention in the
  * launches of pa_decode_split ("vLLM PagedAttention深度解析与工程实践" §二:
  * each step appends the new token's K/V, then attends over the sequence).

@@ -34,7 +34,8 @@ DEVICE_FLAGS = [
 # operations then need no quieting of signalling NaNs (two instructions per
 # max of values the compiler cannot prove canonical); infinities, which the
 # masks use, are still honoured.
-FILE_FLAGS = {"pa_inst_prefill.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"pa_inst_prefill.hip": ["-fno-honor-nans"],
+              "pa_inst_prefill_shared.hip": ["-fno-honor-nans"]}
 
 
 def hipcc():

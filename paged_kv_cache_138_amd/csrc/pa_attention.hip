@@ -694,3 +694,48 @@ extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(waves * 64), 0, (hipStream_t)stream, a);
     return check_launch("pa_prefill");
 }
+
+#ifndef PA_PREFILL_SHARED_WAVES
+#define PA_PREFILL_SHARED_WAVES 8
+#endif
+
+extern "C" pa_status pa_prefill_shared_prefix(
+    void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
+    const void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start, int num_seqs, int num_tokens, int max_query_len, int num_heads,
+    int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+    float scale, pa_dtype kv_dtype, int shared_prefix_tokens, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                   context_lens, s, scale, kv_dtype);
+    if (st != PA_OK) return st;
+    PA_REQUIRE(num_tokens >= 0 && max_query_len >= 0, PA_ERR_SHAPE,
+               "num_tokens and max_query_len must be >= 0");
+    PA_REQUIRE(max_query_len <= (int64_t)max_blocks_per_seq * block_size, PA_ERR_SHAPE,
+               "max_query_len %d exceeds the longest context %d", max_query_len,
+               max_blocks_per_seq * block_size);
+    PA_REQUIRE(shared_prefix_tokens >= 0 && shared_prefix_tokens % block_size == 0 &&
+                   shared_prefix_tokens <= (int64_t)max_blocks_per_seq * block_size,
+               PA_ERR_SHAPE,
+               "shared_prefix_tokens %d must be a multiple of block_size %d within "
+               "max_blocks_per_seq * block_size", shared_prefix_tokens, block_size);
+    const int G = num_heads / num_kv_heads;
+    PA_REQUIRE(G <= 16, PA_ERR_UNSUPPORTED,
+               "prefill takes at most 16 query heads per kv head (got %d)", G);
+    if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+    PA_REQUIRE(query_start, PA_ERR_NULL, "null query_start");
+    const int waves = head_dim == 128 ? PA_PREFILL_SHARED_WAVES : 4;
+    attn_fn fn = pick_prefill_shared_kernel(kv_dtype, out_dtype, head_dim, block_size, waves);
+    PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
+    AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
+                           scale);
+    a.query_start = query_start;
+    a.prefix_tokens = shared_prefix_tokens;
+    const int rows = waves * (16 / G);  // new tokens per workgroup
+    const int64_t grid = (int64_t)ceil_div(num_tokens, rows) * num_kv_heads;
+    PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(waves * 64), 0, (hipStream_t)stream, a);
+    return check_launch("pa_prefill_shared_prefix");
+}

@@ -79,7 +79,19 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #define PA_PREFILL_DEPTH 2
 #endif
 
-template <class KV, class OUT, int D, int BS, int NW, int TR>
+// Finds the request of flattened new token tok: the last r < num_seqs with
+// query_start[r] <= tok (requests without new tokens are passed over).
+__device__ __forceinline__ int request_of(const int32_t* qs, int num_seqs, int tok) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qs[mid] <= tok) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <class KV, class OUT, int D, int BS, int NW, int TR, bool SH>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_kernel(AttnArgs a) {
     constexpr int CH = 32;         // tokens per chunk
@@ -127,49 +139,97 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // partition_size whose (max, sum, normalised output) go to the split
     // workspace when a sequence has several; the grid's second coordinate
     // is then the partition instead of the tile of new tokens.
-    const bool dec = a.query_start == nullptr;
-    int bid = blockIdx.x;  // kv head fastest, then token tile (partition), then sequence
-    const int kvh = bid % Hkv;
-    bid /= Hkv;
-    const int tile = dec ? 0 : bid % a.num_q_tiles;
-    const int part = dec ? bid % a.num_q_tiles : 0;
-    const int seq = bid / a.num_q_tiles;
-    const int qb0 = dec ? seq : a.query_start[seq];
-    const int S = dec ? 1 : a.query_start[seq + 1] - qb0;
-    const int t0 = tile * NW * TR * R;  // the workgroup's first new token
-    if (t0 >= S) return;                // uniform over the workgroup
-    int L = a.context_lens[seq];
-    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-    const int P = a.partition_size;
-    const int nparts = dec ? (L + P - 1) / P : 1;
-    if (part > 0 && part >= nparts) return;  // uniform over the workgroup
-    const int start = part * P;
-    // positions the workgroup reads: up to its last row's own position
-    const int end = min(max(min(L, L - S + t0 + min(NW * TR * R, S - t0)), 0),
-                        dec ? start + P : L);
-    // this wave's tiles: tile u holds new tokens tw + u*R .. + R - 1
-    const int tw = t0 + wave * TR * R;
-    const int nq = max(min(TR * R, S - tw), 0);  // new tokens of the wave
-    const int wend = nq > 0 ? max(min(L, L - S + tw + nq), 0) : 0;  // 0: no rows
-    const int first_pos = L - S + tw;  // position of the wave's first row
-    const int head = kvh * G + n % G;
+    const bool dec = !SH && a.query_start == nullptr;
+    int kvh, seq = 0, part = 0, qb0 = 0, S = 0, L = 0, start = 0, end = 0, tw, wend = 0,
+        first_pos;
+    int nparts = 1;
     bool rowv[TR];
-    int lim[TR];       // last position row n of tile u attends to (-1: padding row)
+    int lim[TR];  // last position row n of tile u attends to (-1: padding row)
+    int rq[TR];   // shared-prefix mode: the request of row n of tile u
     size_t orow[TR];
+    // shared-prefix mode: the prefix, the workgroup's requests
+    int ps = 0, r_lo = 0, r_hi = -1;
+    if constexpr (!SH) {
+        // Decode mode (no query_start): one new token per sequence, query
+        // and out rows indexed by sequence, the context split into
+        // partitions of partition_size whose (max, sum, normalised output)
+        // go to the split workspace when a sequence has several; the
+        // grid's second coordinate is then the partition instead of the
+        // tile of new tokens.
+        int bid = blockIdx.x;  // kv head fastest, then token tile (partition), then sequence
+        kvh = bid % Hkv;
+        bid /= Hkv;
+        const int tile = dec ? 0 : bid % a.num_q_tiles;
+        part = dec ? bid % a.num_q_tiles : 0;
+        seq = bid / a.num_q_tiles;
+        qb0 = dec ? seq : a.query_start[seq];
+        S = dec ? 1 : a.query_start[seq + 1] - qb0;
+        const int t0 = tile * NW * TR * R;  // the workgroup's first new token
+        if (t0 >= S) return;                // uniform over the workgroup
+        L = a.context_lens[seq];
+        L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+        const int P = a.partition_size;
+        nparts = dec ? (L + P - 1) / P : 1;
+        if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+        start = part * P;
+        // positions the workgroup reads: up to its last row's own position
+        end = min(max(min(L, L - S + t0 + min(NW * TR * R, S - t0)), 0), dec ? start + P : L);
+        // this wave's tiles: tile u holds new tokens tw + u*R .. + R - 1
+        tw = t0 + wave * TR * R;
+        const int nq = max(min(TR * R, S - tw), 0);  // new tokens of the wave
+        wend = nq > 0 ? max(min(L, L - S + tw + nq), 0) : 0;  // 0: no rows
+        first_pos = L - S + tw;  // position of the wave's first row
 #pragma unroll
-    for (int u = 0; u < TR; ++u) {
-        const int tok = tw + u * R + n / G;  // the new token of row n
-        rowv[u] = n < R * G && tok < S;
-        lim[u] = rowv[u] ? L - S + tok : -1;
-        orow[u] = ((size_t)(qb0 + (rowv[u] ? tok : 0)) * Hq + head) * D;
+        for (int u = 0; u < TR; ++u) {
+            const int tok = tw + u * R + n / G;  // the new token of row n
+            rowv[u] = n < R * G && tok < S;
+            lim[u] = rowv[u] ? L - S + tok : -1;
+            rq[u] = seq;
+            orow[u] = ((size_t)(qb0 + (rowv[u] ? tok : 0)) * Hq + kvh * G + n % G) * D;
+        }
+    } else {
+        // Shared-prefix mode: the new tokens of all requests are one list of
+        // rows (query_start[num_seqs] of them); a workgroup takes NW*TR*R
+        // consecutive tokens, whatever their requests. The first ps
+        // positions are the same blocks for every request (read through
+        // block_tables row 0): the workgroup streams them once for all its
+        // rows, then each of its requests' own positions ps .. L_r - 1 for
+        // that request's rows.
+        const int32_t* qs = a.query_start;
+        const int B = a.num_seqs;
+        const int T = qs[B];
+        kvh = blockIdx.x % Hkv;
+        const int t0 = (blockIdx.x / Hkv) * NW * TR * R;
+        if (t0 >= T) return;  // uniform over the workgroup
+        ps = min(a.prefix_tokens, Lmax);
+        r_lo = __builtin_amdgcn_readfirstlane(request_of(qs, B, t0));
+        r_hi = __builtin_amdgcn_readfirstlane(request_of(qs, B, min(t0 + NW * TR * R, T) - 1));
+        tw = t0 + wave * TR * R;
+        int lo_pos = 0x7fffffff;
+#pragma unroll
+        for (int u = 0; u < TR; ++u) {
+            const int tok = tw + u * R + n / G;
+            rowv[u] = n < R * G && tok < T;
+            const int r = request_of(qs, B, rowv[u] ? tok : t0);
+            int Lr = a.context_lens[r];
+            Lr = Lr < 0 ? 0 : (Lr > Lmax ? Lmax : Lr);
+            const int pos = Lr - (qs[r + 1] - qs[r]) + (tok - qs[r]);
+            lim[u] = rowv[u] ? pos : -1;
+            rq[u] = r;
+            orow[u] = ((size_t)(rowv[u] ? tok : 0) * Hq + kvh * G + n % G) * D;
+            if (rowv[u]) lo_pos = min(lo_pos, pos);
+        }
+        // the wave's smallest row position (prefix chunks at or before it
+        // need no mask)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) lo_pos = min(lo_pos, __shfl_xor(lo_pos, o));
+        first_pos = __builtin_amdgcn_readfirstlane(lo_pos);
     }
-
+    const int head = kvh * G + n % G;
     const size_t row_bytes = (size_t)Hkv * D * 2;
     const size_t block_bytes = row_bytes * BS;
     const char* kbase = (const char*)a.key_cache + (size_t)kvh * D * 2;
     const char* vbase = (const char*)a.value_cache + (size_t)kvh * D * 2;
-    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-    const int nb = (L + BS - 1) / BS;
     const uint32_t loff = (uint32_t)(lr * row_bytes) + (lc * 8 < D ? (uint32_t)(lc * 16) : kNoSlice);
 
     // Qᵀ operands: lane (g, n) holds row n's q[32j + 8g .. +7]; padding rows are 0
@@ -226,8 +286,6 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     constexpr int LOG_BS = BS == 8 ? 3 : (BS == 16 ? 4 : (BS == 32 ? 5 : 6));
     static_assert((1 << LOG_BS) == BS, "block size a power of two");
     constexpr int NBC = CH / BSC;  // blocks of a chunk
-    const uint32_t nbu = (uint32_t)nb;
-    const uint32_t nb_last = nbu > 0 ? nbu - 1 : 0;  // a table entry that exists
     const uint32_t nblk = (uint32_t)a.num_blocks;
     const uint32_t row32 = (uint32_t)row_bytes;
     const uint32_t block32 = (uint32_t)block_bytes;
@@ -245,26 +303,32 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         vb_j[j] = vbase + o;
     }
     typedef u32x4 Stage[LPC];  // one chunk's rows of this lane, K or V
-    // Issues chunk cs's loads into (kr, vr); returns bit e set when position cs + e lies
-    // in a block of the pool (in decode mode also below `end`, the
-    // partition's end). Rows below `end` lie in blocks below nb (end <= L),
-    // so a block's place in the table needs no test of its own: the row
-    // counts cover it, and in prefill every row's limit is below `end`.
+    // Issues the loads of chunk cs of a stream of positions below tend whose
+    // table tb has tnb entries, into (kr, vr); returns bit e set when
+    // position cs + e lies in a block of the pool (in decode mode and in
+    // shared-prefix mode also below tend). Rows below tend lie in blocks
+    // below tnb, so a block's place in the table needs no test of its own:
+    // the row counts cover it.
     // Each select depends on one comparison (the compiler turns a
     // combination of comparisons into lane masks and several instructions).
-    auto issue = [&](int cs, Stage& kr, Stage& vr) -> uint32_t {
+    auto issue = [&](int cs, const int32_t* tb, int tnb, int tend, Stage& kr,
+                     Stage& vr) -> uint32_t {
         const uint32_t lb0 = (uint32_t)cs >> LOG_BS;
+        const uint32_t last = tnb > 0 ? (uint32_t)tnb - 1 : 0;  // a table entry that exists
         uint32_t pid[NBC];
 #pragma unroll
         for (int b = 0; b < NBC; ++b) {
             const uint32_t lb = lb0 + b;
-            pid[b] = (uint32_t)bt[lb < nb_last ? lb : nb_last];
+            pid[b] = (uint32_t)tb[lb < last ? lb : last];
         }
         uint32_t okm = 0;
 #pragma unroll
         for (int b = 0; b < NBC; ++b) okm |= pid[b] < nblk ? kBlockBits << (b * BSC) : 0u;
-        const int rest = end - cs;  // rows of the chunk below `end`
-        if (dec) okm &= rest >= CH ? 0xffffffffu : (rest > 0 ? (1u << rest) - 1u : 0u);
+        const int rest = tend - cs;  // rows of the chunk below tend
+        // (per-request prefill: every row's limit is below tend; not so in
+        // decode mode, nor for the shared prefix, which ends where each
+        // request's own positions begin)
+        if (dec || SH) okm &= rest >= CH ? 0xffffffffu : (rest > 0 ? (1u << rest) - 1u : 0u);
         const size_t coff = BS > CH ? (size_t)(((uint32_t)cs & (BS - 1)) * row32) : 0;
 #pragma unroll
         for (int j = 0; j < LPC; ++j) {
@@ -309,11 +373,13 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
 #pragma unroll
     for (int u = 0; u < TR; ++u) dl[u] = lim[u] - 4 * g;
 
-    auto compute = [&](int cs, uint32_t okm, const char* kt, const char* vt) {
+    // rseg: shared-prefix mode, the request whose own positions the chunk
+    // holds (its rows alone attend to it), or -1 for the shared prefix
+    auto compute = [&](int cs, int rseg, uint32_t okm, const char* kt, const char* vt) {
         const bool all = okm == 0xffffffffu;
         // a chunk wholly present and at or before every row's own position
         // needs no mask (most chunks of a long cached prefix)
-        const bool inside = all & (cs + CH - 1 <= first_pos);
+        const bool inside = all & (cs + CH - 1 <= first_pos) & (rseg < 0);
         // ---- scores Sᵀ: lane (g, n) gets row n, tokens 16s + 4g + k; each
         // K operand read from LDS serves every tile of the wave ------------
         f32x4 sc[TR][NS];
@@ -340,7 +406,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
 #pragma unroll
             for (int e = 0; e < 4 * NS; ++e) sv[e] = sc[u][e / 4][e % 4];
             if (!inside) {
-                const int d = dl[u] - cs;
+                int d = dl[u] - cs;
+                if constexpr (SH) d = ((rseg < 0) | (rq[u] == rseg)) ? d : -1;
                 if (all) {  // every block present: the row limit alone
 #pragma unroll
                     for (int e = 0; e < 4 * NS; ++e)
@@ -413,52 +480,120 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // chunk would then wait for the next chunk's loads. The table reads of
     // chunk c + 1 come with its loads, before chunk c's LDS reads, whose
     // wait counter they share. ---------------------------------------------
-    const int nch = (max(end - start, 0) + CH - 1) / CH;
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    const int nb = (L + BS - 1) / BS;
+    if constexpr (!SH) {
+        const int nch = (max(end - start, 0) + CH - 1) / CH;
 #if PA_PREFILL_DEPTH == 1
-    Stage kr, vr;
-    uint32_t okm = issue(start, kr, vr);
-    stash(0, kr, vr);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        const int cs = start + c * CH;
-        const uint32_t okm_next = issue(cs + CH, kr, vr);
-        if (cs < wend) compute(cs, okm, sm_k[c & 1], sm_v[c & 1]);
-        stash((c + 1) & 1, kr, vr);
+        Stage kr, vr;
+        uint32_t okm = issue(start, bt, nb, end, kr, vr);
+        stash(0, kr, vr);
         __syncthreads();
-        okm = okm_next;
-    }
-#else
-    // Two chunks in flight: register set 0 stages the even chunks, set 1
-    // the odd ones, and the loop is unrolled by two so that both sets and
-    // both LDS buffers are fixed in each half. In step c the loads of chunk
-    // c + 2 are issued, chunk c is computed from LDS, and chunk c + 1
-    // (issued a step earlier) is stored to the other buffer; its wait
-    // leaves chunk c + 2's loads in flight.
-    Stage k0, v0, k1, v1;
-    uint32_t okm0 = issue(start, k0, v0);
-    uint32_t okm1 = issue(start + CH, k1, v1);
-    stash(0, k0, v0);
-    __syncthreads();
-    for (int c = 0; c < nch; c += 2) {
-        {
+        for (int c = 0; c < nch; ++c) {
             const int cs = start + c * CH;
-            const uint32_t okm2 = issue(cs + 2 * CH, k0, v0);
-            if (cs < wend) compute(cs, okm0, sm_k[0], sm_v[0]);
-            stash(1, k1, v1);
+            const uint32_t okm_next = issue(cs + CH, bt, nb, end, kr, vr);
+            if (cs < wend) compute(cs, -1, okm, sm_k[c & 1], sm_v[c & 1]);
+            stash((c + 1) & 1, kr, vr);
             __syncthreads();
-            okm0 = okm2;
+            okm = okm_next;
         }
-        if (c + 1 >= nch) break;
-        {
-            const int cs = start + (c + 1) * CH;
-            const uint32_t okm3 = issue(cs + 2 * CH, k1, v1);
-            if (cs < wend) compute(cs, okm1, sm_k[1], sm_v[1]);
-            stash(0, k0, v0);
-            __syncthreads();
-            okm1 = okm3;
+#else
+        // Two chunks in flight: register set 0 stages the even chunks, set
+        // 1 the odd ones, and the loop is unrolled by two so that both sets
+        // and both LDS buffers are fixed in each half. In step c the loads
+        // of chunk c + 2 are issued, chunk c is computed from LDS, and
+        // chunk c + 1 (issued a step earlier) is stored to the other
+        // buffer; its wait leaves chunk c + 2's loads in flight.
+        Stage k0, v0, k1, v1;
+        uint32_t okm0 = issue(start, bt, nb, end, k0, v0);
+        uint32_t okm1 = issue(start + CH, bt, nb, end, k1, v1);
+        stash(0, k0, v0);
+        __syncthreads();
+        for (int c = 0; c < nch; c += 2) {
+            {
+                const int cs = start + c * CH;
+                const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0);
+                if (cs < wend) compute(cs, -1, okm0, sm_k[0], sm_v[0]);
+                stash(1, k1, v1);
+                __syncthreads();
+                okm0 = okm2;
+            }
+            if (c + 1 >= nch) break;
+            {
+                const int cs = start + (c + 1) * CH;
+                const uint32_t okm3 = issue(cs + 2 * CH, bt, nb, end, k1, v1);
+                if (cs < wend) compute(cs, -1, okm1, sm_k[1], sm_v[1]);
+                stash(0, k0, v0);
+                __syncthreads();
+                okm1 = okm3;
+            }
+        }
+#endif
+    } else {
+        // The workgroup's streams, one after another: the shared prefix
+        // (positions 0 .. ps - 1, table row 0), then for each of its
+        // requests r with positions past the prefix, positions ps .. L_r - 1
+        // of r's table. A cursor is one chunk of one stream; a finished
+        // cursor (r = kDone) has no positions and loads nothing.
+        constexpr int kDone = 0x3fffffff;
+        struct Cur {
+            int r, cs, end, nb;
+            const int32_t* tb;
+        };
+        const int32_t* qs = a.query_start;
+        // the first stream of request r or a later one of the workgroup
+        auto stream_from = [&](int r) -> Cur {
+            for (; r <= r_hi; ++r) {
+                int Lr = a.context_lens[r];
+                Lr = Lr < 0 ? 0 : (Lr > Lmax ? Lmax : Lr);
+                if (qs[r + 1] > qs[r] && Lr > ps)
+                    return Cur{r, ps, Lr, (Lr + BS - 1) / BS,
+                               a.block_tables + (size_t)r * a.max_blocks_per_seq};
+            }
+            return Cur{kDone, 0, 0, 1, a.block_tables};
+        };
+        auto next = [&](Cur c) -> Cur {
+            c.cs += CH;
+            if (c.cs < c.end || c.r == kDone) return c;
+            return stream_from(c.r < 0 ? r_lo : c.r + 1);
+        };
+        // does a row of this wave attend to a position of chunk c
+        auto wanted = [&](const Cur& c) -> bool {
+            bool any = false;
+#pragma unroll
+            for (int u = 0; u < TR; ++u)
+                any |= ((c.r < 0) | (rq[u] == c.r)) & (lim[u] >= c.cs);
+            return __builtin_amdgcn_ballot_w64(any) != 0;
+        };
+        Cur c0 = ps > 0 ? Cur{-1, 0, ps, ps / BS, a.block_tables} : stream_from(r_lo);
+        Cur c1 = next(c0);
+        Stage k0, v0, k1, v1;
+        uint32_t okm0 = issue(c0.cs, c0.tb, c0.nb, c0.end, k0, v0);
+        uint32_t okm1 = issue(c1.cs, c1.tb, c1.nb, c1.end, k1, v1);
+        stash(0, k0, v0);
+        __syncthreads();
+        while (c0.r != kDone) {
+            const Cur c2 = next(c1);
+            {
+                const uint32_t okm2 = issue(c2.cs, c2.tb, c2.nb, c2.end, k0, v0);
+                if (wanted(c0)) compute(c0.cs, c0.r, okm0, sm_k[0], sm_v[0]);
+                stash(1, k1, v1);
+                __syncthreads();
+                okm0 = okm2;
+            }
+            if (c1.r == kDone) break;
+            const Cur c3 = next(c2);
+            {
+                const uint32_t okm3 = issue(c3.cs, c3.tb, c3.nb, c3.end, k1, v1);
+                if (wanted(c1)) compute(c1.cs, c1.r, okm1, sm_k[1], sm_v[1]);
+                stash(0, k0, v0);
+                __syncthreads();
+                okm1 = okm3;
+            }
+            c0 = c2;
+            c1 = c3;
         }
     }
-#endif
 
     // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ; in decode
     // mode with several partitions, the partition's row of the workspace --
@@ -490,38 +625,38 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     }
 }
 
-template <class KV, class OUT, int D, int NW, int TR>
+template <class KV, class OUT, int D, int NW, int TR, bool SH>
 attn_fn pick_prefill_bs(int bs) {
     switch (bs) {
-        case 8: return attn_prefill_kernel<KV, OUT, D, 8, NW, TR>;
-        case 16: return attn_prefill_kernel<KV, OUT, D, 16, NW, TR>;
-        case 32: return attn_prefill_kernel<KV, OUT, D, 32, NW, TR>;
-        case 64: return attn_prefill_kernel<KV, OUT, D, 64, NW, TR>;
+        case 8: return attn_prefill_kernel<KV, OUT, D, 8, NW, TR, SH>;
+        case 16: return attn_prefill_kernel<KV, OUT, D, 16, NW, TR, SH>;
+        case 32: return attn_prefill_kernel<KV, OUT, D, 32, NW, TR, SH>;
+        case 64: return attn_prefill_kernel<KV, OUT, D, 64, NW, TR, SH>;
     }
     return nullptr;
 }
 
-template <class KV, class OUT, int NW, int TR>
+template <class KV, class OUT, int NW, int TR, bool SH>
 attn_fn pick_prefill_d(int d, int bs) {
-    if (d == 128) return pick_prefill_bs<KV, OUT, 128, NW, TR>(bs);
+    if (d == 128) return pick_prefill_bs<KV, OUT, 128, NW, TR, SH>(bs);
     if constexpr (NW == 4) {
-        if (d == 256) return pick_prefill_bs<KV, OUT, 256, NW, TR>(bs);
+        if (d == 256) return pick_prefill_bs<KV, OUT, 256, NW, TR, SH>(bs);
     }
-    if (d == 96) return pick_prefill_bs<KV, OUT, 96, NW, TR>(bs);
-    if (d == 80) return pick_prefill_bs<KV, OUT, 80, NW, TR>(bs);
+    if (d == 96) return pick_prefill_bs<KV, OUT, 96, NW, TR, SH>(bs);
+    if (d == 80) return pick_prefill_bs<KV, OUT, 80, NW, TR, SH>(bs);
     // head_dim 64: 8 rows per wave-load, at most 4 waves for a 32-token chunk
     if constexpr (NW <= 4) {
-        if (d == 64) return pick_prefill_bs<KV, OUT, 64, NW, TR>(bs);
+        if (d == 64) return pick_prefill_bs<KV, OUT, 64, NW, TR, SH>(bs);
     }
     return nullptr;
 }
 
-template <class KV, int NW, int TR>
+template <class KV, int NW, int TR, bool SH>
 attn_fn pick_prefill_out(pa_dtype out, pa_dtype kv, int d, int bs) {
-    if (out == PA_F32) return pick_prefill_d<KV, OutF32, NW, TR>(d, bs);
+    if (out == PA_F32) return pick_prefill_d<KV, OutF32, NW, TR, SH>(d, bs);
     if (out != kv) return nullptr;
-    if (kv == PA_F16) return pick_prefill_d<KV, OutF16, NW, TR>(d, bs);
-    return pick_prefill_d<KV, OutBF16, NW, TR>(d, bs);
+    if (kv == PA_F16) return pick_prefill_d<KV, OutF16, NW, TR, SH>(d, bs);
+    return pick_prefill_d<KV, OutBF16, NW, TR, SH>(d, bs);
 }
 
 }  // namespace pa

@@ -33,5 +33,8 @@ attn_fn pick_prefix_kernel(pa_dtype kv, pa_dtype out, int d, int bs);   // pa_in
 // prefill kernel with `waves` (4 or 8) wavefronts of 16 rows per workgroup
 attn_fn pick_prefill_kernel(pa_dtype kv, pa_dtype out, int d, int bs,
                             int waves);  // pa_inst_prefill.hip
+// the same kernel in shared-prefix mode (rows of every request in one list)
+attn_fn pick_prefill_shared_kernel(pa_dtype kv, pa_dtype out, int d, int bs,
+                                   int waves);  // pa_inst_prefill_shared.hip
 
 }  // namespace pa

@@ -54,6 +54,9 @@ def load():
     lib.pa_prefill.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                i32, i32, f32, i32, vp]
     lib.pa_prefill.restype = i32
+    lib.pa_prefill_shared_prefix.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                             i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.pa_prefill_shared_prefix.restype = i32
     lib.pa_decode.restype = i32
     lib.pa_decode_split.argtypes = dec + [i32, vp, sz, vp]
     lib.pa_decode_split.restype = i32
@@ -225,12 +228,15 @@ def decode(query, key_cache, value_cache, block_tables, context_lens, scale, out
 
 
 def prefill(query, key_cache, value_cache, block_tables, context_lens, query_start, scale,
-            max_query_len, out=None, out_dtype=None):
+            max_query_len, out=None, out_dtype=None, shared_prefix_tokens=None):
     """Causal attention of the new tokens query [T, Hq, D] (sequence i owns
     rows query_start[i] .. query_start[i+1] - 1, the last positions of its
     context_lens[i] tokens, whose K/V are already cached) over each
     sequence's paged context; returns out [T, Hq, D]. max_query_len bounds
-    every sequence's new-token count; see pa_prefill."""
+    every sequence's new-token count; see pa_prefill. With
+    shared_prefix_tokens set, pa_prefill_shared_prefix: every sequence's
+    first shared_prefix_tokens positions are the blocks of row 0 of
+    block_tables."""
     _on_gpu(query, key_cache, value_cache, block_tables, context_lens, query_start)
     _kv_checks(query, key_cache, value_cache)
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.is_contiguous(),
@@ -250,11 +256,14 @@ def prefill(query, key_cache, value_cache, block_tables, context_lens, query_sta
     _on_gpu(query, out)
     _need(out.shape == (T, Hq, D) and out.is_contiguous(), "out must be a contiguous [T, Hq, D] tensor")
     _need(out.dtype in _DT, "unsupported out dtype")
-    st = load().pa_prefill(_ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache), _ptr(value_cache),
-                           _ptr(block_tables), _ptr(context_lens), _ptr(query_start), B, T,
-                           int(max_query_len), Hq, Hkv, D, BS, block_tables.shape[1], NB,
-                           float(scale), _DT[key_cache.dtype], _stream(query))
-    _check(st, "pa_prefill")
+    args = (_ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache), _ptr(value_cache),
+            _ptr(block_tables), _ptr(context_lens), _ptr(query_start), B, T, int(max_query_len),
+            Hq, Hkv, D, BS, block_tables.shape[1], NB, float(scale), _DT[key_cache.dtype])
+    if shared_prefix_tokens is None:
+        _check(load().pa_prefill(*args, _stream(query)), "pa_prefill")
+    else:
+        _check(load().pa_prefill_shared_prefix(*args, int(shared_prefix_tokens), _stream(query)),
+               "pa_prefill_shared_prefix")
     return out
 
 

@@ -173,9 +173,13 @@ class DevicePrefill:
     K/V into their slots (pa_reshape_and_cache), then runs pa_prefill: the
     new tokens attend over the cached prompt blocks and themselves, causally
     (lqnn.cn/news/170268 §3.4: prefill from the first missing position on
-    top of the hit blocks)."""
+    top of the hit blocks). With shared_prefix_tokens set (the cached
+    prompt's tokens, which every table starts with), the attention is
+    pa_prefill_shared_prefix, which reads the shared blocks once per group
+    of rows of all requests."""
 
-    def __init__(self, batch, device="cuda", out_dtype=None):
+    def __init__(self, batch, device="cuda", out_dtype=None, shared_prefix_tokens=None):
+        self.shared_prefix_tokens = shared_prefix_tokens
         dt = batch.workload.dtype
         self.batch = batch
         self.query = to_device_tensor(batch.query, dt, device)
@@ -199,7 +203,7 @@ class DevicePrefill:
     def attend(self):
         return palib.prefill(self.query, self.key_cache, self.value_cache, self.block_tables,
                              self.context_lens, self.query_start, self.scale, self.max_query_len,
-                             out=self.out)
+                             out=self.out, shared_prefix_tokens=self.shared_prefix_tokens)
 
     def step(self):
         self.write_cache()

@@ -166,3 +166,27 @@ def test_prefill_rejects_bad_arguments_without_launching(lib, kw, status):
 def test_prefill_without_new_tokens_is_a_no_op(lib):
     assert _prefill(lib, T=0, maxq=0, qs=None) == 0
     assert _prefill(lib, B=0, T=0, maxq=0, qs=None) == 0
+
+
+def _prefill_shared(lib, ps=16, **kw):
+    a = dict(out=1 << 12, out_dtype=2, query=1 << 12, kc=1 << 12, vc=1 << 12, bt=1 << 12, cl=1 << 12,
+             qs=1 << 12, B=2, T=5, maxq=4, Hq=8, Hkv=8, D=128, BS=16, MB=8, NB=64, scale=0.1, kvdt=0)
+    a.update(kw)
+    return lib.pa_prefill_shared_prefix(
+        a["out"], a["out_dtype"], a["query"], a["kc"], a["vc"], a["bt"], a["cl"], a["qs"], a["B"],
+        a["T"], a["maxq"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["MB"], a["NB"], a["scale"],
+        a["kvdt"], ps, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=-16), 2), (dict(ps=8), 2), (dict(ps=8 * 16 + 16), 2), (dict(Hq=34, Hkv=2), 4),
+    (dict(D=72), 4), (dict(T=-1), 2), (dict(qs=None), 1), (dict(kvdt=2), 3),
+])
+def test_prefill_shared_prefix_rejects_bad_arguments_without_launching(lib, kw, status):
+    assert _prefill_shared(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_prefill_shared_prefix_without_new_tokens_is_a_no_op(lib):
+    assert _prefill_shared(lib, T=0, maxq=0, qs=None) == 0
+    assert _prefill_shared(lib, ps=0, B=0, T=0, maxq=0, qs=None) == 0

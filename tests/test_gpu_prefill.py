@@ -85,6 +85,35 @@ def test_prefill_matches_oracle(case, out_kind):
     _assert_close(to_host_f64(out), ref, "f32" if out_kind == "f32" else dt, "case %d" % case)
 
 
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("share", ["cached", "none"])
+def test_prefill_shared_prefix_matches_oracle(case, share):
+    # every table starts with the cached prompt's blocks (the same physical
+    # blocks): pa_prefill_shared_prefix reads them once for the rows of all
+    # requests; with nothing declared shared it streams each request whole
+    Hq, Hkv, D, dt, BS, cached, lens = CASES[case]
+    b = W.make_prefill_batch(_workload(Hq, Hkv, D, dt, BS, cached, lens), seed=700 + case,
+                             lens=lens)
+    ps = cached if share == "cached" else 0
+    db = DevicePrefill(b, out_dtype=torch.float32, shared_prefix_tokens=ps)
+    out = db.step()
+    torch.cuda.synchronize()
+    _, _, ref = _oracle(b)
+    _assert_close(to_host_f64(out), ref, "f32", "case %d shared %d" % (case, ps))
+
+
+def test_prefill_shared_prefix_many_requests_per_workgroup():
+    # one or two new tokens per request, requests without new tokens among
+    # them: a workgroup's rows span dozens of requests
+    lens = [1, 0, 2, 1, 1, 0, 0, 2] * 12 + [40, 1, 0]
+    b = W.make_prefill_batch(_workload(8, 8, 128, "bf16", 16, 64, lens), seed=31, lens=lens)
+    db = DevicePrefill(b, shared_prefix_tokens=48)  # part of the cached prompt declared shared
+    out = db.step()
+    torch.cuda.synchronize()
+    _, _, ref = _oracle(b)
+    _assert_close(to_host_f64(out), ref, "bf16", "many requests")
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0])
 def test_prefill_negative_and_zero_scale(scale):
     # the kernel keeps scores unscaled and applies |scale| in the exponent,
@@ -160,6 +189,24 @@ def test_prefill_workloads_on_sampled_requests(name):
     assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
     assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
     idx = [0, 1, int(np.argmax(np.diff(b.query_start))), len(b.context_lens) - 1]
+    rows, starts = _sub_batch(b, idx)
+    ref = oracle.prefill(b.query[rows], kc, vc, b.block_tables[idx], b.context_lens[idx], starts,
+                         b.scale, b.dtype)
+    _assert_close(to_host_f64(out)[rows], ref, b.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["prefix_prefill", "prefix_prefill_gqa"])
+def test_prefill_shared_prefix_workloads_on_sampled_requests(name):
+    # the full workloads with the cached prompt declared shared, as the
+    # benchmark's shared-prefix step runs them; the oracle checks a sample
+    w = W.PREFILL_WORKLOADS[name]
+    b = W.make_prefill_batch(w, seed=0)
+    db = DevicePrefill(b, shared_prefix_tokens=w.cached_tokens)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    idx = [0, 1, int(np.argmax(np.diff(b.query_start))), 57, len(b.context_lens) - 1]
     rows, starts = _sub_batch(b, idx)
     ref = oracle.prefill(b.query[rows], kc, vc, b.block_tables[idx], b.context_lens[idx], starts,
                          b.scale, b.dtype)
