@@ -74,9 +74,12 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #define PA_PREFILL_LOAD_AUX 0
 #endif
 
-// Chunks of K/V in flight per wave: 1 (one register set) or 2.
-#ifndef PA_PREFILL_DEPTH
-#define PA_PREFILL_DEPTH 2
+// Chunks of K/V in flight per wave: 2 (two register sets) where a chunk
+// takes at most two loads of K and of V per lane, else 1 (head_dim 256:
+// two sets of four would cost 32 registers and the waves that hide
+// latency).
+#ifndef PA_PREFILL_MAX_DEPTH
+#define PA_PREFILL_MAX_DEPTH 2
 #endif
 
 // Finds the request of flattened new token tok: the last r < num_seqs with
@@ -117,6 +120,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     static_assert(LPC >= 1 && LPC * RPL == CH, "the workgroup's loads tile the chunk");
     static_assert(BS % RPW == 0, "the rows of one wave's load share a block");
     static_assert(NS == 2, "one p·v contraction (32 tokens) per chunk");
+    constexpr int DEPTH = LPC <= 2 ? PA_PREFILL_MAX_DEPTH : 1;
 
     __shared__ __attribute__((aligned(16))) char sm_k[2][TILE];
     __shared__ __attribute__((aligned(16))) char sm_v[2][TILE];
@@ -484,51 +488,52 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     const int nb = (L + BS - 1) / BS;
     if constexpr (!SH) {
         const int nch = (max(end - start, 0) + CH - 1) / CH;
-#if PA_PREFILL_DEPTH == 1
-        Stage kr, vr;
-        uint32_t okm = issue(start, bt, nb, end, kr, vr);
-        stash(0, kr, vr);
-        __syncthreads();
-        for (int c = 0; c < nch; ++c) {
-            const int cs = start + c * CH;
-            const uint32_t okm_next = issue(cs + CH, bt, nb, end, kr, vr);
-            if (cs < wend) compute(cs, -1, okm, sm_k[c & 1], sm_v[c & 1]);
-            stash((c + 1) & 1, kr, vr);
+        if constexpr (DEPTH == 1) {
+            Stage kr, vr;
+            uint32_t okm = issue(start, bt, nb, end, kr, vr);
+            stash(0, kr, vr);
             __syncthreads();
-            okm = okm_next;
-        }
-#else
-        // Two chunks in flight: register set 0 stages the even chunks, set
-        // 1 the odd ones, and the loop is unrolled by two so that both sets
-        // and both LDS buffers are fixed in each half. In step c the loads
-        // of chunk c + 2 are issued, chunk c is computed from LDS, and
-        // chunk c + 1 (issued a step earlier) is stored to the other
-        // buffer; its wait leaves chunk c + 2's loads in flight.
-        Stage k0, v0, k1, v1;
-        uint32_t okm0 = issue(start, bt, nb, end, k0, v0);
-        uint32_t okm1 = issue(start + CH, bt, nb, end, k1, v1);
-        stash(0, k0, v0);
-        __syncthreads();
-        for (int c = 0; c < nch; c += 2) {
-            {
+            for (int c = 0; c < nch; ++c) {
                 const int cs = start + c * CH;
-                const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0);
-                if (cs < wend) compute(cs, -1, okm0, sm_k[0], sm_v[0]);
-                stash(1, k1, v1);
+                const uint32_t okm_next = issue(cs + CH, bt, nb, end, kr, vr);
+                if (cs < wend) compute(cs, -1, okm, sm_k[c & 1], sm_v[c & 1]);
+                stash((c + 1) & 1, kr, vr);
                 __syncthreads();
-                okm0 = okm2;
+                okm = okm_next;
             }
-            if (c + 1 >= nch) break;
-            {
-                const int cs = start + (c + 1) * CH;
-                const uint32_t okm3 = issue(cs + 2 * CH, bt, nb, end, k1, v1);
-                if (cs < wend) compute(cs, -1, okm1, sm_k[1], sm_v[1]);
-                stash(0, k0, v0);
-                __syncthreads();
-                okm1 = okm3;
+        } else {
+            // Two chunks in flight: register set 0 stages the even chunks,
+            // set 1 the odd ones, and the loop is unrolled by two so that
+            // both sets and both LDS buffers are fixed in each half. In step
+            // c the loads of chunk c + 2 are issued, chunk c is computed
+            // from LDS, and chunk c + 1 (issued a step earlier) is stored to
+            // the other buffer; its wait leaves chunk c + 2's loads in
+            // flight.
+            Stage k0, v0, k1, v1;
+            uint32_t okm0 = issue(start, bt, nb, end, k0, v0);
+            uint32_t okm1 = issue(start + CH, bt, nb, end, k1, v1);
+            stash(0, k0, v0);
+            __syncthreads();
+            for (int c = 0; c < nch; c += 2) {
+                {
+                    const int cs = start + c * CH;
+                    const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0);
+                    if (cs < wend) compute(cs, -1, okm0, sm_k[0], sm_v[0]);
+                    stash(1, k1, v1);
+                    __syncthreads();
+                    okm0 = okm2;
+                }
+                if (c + 1 >= nch) break;
+                {
+                    const int cs = start + (c + 1) * CH;
+                    const uint32_t okm3 = issue(cs + 2 * CH, bt, nb, end, k1, v1);
+                    if (cs < wend) compute(cs, -1, okm1, sm_k[1], sm_v[1]);
+                    stash(0, k0, v0);
+                    __syncthreads();
+                    okm1 = okm3;
+                }
             }
         }
-#endif
     } else {
         // The workgroup's streams, one after another: the shared prefix
         // (positions 0 .. ps - 1, table row 0), then for each of its
@@ -567,31 +572,47 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         };
         Cur c0 = ps > 0 ? Cur{-1, 0, ps, ps / BS, a.block_tables} : stream_from(r_lo);
         Cur c1 = next(c0);
-        Stage k0, v0, k1, v1;
-        uint32_t okm0 = issue(c0.cs, c0.tb, c0.nb, c0.end, k0, v0);
-        uint32_t okm1 = issue(c1.cs, c1.tb, c1.nb, c1.end, k1, v1);
-        stash(0, k0, v0);
-        __syncthreads();
-        while (c0.r != kDone) {
-            const Cur c2 = next(c1);
-            {
-                const uint32_t okm2 = issue(c2.cs, c2.tb, c2.nb, c2.end, k0, v0);
-                if (wanted(c0)) compute(c0.cs, c0.r, okm0, sm_k[0], sm_v[0]);
-                stash(1, k1, v1);
+        if constexpr (DEPTH == 1) {
+            Stage kr, vr;
+            uint32_t okm = issue(c0.cs, c0.tb, c0.nb, c0.end, kr, vr);
+            stash(0, kr, vr);
+            __syncthreads();
+            for (int buf = 0; c0.r != kDone; buf ^= 1) {
+                const uint32_t okm_next = issue(c1.cs, c1.tb, c1.nb, c1.end, kr, vr);
+                if (wanted(c0)) compute(c0.cs, c0.r, okm, sm_k[buf], sm_v[buf]);
+                stash(buf ^ 1, kr, vr);
                 __syncthreads();
-                okm0 = okm2;
+                okm = okm_next;
+                c0 = c1;
+                c1 = next(c1);
             }
-            if (c1.r == kDone) break;
-            const Cur c3 = next(c2);
-            {
-                const uint32_t okm3 = issue(c3.cs, c3.tb, c3.nb, c3.end, k1, v1);
-                if (wanted(c1)) compute(c1.cs, c1.r, okm1, sm_k[1], sm_v[1]);
-                stash(0, k0, v0);
-                __syncthreads();
-                okm1 = okm3;
+        } else {
+            Stage k0, v0, k1, v1;
+            uint32_t okm0 = issue(c0.cs, c0.tb, c0.nb, c0.end, k0, v0);
+            uint32_t okm1 = issue(c1.cs, c1.tb, c1.nb, c1.end, k1, v1);
+            stash(0, k0, v0);
+            __syncthreads();
+            while (c0.r != kDone) {
+                const Cur c2 = next(c1);
+                {
+                    const uint32_t okm2 = issue(c2.cs, c2.tb, c2.nb, c2.end, k0, v0);
+                    if (wanted(c0)) compute(c0.cs, c0.r, okm0, sm_k[0], sm_v[0]);
+                    stash(1, k1, v1);
+                    __syncthreads();
+                    okm0 = okm2;
+                }
+                if (c1.r == kDone) break;
+                const Cur c3 = next(c2);
+                {
+                    const uint32_t okm3 = issue(c3.cs, c3.tb, c3.nb, c3.end, k1, v1);
+                    if (wanted(c1)) compute(c1.cs, c1.r, okm1, sm_k[1], sm_v[1]);
+                    stash(0, k0, v0);
+                    __syncthreads();
+                    okm1 = okm3;
+                }
+                c0 = c2;
+                c1 = c3;
             }
-            c0 = c2;
-            c1 = c3;
         }
     }
 
