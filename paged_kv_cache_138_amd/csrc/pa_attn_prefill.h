@@ -82,10 +82,10 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #define PA_PREFILL_MAX_DEPTH 2
 #endif
 
-// Finds the request of flattened new token tok: the last r < num_seqs with
-// query_start[r] <= tok (requests without new tokens are passed over).
-__device__ __forceinline__ int request_of(const int32_t* qs, int num_seqs, int tok) {
-    int lo = 0, hi = num_seqs - 1;
+// Finds the request of flattened new token tok among requests lo .. hi:
+// the last r in that range with query_start[r] <= tok (requests without
+// new tokens are passed over).
+__device__ __forceinline__ int request_of(const int32_t* qs, int lo, int hi, int tok) {
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (qs[mid] <= tok) lo = mid;
@@ -206,15 +206,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         const int t0 = (blockIdx.x / Hkv) * NW * TR * R;
         if (t0 >= T) return;  // uniform over the workgroup
         ps = min(a.prefix_tokens, Lmax);
-        r_lo = __builtin_amdgcn_readfirstlane(request_of(qs, B, t0));
-        r_hi = __builtin_amdgcn_readfirstlane(request_of(qs, B, min(t0 + NW * TR * R, T) - 1));
+        r_lo = __builtin_amdgcn_readfirstlane(request_of(qs, 0, B - 1, t0));
+        r_hi = __builtin_amdgcn_readfirstlane(
+            request_of(qs, r_lo, B - 1, min(t0 + NW * TR * R, T) - 1));
         tw = t0 + wave * TR * R;
         int lo_pos = 0x7fffffff;
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
             const int tok = tw + u * R + n / G;
             rowv[u] = n < R * G && tok < T;
-            const int r = request_of(qs, B, rowv[u] ? tok : t0);
+            const int r = request_of(qs, r_lo, r_hi, rowv[u] ? tok : t0);  // a short search
             int Lr = a.context_lens[r];
             Lr = Lr < 0 ? 0 : (Lr > Lmax ? Lmax : Lr);
             const int pos = Lr - (qs[r + 1] - qs[r]) + (tok - qs[r]);
