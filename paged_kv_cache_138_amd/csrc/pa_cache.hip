@@ -24,16 +24,20 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
         const int64_t tok = idx / pieces_per_token;
         const int64_t piece = idx - tok * pieces_per_token;
         // the source pieces do not depend on the slot: their loads are issued
-        // together with the slot's, not after it
-        const u32x4 k = *(const u32x4*)(key + tok * key_stride + piece * 8);
-        const u32x4 v = *(const u32x4*)(value + tok * value_stride + piece * 8);
+        // together with the slot's, not after it. Loads and stores are
+        // non-temporal: the rows pass through once, and a prefill's scatter
+        // would otherwise push the cached prompt, which the attention after
+        // it re-reads, out of L2.
+        const u32x4 k = __builtin_nontemporal_load((const u32x4*)(key + tok * key_stride + piece * 8));
+        const u32x4 v =
+            __builtin_nontemporal_load((const u32x4*)(value + tok * value_stride + piece * 8));
         const int64_t slot = slot_mapping[tok];
         if (slot < 0 || slot >= num_slots) continue;  // padding, or outside the cache
         // slot = block * block_size + row, and rows are dense inside a block,
         // so the destination row is simply `slot` rows into the cache
         const int64_t dst = slot * row_elems + piece * 8;
-        *(u32x4*)(key_cache + dst) = k;
-        *(u32x4*)(value_cache + dst) = v;
+        __builtin_nontemporal_store(k, (u32x4*)(key_cache + dst));
+        __builtin_nontemporal_store(v, (u32x4*)(value_cache + dst));
     }
 }
 
