@@ -15,8 +15,9 @@
 // The workgroup walks the context in 32-token chunks, and all its waves
 // read each chunk's K and V rows from LDS, so a row of the cache comes from
 // memory once per NW * 16 rows rather than once per 16 (the 16-row
-// grouped-query kernel's reuse). Chunks are double-buffered in LDS: the
-// global loads of chunk c + 1 are in flight while chunk c is computed, and
+// grouped-query kernel's reuse). Chunks are double-buffered in LDS and
+// staged through registers: the global loads of chunks c + 1 and c + 2 (of
+// c + 1 only at head_dim 256) are in flight while chunk c is computed, and
 // one barrier per chunk orders the buffer swap.
 //
 // Per chunk and tile, the products are those of the grouped-query decode
@@ -27,6 +28,13 @@
 // split into hi + lo 16-bit halves. Each row is masked to positions up to
 // its own; a wave whose rows all sit before a chunk, or that has no rows,
 // skips its products (it still loads and waits at the barrier).
+//
+// Shared-prefix mode (SH, lqnn.cn/news/170268 §4.3: requests that hit the
+// same cached prompt): the new tokens of all sequences form one list of
+// rows and a workgroup takes consecutive ones, whatever their sequences.
+// It streams the shared prompt blocks once for all its rows, then each of
+// its sequences' own positions for that sequence's rows only; the online
+// softmax runs on across the streams, so no merge is needed.
 //
 // The same kernel has a decode mode (no query_start): one new token per
 // sequence and context partitions with the split path's workspace rows.
