@@ -164,7 +164,7 @@ def cpu_baseline(batch, target_s):
     t_write = time.perf_counter() - t0
     elapsed = 0.0
     i = 0
-    while elapsed < target_s and i < 4 * B:
+    while elapsed < target_s and i < 64 * B:  # the batch's sequences, cycled until target_s
         s = order[i % B]
         sl = slice(s, s + 1)
         if kc is None:
