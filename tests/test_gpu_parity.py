@@ -731,3 +731,39 @@ def test_swap_refuses_pageable_host_memory():
     assert st == 4
     with pytest.raises(ValueError):
         palib.swap_blocks(pageable, pageable, kc, kc, mapping)
+
+
+def _drop_block(tables, lens, seqs, j, block_size):
+    """The oracle's view of tables whose entry j is outside the pool for
+    sequences seqs: that block's tokens are absent, which is the same as a
+    context without the block (a full block, so every later token keeps its
+    offset in its block)."""
+    t = tables.copy()
+    L = lens.copy()
+    for i in seqs:
+        t[i, j:-1] = tables[i, j + 1:]
+        t[i, -1] = -1
+        L[i] -= block_size
+    return t, L
+
+
+@pytest.mark.parametrize("path", ["single", "split", "fused"])
+@pytest.mark.parametrize("bad", [64 + 5, -7])
+def test_block_outside_the_pool_counts_as_absent(path, bad):
+    # pa.h: a block id outside [0, num_blocks) makes its tokens count as
+    # absent; block 1 of sequence 0 (positions 16..31, not its last block)
+    w = _small("absent", num_seqs=3, num_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+               block_size=16, num_blocks=64, max_blocks_per_seq=8)
+    b = W.make_batch(w, seed=77, lens=[100, 70, 33], unallocated="nan")
+    ref_tables, ref_lens = _drop_block(b.block_tables, b.context_lens, [0], 1, 16)
+    b.block_tables = b.block_tables.copy()
+    b.block_tables[0, 1] = bad
+    db = DeviceBatch(b, out_dtype=torch.float32, split=path != "single",
+                     partition_size=32 if path != "single" else None, fused=path == "fused")
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    ref = oracle.decode(b.query, kc, vc, ref_tables, ref_lens, b.scale, b.dtype)
+    _assert_close(to_host_f64(out), ref, "f32", "absent block, %s path" % path)
+

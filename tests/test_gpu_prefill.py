@@ -211,3 +211,28 @@ def test_prefill_shared_prefix_workloads_on_sampled_requests(name):
     ref = oracle.prefill(b.query[rows], kc, vc, b.block_tables[idx], b.context_lens[idx], starts,
                          b.scale, b.dtype)
     _assert_close(to_host_f64(out)[rows], ref, b.dtype, name)
+
+
+@pytest.mark.parametrize("entry", ["plain", "shared"])
+def test_prefill_block_outside_the_pool_counts_as_absent(entry):
+    # pa.h: a block id outside [0, num_blocks) makes its tokens count as
+    # absent. Block 1 of the cached prompt (positions 16..31) is out of the
+    # pool in every table; the oracle sees contexts without it (a full block
+    # before every new token, so the new tokens keep their offsets)
+    lens = [5, 20, 33]
+    b = W.make_prefill_batch(_workload(8, 2, 128, "f16", 16, 64, lens), seed=41, lens=lens)
+    ref_tables = b.block_tables.copy()
+    ref_tables[:, 1:-1] = b.block_tables[:, 2:]
+    ref_tables[:, -1] = -1
+    ref_lens = b.context_lens - 16
+    b.block_tables = b.block_tables.copy()
+    b.block_tables[:, 1] = b.workload.num_blocks + 3
+    db = DevicePrefill(b, out_dtype=torch.float32,
+                       shared_prefix_tokens=64 if entry == "shared" else None)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    ref = oracle.prefill(b.query, kc, vc, ref_tables, ref_lens, b.query_start, b.scale, b.dtype)
+    _assert_close(to_host_f64(out), ref, "f32", "absent block, %s" % entry)
+
