@@ -767,3 +767,24 @@ def test_block_outside_the_pool_counts_as_absent(path, bad):
     ref = oracle.decode(b.query, kc, vc, ref_tables, ref_lens, b.scale, b.dtype)
     _assert_close(to_host_f64(out), ref, "f32", "absent block, %s path" % path)
 
+
+@pytest.mark.parametrize("path", ["single", "split", "fused"])
+def test_context_lengths_are_clamped(path):
+    # pa.h: a context length is clamped to [0, max_blocks_per_seq * block_size]
+    w = _small("clamp", num_seqs=3, num_heads=4, num_kv_heads=4, head_dim=128, dtype="f16",
+               block_size=16, num_blocks=64, max_blocks_per_seq=8)
+    b = W.make_batch(w, seed=91, lens=[1, 128, 50], unallocated="nan")
+    ref_lens = np.array([0, 128, 50], dtype=np.int32)
+    b.context_lens = np.array([-5, 200, 50], dtype=np.int32)
+    db = DeviceBatch(b, out_dtype=torch.float32, split=path != "single",
+                     partition_size=32 if path != "single" else None, fused=path == "fused")
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    ref = oracle.decode(b.query, kc, vc, b.block_tables, ref_lens, b.scale, b.dtype)
+    got = to_host_f64(out)
+    assert np.all(got[0] == 0.0)  # no positions: a zero row
+    _assert_close(got, ref, "f32", "clamped lengths, %s path" % path)
+
