@@ -436,16 +436,18 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                 }
             }
             // ---- online softmax of row n ---------------------------------
-            // The reference m moves only when the chunk's max passes it by
-            // more than thr (log2 units), and then for every row of the
-            // tile: the result is the same for any reference, the weights
-            // stay below 2^thr, and most chunks skip rescaling the
-            // accumulators.
+            // The reference m moves only when a score of the chunk passes it
+            // by more than thr (log2 units), and then for every row of the
+            // tile, to the row's max: the result is the same for any
+            // reference, the weights stay below 2^thr, and most chunks skip
+            // rescaling the accumulators (and the max across lanes).
+            // The test uses this lane's own max; the row's max (across its
+            // four lanes) is only needed when some reference moves.
             float cr = sv[0];
 #pragma unroll
             for (int e = 1; e < 4 * NS; ++e) cr = fmaxf(cr, sv[e]);
-            const float cm = max_over_groups(cr) * sl;
-            if (__builtin_amdgcn_ballot_w64(cm > m[u] + thr) != 0) {
+            if (__builtin_amdgcn_ballot_w64(cr * sl > m[u] + thr) != 0) {
+                const float cm = max_over_groups(cr) * sl;
                 const float mn = fmaxf(m[u], cm);
                 const float alpha = fast_exp2(m[u] - mn);  // 0 while m is the sentinel
                 m[u] = mn;
