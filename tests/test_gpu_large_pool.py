@@ -1,0 +1,122 @@
+"""Block pools larger than 4 GiB per cache: the blocks a step touches sit
+beyond byte offset 2^32 of the key and value caches, so a byte offset
+truncated to 32 bits anywhere in the scatter, the decode kernels or prefill
+would read or write the wrong block.
+
+A small workload is built as usual, its blocks are copied to the top of a
+pool of 196608 blocks of 32 KiB (6 GiB per cache), and the block tables and
+slot mapping are renamed to match. The oracle runs on the compact pool; the
+renaming changes no value, so the outputs meet the usual bars and the moved
+blocks equal the oracle's cache bit for bit after the scatter.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_138_amd import lib as palib
+from paged_kv_cache_138_amd import workloads as W
+from paged_kv_cache_138_amd.pipeline import DeviceBatch, DevicePrefill, to_host_bits, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+BIG = 196608  # blocks of 16 tokens x 8 kv heads x 128 x 2 bytes: 6 GiB per cache
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_present():
+    assert os.path.exists(palib.LIB_PATH), "libpa.so must be built before the GPU tests"
+    palib.load()
+
+
+def _high_ids(n):
+    # compact block i -> BIG - 1 - 3i (every id above 2^32 bytes / 32 KiB)
+    ids = BIG - 1 - 3 * np.arange(n, dtype=np.int64)
+    assert ids.min() * 32768 >= 2 ** 32
+    return ids
+
+
+def _move_to_high_pool(db):
+    """Copy db's compact caches to the top of a BIG-block pool and rename its
+    block tables and slot mapping to the new ids (negative entries kept)."""
+    n, BS = db.key_cache.shape[0], db.key_cache.shape[1]
+    assert db.key_cache.element_size() * db.key_cache[0].numel() == 32768
+    ids = _high_ids(n)
+    lut = torch.from_numpy(ids).to(db.key_cache.device)
+    for name in ("key_cache", "value_cache"):
+        small = getattr(db, name)
+        big = torch.empty((BIG,) + tuple(small.shape[1:]), dtype=small.dtype, device=small.device)
+        big[lut] = small
+        setattr(db, name, big)
+    t = db.block_tables
+    inside = (t >= 0) & (t < n)
+    db.block_tables = torch.where(inside, lut[t.clamp(0, n - 1).long()].to(t.dtype), t)
+    s = db.slot_mapping
+    blk = torch.div(s.clamp(min=0), BS, rounding_mode="floor")
+    moved = lut[blk.clamp(max=n - 1)] * BS + s.clamp(min=0) % BS
+    db.slot_mapping = torch.where(s >= 0, moved.to(s.dtype), s)
+    return ids
+
+
+def _moved_blocks_equal(db, ids, kc, vc):
+    lut = torch.from_numpy(ids).to(db.key_cache.device)
+    for big, ref in ((db.key_cache, kc), (db.value_cache, vc)):
+        got = to_host_bits(big[lut].contiguous())
+        assert np.array_equal(got, ref.view(np.uint16)), "moved blocks differ after the scatter"
+
+
+def _assert_close(got, ref, what):
+    assert np.isfinite(got).all(), "non-finite output " + what
+    err = np.abs(got - ref)
+    assert err.max() <= ATOL, "%s: max err %.3g" % (what, err.max())
+
+
+def _free(db):
+    db.key_cache = db.value_cache = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("Hq", [8, 32])  # one query head per kv head, and four
+@pytest.mark.parametrize("path", ["single", "split", "fused"])
+def test_decode_with_blocks_beyond_4_gib(Hq, path):
+    w = W.custom_workload("big", num_seqs=4, num_heads=Hq, num_kv_heads=8, head_dim=128,
+                          dtype="f16", block_size=16, num_blocks=96, max_blocks_per_seq=24,
+                          lens="uniform:1:380")
+    b = W.make_batch(w, seed=4242 + Hq, lens=[1, 129, 380, 47], unallocated="nan")
+    db = DeviceBatch(b, out_dtype=torch.float32, split=path != "single",
+                     partition_size=64 if path != "single" else None, fused=path == "fused")
+    ids = _move_to_high_pool(db)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    ref = oracle.decode(b.query, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype)
+    _moved_blocks_equal(db, ids, kc, vc)
+    _assert_close(to_host_f64(out), ref, "decode %s, %d heads" % (path, Hq))
+    _free(db)
+
+
+@pytest.mark.parametrize("shared", [None, 64])
+def test_prefill_with_blocks_beyond_4_gib(shared):
+    lens = [1, 17, 40, 5]
+    cached, BS = 64, 16
+    need = cached // BS + sum(-(-(cached + S) // BS) - cached // BS for S in lens) + 4
+    mb = -(-(cached + max(lens)) // BS)
+    w = W.PrefillWorkload("big", len(lens), 32, 8, 128, "f16", BS, need, mb, cached, "fixed:1")
+    b = W.make_prefill_batch(w, seed=977, lens=lens)
+    db = DevicePrefill(b, out_dtype=torch.float32, shared_prefix_tokens=shared)
+    ids = _move_to_high_pool(db)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    ref = oracle.prefill(b.query, kc, vc, b.block_tables, b.context_lens, b.query_start, b.scale,
+                         b.dtype)
+    _moved_blocks_equal(db, ids, kc, vc)
+    _assert_close(to_host_f64(out), ref, "prefill, shared %s" % shared)
+    _free(db)
