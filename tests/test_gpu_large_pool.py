@@ -1,7 +1,7 @@
 """Block pools larger than 4 GiB per cache: the blocks a step touches sit
 beyond byte offset 2^32 of the key and value caches, so a byte offset
-truncated to 32 bits anywhere in the scatter, the decode kernels or prefill
-would read or write the wrong block.
+truncated to 32 bits anywhere in the scatter, the decode kernels, prefill,
+the block copy or the swap would read or write the wrong block.
 
 A small workload is built as usual, its blocks are copied to the top of a
 pool of 196608 blocks of 32 KiB (6 GiB per cache), and the block tables and
@@ -120,3 +120,65 @@ def test_prefill_with_blocks_beyond_4_gib(shared):
     _moved_blocks_equal(db, ids, kc, vc)
     _assert_close(to_host_f64(out), ref, "prefill, shared %s" % shared)
     _free(db)
+
+
+def _compact(pool, ids):
+    return to_host_bits(pool[torch.from_numpy(ids).to(pool.device)].contiguous())
+
+
+def test_copy_blocks_beyond_4_gib():
+    # copies from low to high ids, high to low, and high to high
+    rng = np.random.default_rng(5)
+    shape = (BIG, 16, 8, 128)
+    kc = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    ids = np.concatenate([rng.choice(1000, 12, replace=False),
+                          _high_ids(24)]).astype(np.int64)      # the blocks taking part
+    g = torch.Generator().manual_seed(6)
+    lut = torch.from_numpy(ids).cuda()
+    kc[lut] = torch.randn((len(ids),) + shape[1:], generator=g).bfloat16().cuda()
+    vc[lut] = torch.randn((len(ids),) + shape[1:], generator=g).bfloat16().cuda()
+    # compact indices: 0..11 low, 12..35 high
+    pairs_c = np.array([[0, 12], [13, 1], [14, 15], [2, 16], [17, 3], [18, 19], [20, 21],
+                        [4, 22], [23, 5], [24, 25]], dtype=np.int64)
+    k0, v0 = _compact(kc, ids), _compact(vc, ids)
+    palib.copy_blocks(kc, vc, torch.from_numpy(ids[pairs_c]).cuda())
+    torch.cuda.synchronize()
+    rk, rv = oracle.copy_blocks(k0, v0, pairs_c)
+    assert np.array_equal(_compact(kc, ids), rk)
+    assert np.array_equal(_compact(vc, ids), rv)
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def test_swap_blocks_beyond_4_gib():
+    # out: high device blocks -> pinned host pool; in: host pool -> other high
+    # device blocks
+    shape = (BIG, 16, 8, 128)
+    kc = torch.empty(shape, dtype=torch.float16, device="cuda")
+    vc = torch.empty(shape, dtype=torch.float16, device="cuda")
+    ids = _high_ids(16)
+    g = torch.Generator().manual_seed(8)
+    lut = torch.from_numpy(ids).cuda()
+    kc[lut] = torch.randn((16,) + shape[1:], generator=g).half().cuda()
+    vc[lut] = torch.randn((16,) + shape[1:], generator=g).half().cuda()
+    hk = torch.zeros((10,) + shape[1:], dtype=torch.float16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    out_c = np.array([[0, 3], [5, 0], [7, 9], [15, 4]], dtype=np.int64)  # compact dev -> host
+    k0, v0 = _compact(kc, ids), _compact(vc, ids)
+    out_pairs = np.stack([ids[out_c[:, 0]], out_c[:, 1]], axis=1)
+    palib.swap_blocks(hk, hv, kc, vc, torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    z = np.zeros((10,) + shape[1:], np.uint16)
+    rk, rv = oracle.swap_blocks(z, z.copy(), k0, v0, out_c)
+    assert np.array_equal(hk.view(torch.int16).numpy().view(np.uint16), rk)
+    assert np.array_equal(hv.view(torch.int16).numpy().view(np.uint16), rv)
+    in_c = np.array([[3, 1], [0, 2], [9, 14], [4, 6]], dtype=np.int64)   # host -> compact dev
+    in_pairs = np.stack([in_c[:, 0], ids[in_c[:, 1]]], axis=1)
+    palib.swap_blocks(kc, vc, hk, hv, torch.from_numpy(in_pairs).cuda())
+    torch.cuda.synchronize()
+    rk2, rv2 = oracle.swap_blocks(k0, v0, rk, rv, in_c)
+    assert np.array_equal(_compact(kc, ids), rk2)
+    assert np.array_equal(_compact(vc, ids), rv2)
+    del kc, vc
+    torch.cuda.empty_cache()
