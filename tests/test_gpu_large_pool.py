@@ -1,4 +1,7 @@
-"""Block pools larger than 4 GiB per cache: the blocks a step touches sit
+"""The largest sizes: block pools larger than 4 GiB per cache, and contexts
+of 128k positions.
+
+In the large pools, the blocks a step touches sit
 beyond byte offset 2^32 of the key and value caches, so a byte offset
 truncated to 32 bits anywhere in the scatter, the decode kernels, prefill,
 the block copy or the swap would read or write the wrong block.
@@ -182,3 +185,32 @@ def test_swap_blocks_beyond_4_gib():
     assert np.array_equal(_compact(vc, ids), rv2)
     del kc, vc
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1)])
+@pytest.mark.parametrize("path", ["single", "split", "fused"])
+def test_decode_at_128k_context(Hq, Hkv, path):
+    # the longest contexts: 131072 and 100001 positions (256 partitions of
+    # 512 on the split paths), against the oracle over every position
+    lens = [131072, 100001]
+    w = W.custom_workload("long", num_seqs=2, num_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                          dtype="bf16", block_size=16, num_blocks=14500,
+                          max_blocks_per_seq=8192, lens="uniform:1:131072")
+    b = W.make_batch(w, seed=1311 + Hq, lens=lens, unallocated="nan")
+    db = DeviceBatch(b, out_dtype=torch.float32, split=path != "single",
+                     partition_size=512 if path != "single" else None, fused=path == "fused")
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    ref = oracle.decode(b.query, kc, vc, b.block_tables, b.context_lens, b.scale, b.dtype)
+    # an average of ~1e5 N(0,1) value rows is ~1e-2: the bar is the usual
+    # 2e-3, relative to the largest output (3.3e-5 here). One wrong block in
+    # sequence 0's table moves the oracle's output by 2.6e-4 to 3.2e-4.
+    got = to_host_f64(out)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    bound = ATOL * np.abs(ref).max()
+    assert err <= bound, "128k context, %s path, %d/%d heads: max err %.3g > %.3g" % (
+        path, Hq, Hkv, err, bound)
