@@ -90,6 +90,12 @@ def test_full_size_workload(name):
                 err = np.abs(got[i, qh] - ref)
                 bound = ATOL + _ulp(ref, w.dtype)
                 assert (err <= bound).all(), "%s seq %d kv %d: max err %.3g" % (name, i, kv, err.max())
+                # long contexts average their value rows down to ~1e-2, where
+                # one wrong block moves the output by less than ATOL: also
+                # 2e-3 relative to the row's largest output, plus the rounding
+                rel = ATOL * np.abs(ref).max() + _ulp(ref, w.dtype)
+                assert (err <= rel).all(), "%s seq %d kv %d: max err %.3g, relative bar" % (
+                    name, i, kv, err.max())
         finally:
             kc_i[s // BS, s % BS] = rows_k
             vc_i[s // BS, s % BS] = rows_v
