@@ -1,5 +1,5 @@
-"""The largest sizes: block pools larger than 4 GiB per cache, and contexts
-of 128k positions.
+"""The largest sizes: block pools larger than 4 GiB per cache, decode over
+contexts of 128k positions, and prefill behind a 32k-token cached prompt.
 
 In the large pools, the blocks a step touches sit
 beyond byte offset 2^32 of the key and value caches, so a byte offset
@@ -214,3 +214,30 @@ def test_decode_at_128k_context(Hq, Hkv, path):
     bound = ATOL * np.abs(ref).max()
     assert err <= bound, "128k context, %s path, %d/%d heads: max err %.3g > %.3g" % (
         path, Hq, Hkv, err, bound)
+
+
+@pytest.mark.parametrize("shared", [None, 32768])
+def test_prefill_after_a_32k_prompt(shared):
+    # new tokens of four requests behind a 32768-token cached prompt (read
+    # through both entries); the bar is relative to the output scale, as for
+    # the 128k decode: 9.1e-5 here, where one wrong prompt block in request
+    # 1's table moves the oracle's output by 3.1e-3
+    lens = [1, 33, 100, 7]
+    cached, BS = 32768, 16
+    need = cached // BS + sum(-(-(cached + S) // BS) - cached // BS for S in lens) + 4
+    mb = -(-(cached + max(lens)) // BS)
+    w = W.PrefillWorkload("long", len(lens), 8, 2, 128, "bf16", BS, need, mb, cached, "fixed:1")
+    b = W.make_prefill_batch(w, seed=3276, lens=lens)
+    db = DevicePrefill(b, out_dtype=torch.float32, shared_prefix_tokens=shared)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
+                                      b.slot_mapping)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    ref = oracle.prefill(b.query, kc, vc, b.block_tables, b.context_lens, b.query_start, b.scale,
+                         b.dtype)
+    got = to_host_f64(out)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    bound = ATOL * np.abs(ref).max()
+    assert err <= bound, "32k prompt, shared %s: max err %.3g > %.3g" % (shared, err, bound)
