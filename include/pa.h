@@ -22,7 +22,10 @@
  * Conventions for every entry point:
  *   - All data pointers are DEVICE memory owned by the caller; tensors are
  *     dense and row-major in the layouts stated below, 16-byte aligned.
- *     The library allocates nothing and keeps no state between calls.
+ *     The library allocates nothing and keeps no data between calls. It
+ *     does cache, per process, facts of each device it has run on (the
+ *     number of compute units, each kernel's resident workgroups), under a
+ *     lock; they never change while the process runs.
  *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the default
  *     stream); nothing is synchronised. Calls that write the same buffers
  *     race if they overlap on different streams.
@@ -398,8 +401,12 @@ pa_status pa_decode_split_shared_prefix(void* out, pa_dtype out_dtype, const voi
  *             p < ceil(L_i / partition_size).
  *
  * With M = max_p m_p and w_p = l_p exp(m_p - M):
- * out = Σ_p w_p o_p / Σ_p w_p. Sequences with at most one partition are NOT
- * written (pa_decode_split writes those directly).
+ * out = Σ_p w_p o_p / Σ_p w_p over the np_i = ceil(L_i / partition_size)
+ * partitions of sequence i (at most max_partitions). Every row of `out` is
+ * written: a sequence with one partition gets o_0 as it is (the merge of a
+ * single partition), one with L_i <= 0 gets zeros. (The split calls run the
+ * same kernel but leave single-partition rows to their partition launch,
+ * which wrote the final output there.)
  */
 pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,
                        const float* part_max, const float* part_sum,

@@ -36,11 +36,24 @@ struct MergeArgs {
     int num_heads;
     int max_partitions;
     int partition_size;
+    // 0: rows of sequences with at most one partition are skipped (the split
+    // paths, whose partition launch wrote them); 1: every row is written,
+    // a single partition's output copied and an empty context as zeros
+    int complete;
 };
 
+// A row (one query head of one sequence) with np <= 1 partitions: whether
+// the merge writes it, and the element it writes (np = 1: the partition's
+// output o_0 as it is, the merge of one partition; np = 0: zero).
+__device__ __forceinline__ bool merge_trivial_row(const MergeArgs& a, int np, size_t r, int D,
+                                                  int d, float* v) {
+    if (np > 1) return false;
+    *v = np == 1 ? a.part_out[r * D + d] : 0.f;
+    return true;
+}
+
 // 256 threads merge 256 / head_dim workspace rows (row = one query head of
-// one sequence), one output element per thread; rows of sequences with at
-// most one partition are skipped (the partition kernel wrote them).
+// one sequence), one output element per thread.
 template <class OUT, int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     constexpr int RPW = 256 / D;
@@ -53,9 +66,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     if (L < 0) L = 0;
     int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
     if (np > a.max_partitions) np = a.max_partitions;
-    if (np <= 1) return;
+    if (np <= 1 && !a.complete) return;
     const size_t r = (size_t)row * a.max_partitions;
-    const float o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D);
+    float o;
+    if (!merge_trivial_row(a, np, r, D, d, &o))
+        o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D);
     OUT::store(a.out, (size_t)row * D + d, o);
 }
 
@@ -72,12 +87,13 @@ __global__ __launch_bounds__(256) void lse_merge_wave_kernel(MergeArgs a) {
     if (L < 0) L = 0;
     int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
     if (np > a.max_partitions) np = a.max_partitions;
-    if (np <= 1) return;
+    if (np <= 1 && !a.complete) return;
     const size_t r = (size_t)row * a.max_partitions;
 #pragma unroll
     for (int d = lane; d < D; d += 64) {
-        const float o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d,
-                                          np, D);
+        float o;
+        if (!merge_trivial_row(a, np, r, D, d, &o))
+            o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D);
         OUT::store(a.out, (size_t)row * D + d, o);
     }
 }
@@ -451,11 +467,12 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
 pa_status launch_merge(void* out, pa_dtype out_dtype, const float* part_out,
                        const float* part_max, const float* part_sum,
                        const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
-                       int max_partitions, int partition_size, void* stream, const char* what) {
+                       int max_partitions, int partition_size, void* stream, const char* what,
+                       bool complete = false) {
     merge_fn mfn = pick_merge(out_dtype, head_dim);
     PA_REQUIRE(mfn, PA_ERR_UNSUPPORTED, "no merge instance");
-    MergeArgs m{out, part_out, part_max, part_sum, context_lens,
-                num_seqs, num_heads, max_partitions, partition_size};
+    MergeArgs m{out,      part_out,      part_max, part_sum, context_lens, num_seqs,
+                num_heads, max_partitions, partition_size, complete ? 1 : 0};
     const int64_t rows = (int64_t)num_seqs * num_heads;
     const int64_t rpw = head_dim % 64 == 0 ? 256 / head_dim : 4;  // rows per workgroup
     const int64_t grid = (rows + rpw - 1) / rpw;
@@ -638,7 +655,7 @@ extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* pa
                "out and part_out must be 16-byte aligned");
     return launch_merge(out, out_dtype, part_out, part_max, part_sum, context_lens, num_seqs,
                         num_heads, head_dim, max_partitions, partition_size, stream,
-                        "pa_lse_merge");
+                        "pa_lse_merge", /*complete=*/true);
 }
 
 // ---------------------------------------------------------------------------

@@ -127,13 +127,15 @@ class DeviceBatch:
 
 
 class RotatedBatch(DeviceBatch):
-    """A copy of a DeviceBatch whose allocated blocks are moved, in a new
-    random physical order, into a compact pool of their own.
+    """A copy of a DeviceBatch whose whole pool is permuted: block b of the
+    source is block perm[b] here, for every one of the pool's blocks.
 
     The logical content of every sequence is unchanged, so the outputs are
-    bit-identical to the source batch's; timing loops cycle through several
-    such copies so that no step finds the previous step's cache blocks in
-    the GPU's last-level cache.
+    bit-identical to the source batch's, and the blocks in use stay spread
+    over a pool of the workload's full size (the same address range and
+    page spread as the source); timing loops cycle through several such
+    copies so that no step finds the previous step's cache blocks in the
+    GPU's last-level cache.
     """
 
     def __init__(self, src, seed):  # noqa: D401 - no DeviceBatch.__init__
@@ -146,24 +148,22 @@ class RotatedBatch(DeviceBatch):
         self.partition_size = src.partition_size
         self.prefix_tokens = src.prefix_tokens
         self.fused = src.fused
-        bt = src.block_tables
-        used = torch.unique(bt[bt >= 0])
-        n = int(used.numel())
+        NB, BS = src.key_cache.shape[0], src.key_cache.shape[1]
         g = torch.Generator(device="cpu").manual_seed(seed)
-        perm = torch.randperm(n, generator=g).to(src.device)
-        remap = torch.full((src.key_cache.shape[0],), -1, dtype=torch.int64, device=src.device)
-        remap[used] = perm
-        shape = (n,) + tuple(src.key_cache.shape[1:])
-        self.key_cache = torch.empty(shape, dtype=src.key_cache.dtype, device=src.device)
-        self.value_cache = torch.empty_like(self.key_cache)
-        self.key_cache[perm] = src.key_cache[used]
-        self.value_cache[perm] = src.value_cache[used]
-        self.block_tables = torch.where(bt >= 0, remap[bt.clamp(min=0).long()],
-                                        torch.full_like(bt, -1, dtype=torch.int64)).to(torch.int32)
-        BS = self.key_cache.shape[1]
+        perm = torch.randperm(NB, generator=g).to(src.device)
+        self.key_cache = torch.empty_like(src.key_cache)
+        self.value_cache = torch.empty_like(src.value_cache)
+        self.key_cache[perm] = src.key_cache
+        self.value_cache[perm] = src.value_cache
+        bt = src.block_tables
+        # table entries outside the pool (padding) keep their value
+        ok = (bt >= 0) & (bt < NB)
+        self.block_tables = torch.where(ok, perm[bt.clamp(0, NB - 1).long()].to(torch.int32), bt)
         sm = src.slot_mapping
         blk = torch.div(sm.clamp(min=0), BS, rounding_mode="floor")
-        self.slot_mapping = torch.where(sm >= 0, remap[blk] * BS + sm.clamp(min=0) % BS, sm)
+        sok = (sm >= 0) & (blk < NB)
+        self.slot_mapping = torch.where(sok, perm[blk.clamp(max=NB - 1)] * BS + sm.clamp(min=0) % BS,
+                                        sm)
         self.out = torch.empty_like(src.out)
         self.workspace = None if src.workspace is None else torch.empty_like(src.workspace)
 

@@ -634,6 +634,17 @@ def step_bytes(batch, out_dtype=None):
     return unique_tokens * per_tok + fixed, logical_tokens * per_tok + fixed
 
 
+def kv_read_bytes(batch):
+    """K and V bytes the attention must read: every attended position once
+    per kv head (a shared prefix once), nothing else."""
+    w = batch.workload
+    per_tok = 2 * w.num_kv_heads * w.head_dim * element_bytes(w.dtype)
+    L = batch.context_lens.astype(np.int64)
+    shared_tokens = len(batch.shared_blocks) * w.block_size
+    n_sharing = int((L > shared_tokens).sum()) if shared_tokens else 0
+    return (int(L.sum()) - max(n_sharing - 1, 0) * shared_tokens) * per_tok
+
+
 def cache_write_bytes(batch):
     """reshape_and_cache bytes: new K/V read + written, plus 8-byte slots."""
     w = batch.workload

@@ -299,9 +299,15 @@ def test_exported_lse_merge_matches_oracle_merge(D):
     out = torch.full((4, 4, D), -7.0, device="cuda")
     palib.lse_merge(dev(o), dev(m), dev(l), torch.from_numpy(b.context_lens).cuda(), 128, out=out)
     got = out.cpu().numpy().astype(np.float64)
-    # sequences with <= 1 partition are left untouched by the merge
-    assert np.all(got[0] == -7.0) and np.all(got[1] == -7.0)
-    np.testing.assert_allclose(got[2:], ref[2:], rtol=0, atol=1e-5)
+    # every row is written: an empty context gives zeros, a single partition
+    # is copied as it is (the merge of one partition), the others merged
+    assert np.all(got[0] == 0.0)
+    assert np.array_equal(got[1], np.asarray(o[1, :, 0], dtype=np.float32).astype(np.float64))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5)
+    # the same with a 16-bit output
+    out16 = torch.full((4, 4, D), -7.0, device="cuda", dtype=torch.float16)
+    palib.lse_merge(dev(o), dev(m), dev(l), torch.from_numpy(b.context_lens).cuda(), 128, out=out16)
+    _assert_close(to_host_f64(out16), ref, "f16", "exported merge, fp16 output")
 
 
 def test_fused_qkv_strided_cache_write():

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_runs
 from paged_kv_cache_138_amd import lib as palib
 from paged_kv_cache_138_amd import workloads as W
 from paged_kv_cache_138_amd.pipeline import DevicePrefill, to_host_bits, to_host_f64
@@ -168,49 +169,38 @@ def test_single_new_token_prefill_matches_decode():
     assert np.abs(to_host_f64(out) - to_host_f64(dec)).max() < 1e-5
 
 
-def _sub_batch(b, idx):
-    """The oracle's view of requests idx of a prefill batch (rows re-based)."""
-    qs = b.query_start
-    rows = np.concatenate([np.arange(qs[i], qs[i + 1]) for i in idx])
-    starts = np.concatenate([[0], np.cumsum([qs[i + 1] - qs[i] for i in idx])])
-    return rows, starts
-
-
 @pytest.mark.parametrize("name", ["prefix_prefill", "prefix_prefill_gqa"])
-def test_prefill_workloads_on_sampled_requests(name):
-    # the full workloads as the benchmark runs them; the oracle checks the
-    # caches in full and the outputs of a sample of requests
-    b = W.make_prefill_batch(W.PREFILL_WORKLOADS[name], seed=0)
-    db = DevicePrefill(b)
-    out = db.step()
-    torch.cuda.synchronize()
-    kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
-                                      b.slot_mapping)
-    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
-    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
-    idx = [0, 1, int(np.argmax(np.diff(b.query_start))), len(b.context_lens) - 1]
-    rows, starts = _sub_batch(b, idx)
-    ref = oracle.prefill(b.query[rows], kc, vc, b.block_tables[idx], b.context_lens[idx], starts,
-                         b.scale, b.dtype)
-    _assert_close(to_host_f64(out)[rows], ref, b.dtype, name)
-
-
-@pytest.mark.parametrize("name", ["prefix_prefill", "prefix_prefill_gqa"])
-def test_prefill_shared_prefix_workloads_on_sampled_requests(name):
-    # the full workloads with the cached prompt declared shared, as the
-    # benchmark's shared-prefix step runs them; the oracle checks a sample
+def test_prefill_workloads_every_request(name):
+    # the full workloads as the benchmark runs them, through both entries
+    # (plain, and the cached prompt declared shared) and both output types;
+    # the oracle checks the caches in full and every request's every row
     w = W.PREFILL_WORKLOADS[name]
+    print("full-size prefill parity:", name, flush=True)
     b = W.make_prefill_batch(w, seed=0)
-    db = DevicePrefill(b, shared_prefix_tokens=w.cached_tokens)
-    out = db.step()
-    torch.cuda.synchronize()
     kc, vc = oracle.reshape_and_cache(b.new_key, b.new_value, b.key_cache, b.value_cache,
                                       b.slot_mapping)
-    idx = [0, 1, int(np.argmax(np.diff(b.query_start))), 57, len(b.context_lens) - 1]
-    rows, starts = _sub_batch(b, idx)
-    ref = oracle.prefill(b.query[rows], kc, vc, b.block_tables[idx], b.context_lens[idx], starts,
-                         b.scale, b.dtype)
-    _assert_close(to_host_f64(out)[rows], ref, b.dtype, name)
+    outs = {}
+    for entry, ps in (("plain", None), ("shared", w.cached_tokens)):
+        for od in (None, torch.float32):
+            db = DevicePrefill(b, out_dtype=od, shared_prefix_tokens=ps)
+            out = db.step()
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+            assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+            outs[(entry, "f32" if od is not None else b.dtype)] = to_host_f64(out)
+            del db
+    ref = oracle_runs.prefill_all(b.query, kc, vc, b.block_tables, b.context_lens,
+                                  b.query_start, b.scale, b.dtype)
+    for (entry, od), got in outs.items():
+        _assert_close(got, ref, od, "%s %s, %s out" % (name, entry, od))
+        rowmax = np.abs(ref).max(axis=-1, keepdims=True)
+        # also 2e-3 relative to each row's largest output (a wrong prompt
+        # block moves long-context rows by less than the absolute bar)
+        rel = ATOL * rowmax
+        if od != "f32":
+            a = np.maximum(np.abs(ref), 2.0 ** -14)
+            rel = rel + 2.0 ** (np.floor(np.log2(a)) - {"f16": 10, "bf16": 7}[od])
+        assert (np.abs(got - ref) <= rel).all(), "%s %s, %s out: relative bar" % (name, entry, od)
 
 
 @pytest.mark.parametrize("entry", ["plain", "shared"])
