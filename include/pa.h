@@ -24,8 +24,9 @@
  *     dense and row-major in the layouts stated below, 16-byte aligned.
  *     The library allocates nothing and keeps no data between calls. It
  *     does cache, per process, facts of each device it has run on (the
- *     number of compute units, each kernel's resident workgroups), under a
- *     lock; they never change while the process runs.
+ *     number of compute units, each kernel's resident workgroups, the
+ *     address of pa_decode_split_noalloc's scratch array), under a lock;
+ *     they never change while the process runs.
  *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the default
  *     stream); nothing is synchronised. Calls that write the same buffers
  *     race if they overlap on different streams.
@@ -208,6 +209,34 @@ pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                           int block_size, int max_blocks_per_seq, int num_blocks,
                           float scale, pa_dtype kv_dtype, int partition_size,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_split_noalloc - pa_decode_split for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments and result as pa_decode_split, without the workspace: the
+ * partitions' rows go to a scratch array that the library keeps in device
+ * memory, PA_DECODE_NOALLOC_MAX_WORKSPACE bytes on each GPU it runs on,
+ * from the first call on that GPU until the process ends. Sizes whose
+ * pa_decode_split_workspace_bytes(...) exceeds that return PA_ERR_WORKSPACE
+ * before anything touches the device. Nothing is allocated: no hipMalloc,
+ * no hipFree, no allocating library call (the first call on a device looks
+ * up the array's address once). Every call on one GPU shares its array,
+ * which keeps the last call's partial rows; nothing in it needs to start at
+ * zero. Calls that overlap in time on one GPU (on different streams, or
+ * from different host threads) race on the array and give unspecified
+ * results: serialise them, e.g. on one stream. Two launches on `stream`, as
+ * pa_decode_split.
+ */
+#define PA_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+pa_status pa_decode_split_noalloc(void* out, pa_dtype out_dtype, const void* query,
+                                  const void* key_cache, const void* value_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int num_blocks,
+                                  float scale, pa_dtype kv_dtype, int partition_size,
+                                  void* stream);
 
 /*
  * pa_prefill - causal attention of each sequence's new tokens over its paged

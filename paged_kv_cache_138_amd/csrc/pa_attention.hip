@@ -540,6 +540,89 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
                         stream, "pa_decode_split (merge)");
 }
 
+// ---------------------------------------------------------------------------
+// pa_decode_split_noalloc: the split path with its workspace in a scratch
+// array of the library's own, for callers that cannot allocate
+// ---------------------------------------------------------------------------
+
+// The partitions' (max, sum, output) rows of pa_decode_split_noalloc. Each
+// GPU the library runs on holds its own copy, from the code object's load
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the address hipGetSymbolAddress returns for
+// the current device (scratch_address), never the array's name.
+static constexpr size_t kScratchBytes = PA_DECODE_NOALLOC_MAX_WORKSPACE;  // pa.h
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, set on its first call
+
+// Device address of the current device's scratch array (looked up once per
+// device, with that device current).
+pa_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    PA_REQUIRE(e == hipSuccess, PA_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+    PA_REQUIRE(dev >= 0 && dev < kMaxDevices, PA_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        PA_REQUIRE(e == hipSuccess && p, PA_ERR_LAUNCH,
+                   "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                   hipGetErrorString(e));
+        PA_REQUIRE((reinterpret_cast<uintptr_t>(p) & 255u) == 0, PA_ERR_LAUNCH,
+                   "scratch array is not 256-byte aligned");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_split_noalloc(void* out, pa_dtype out_dtype, const void* query,
+                                             const void* key_cache, const void* value_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, int num_seqs,
+                                             int num_heads, int num_kv_heads, int head_dim,
+                                             int block_size, int max_blocks_per_seq,
+                                             int num_blocks, float scale, pa_dtype kv_dtype,
+                                             int partition_size, void* stream) {
+    clear_error();
+    const DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks};
+    pa_status st = validate_decode(out, out_dtype, query, key_cache, value_cache, block_tables,
+                                   context_lens, s, scale, kv_dtype);
+    if (st != PA_OK) return st;
+    PA_REQUIRE(partition_size > 0 && partition_size % block_size == 0, PA_ERR_SHAPE,
+               "partition_size %d must be a positive multiple of block_size %d", partition_size,
+               block_size);
+    SplitLayout lay;
+    split_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
+                 &lay);
+    // checked before the device is touched
+    PA_REQUIRE(lay.total <= kScratchBytes, PA_ERR_WORKSPACE,
+               "pa_decode_split_noalloc: these sizes need %zu bytes of workspace, more than the "
+               "%zu-byte scratch array (use pa_decode_split with a caller workspace)",
+               lay.total, kScratchBytes);
+    if (num_seqs == 0) return PA_OK;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+    st = launch_partitions(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           context_lens, s, scale, kv_dtype, partition_size, 0, ws, lay.total,
+                           stream, "pa_decode_split_noalloc (partitions)", &lay);
+    if (st != PA_OK) return st;
+    char* w = (char*)ws;
+    return launch_merge(out, out_dtype, (const float*)(w + lay.off_out),
+                        (const float*)(w + lay.off_max), (const float*)(w + lay.off_sum),
+                        context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
+                        stream, "pa_decode_split_noalloc (merge)");
+}
+
 namespace {
 
 // the partition launch of the fused-append calls (validates the new rows)

@@ -60,6 +60,8 @@ def load():
     lib.pa_decode.restype = i32
     lib.pa_decode_split.argtypes = dec + [i32, vp, sz, vp]
     lib.pa_decode_split.restype = i32
+    lib.pa_decode_split_noalloc.argtypes = dec + [i32, vp]
+    lib.pa_decode_split_noalloc.restype = i32
     lib.pa_decode_partitions.argtypes = dec + [i32, vp, sz, vp]
     lib.pa_decode_partitions.restype = i32
     lib.pa_decode_partitions_shared_prefix.argtypes = dec + [i32, i32, vp, sz, vp]
@@ -303,6 +305,25 @@ def decode_split(query, key_cache, value_cache, block_tables, context_lens, scal
     """Paged decode attention as partitions + log-sum-exp merge."""
     return _split_call("pa_decode_split", query, key_cache, value_cache, block_tables, context_lens,
                        scale, partition_size, workspace, out, out_dtype)
+
+
+# bytes of the scratch array pa_decode_split_noalloc uses (PA_DECODE_NOALLOC_MAX_WORKSPACE)
+NOALLOC_MAX_WORKSPACE = 32 << 20
+
+
+def decode_split_noalloc(query, key_cache, value_cache, block_tables, context_lens, scale,
+                         partition_size=512, out=None):
+    """decode_split without a workspace: the partials go to the library's own
+    scratch array on the device (pa_decode_split_noalloc), so nothing is
+    allocated when `out` is given. Calls overlapping in time on one GPU race."""
+    out, (B, Hq, Hkv, D, BS, MB, NB) = _decode_common(
+        query, key_cache, value_cache, block_tables, context_lens, out, None)
+    st = load().pa_decode_split_noalloc(
+        _ptr(out), _DT[out.dtype], _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, BS, MB, NB, float(scale),
+        _DT[key_cache.dtype], int(partition_size), _stream(query))
+    _check(st, "pa_decode_split_noalloc")
+    return out
 
 
 def decode_split_append(query, key_cache, value_cache, block_tables, context_lens, new_key, new_value,

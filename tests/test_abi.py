@@ -92,6 +92,30 @@ def test_split_rejects_bad_partition_and_workspace(lib):
     assert lib.pa_decode_split(*args, 64, p, 16, None) == 5
 
 
+def test_noalloc_split_rejects_sizes_beyond_its_scratch_array(lib):
+    # pa_decode_split_noalloc checks its workspace need against the scratch
+    # array before it touches the device (dummy pointers are never read)
+    p = 1 << 12
+    cap = palib.NOALLOC_MAX_WORKSPACE
+    m = re.search(r"#define PA_DECODE_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == cap
+    fits = [p, 2, p, p, p, p, p, 2, 8, 8, 128, 16, 8, 64, 0.1, 0]
+    assert lib.pa_decode_split_workspace_bytes(2, 8, 128, 8, 16, 64) <= cap
+    assert lib.pa_decode_split(*fits, 24, p, 1 << 20, None) == 2
+    assert lib.pa_decode_split_noalloc(*fits, 24, None) == 2        # partition not a multiple of 16
+    assert lib.pa_decode_split_noalloc(*[None if i in (0, 2) else a for i, a in enumerate(fits)],
+                                       64, None) == 1                 # null out and query
+    # 128 sequences x 64 heads, 8192-token tables in 512-token partitions:
+    # 16 partitions x 8192 rows x (128 + 2) floats, past the 32 MiB array
+    big = [p, 2, p, p, p, p, p, 128, 64, 8, 128, 16, 512, 65536, 0.1, 1]
+    need = lib.pa_decode_split_workspace_bytes(128, 64, 128, 512, 16, 512)
+    assert need > cap
+    assert lib.pa_decode_split_noalloc(*big, 512, None) == 5
+    assert b"scratch" in lib.pa_last_error()
+    assert lib.pa_decode_split_noalloc(*big[:7], 0, *big[8:], 512, None) == 0  # empty batch
+
+
 def test_fused_append_rejects_bad_new_rows(lib):
     # host-side checks run before any launch, so dummy (never dereferenced)
     # pointers suffice
