@@ -7,13 +7,13 @@ CPU oracle can both be fed from it.
 
 Host bookkeeping follows the pages:
 
-* Free-list allocator: the free list starts as the (shuffled) block ids;
-  allocation pops from the front, freeing appends to the back, and a request
-  that needs more blocks than are free raises an out-of-memory error
-  ("vLLM PagedAttention深度解析与工程实践" §3.2 Block Manager 的核心流程).
-* Per-sequence table growth: a new token takes a fresh block exactly when
-  the token count is a multiple of the block size (lqnn.cn/news/170268
-  §2.2, BlockTable.append_token).
+* Free-list order: blocks are handed out in the order of the (shuffled)
+  free list and freed blocks rejoin it at the end; a request that needs more
+  blocks than are free fails with an out-of-memory error ("vLLM
+  PagedAttention深度解析与工程实践" §3.2, the block manager's flow).
+* Table growth: a token whose position is a multiple of the block size
+  opens a new block; the others fill the sequence's last block
+  (lqnn.cn/news/170268 §2.2, appending a token to a block table).
 * Shared prefix blocks are referenced by several tables at once and carry a
   reference count (lqnn.cn/news/170268 §3.2; "vLLM 核心：PagedAttention 与
   Continuous Batching" §3 Prefix Caching).
@@ -28,6 +28,7 @@ to nearest-even into fp16 / bf16. bf16 arrays are carried as uint16 bit
 patterns.
 """
 
+from collections import deque
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 import math
@@ -104,38 +105,54 @@ class OutOfBlocks(RuntimeError):
     """The free list cannot satisfy an allocation (preemption territory)."""
 
 
+def blocks_for(num_tokens, block_size):
+    """Blocks of block_size slots that hold num_tokens tokens."""
+    return -(-int(num_tokens) // int(block_size))
+
+
 class BlockManager:
-    """Free-list allocator: pop from the front, return to the back."""
+    """Reference-counted physical blocks over a first-in first-out free list.
+
+    Blocks leave the free list from its head and return to its tail, so a
+    freshly shuffled list hands out blocks in its shuffled order and a freed
+    block is reused only after every block that was free before it. A block
+    returns to the list when the last table holding it lets it go.
+    """
 
     def __init__(self, free_blocks, block_size):
-        self.free_blocks = list(int(b) for b in free_blocks)
+        self.free_blocks = deque(int(b) for b in free_blocks)
         self.block_size = int(block_size)
-        self.allocated = {}   # seq id -> list of physical blocks
-        self.refcount = {}    # physical block -> number of tables using it
+        self.allocated = {}   # seq id -> its table: physical blocks in logical order
+        self.refcount = {}    # physical block -> number of tables holding it
 
-    def _pop(self):
-        if not self.free_blocks:
-            raise OutOfBlocks("no free KV block left")
-        b = self.free_blocks.pop(0)
-        self.refcount[b] = 1
-        return b
+    def take(self, n):
+        """The n blocks at the head of the free list, each held once."""
+        if n > len(self.free_blocks):
+            raise OutOfBlocks("need %d blocks, %d free" % (n, len(self.free_blocks)))
+        got = [self.free_blocks.popleft() for _ in range(n)]
+        self.refcount.update((b, 1) for b in got)
+        return got
+
+    def release(self, blocks):
+        """Drop one reference to each block; blocks nobody holds go back to
+        the tail of the free list, in the order given."""
+        for b in blocks:
+            self.refcount[b] -= 1
+        idle = [b for b in blocks if self.refcount[b] == 0]
+        for b in idle:
+            del self.refcount[b]
+        self.free_blocks.extend(idle)
 
     def allocate(self, seq_id, num_tokens):
-        """Grow seq_id's table until it holds num_tokens tokens."""
-        have = len(self.allocated.get(seq_id, [])) * self.block_size
-        if have >= num_tokens:
-            return
-        need = -(-(num_tokens - have) // self.block_size)
-        if len(self.free_blocks) < need:
-            raise OutOfBlocks("need %d blocks, %d free" % (need, len(self.free_blocks)))
-        for _ in range(need):
-            self.allocated.setdefault(seq_id, []).append(self._pop())
+        """Extend seq_id's table to cover num_tokens tokens (never shrinks)."""
+        table = self.allocated.setdefault(seq_id, [])
+        table.extend(self.take(max(blocks_for(num_tokens, self.block_size) - len(table), 0)))
 
     def share(self, seq_id, blocks):
-        """Point seq_id's table at existing blocks (shared, read-only)."""
+        """Append existing blocks to seq_id's table (held, not copied)."""
         for b in blocks:
             self.refcount[b] = self.refcount.get(b, 0) + 1
-            self.allocated.setdefault(seq_id, []).append(int(b))
+        self.allocated.setdefault(seq_id, []).extend(int(b) for b in blocks)
 
     def fork(self, parent_id, child_id):
         """child_id starts as a copy of parent_id's table: every block shared.
@@ -148,27 +165,27 @@ class BlockManager:
     def append_slot(self, seq_id, position):
         """Slot of seq_id's token at `position` (tokens 0 .. position-1 held).
 
-        A new block is taken when the token opens one. A token that lands in a
-        block other tables still reference is written to a fresh copy of that
-        block instead (copy-on-write: shared content stays read-only and is
-        copied only when written); the copy replaces the block in this table
-        and the pair (source block, new block) is returned for the device
-        copy. The last table still holding a block writes in place. Returns
-        (slot, (src, dst) or None)."""
-        blocks = self.allocated.setdefault(seq_id, [])
+        A position past the table's last block gets a new block. A token that
+        lands in a block other tables still reference is written to a fresh
+        copy of that block instead (copy-on-write: shared content stays
+        read-only and is copied only when written); the copy replaces the
+        block in this table and the pair (source block, new block) is
+        returned for the device copy. The last table still holding a block
+        writes in place. Returns (slot, (src, dst) or None)."""
+        table = self.allocated.setdefault(seq_id, [])
         idx, off = divmod(int(position), self.block_size)
-        if idx == len(blocks):
-            blocks.append(self._pop())
-            return blocks[idx] * self.block_size + off, None
-        if idx != len(blocks) - 1:
+        if idx == len(table):
+            table.extend(self.take(1))
+            return table[idx] * self.block_size + off, None
+        if idx != len(table) - 1:
             raise ValueError("position %d is not the next token of the table" % position)
-        last = blocks[idx]
-        if self.refcount[last] > 1:
-            new = self._pop()
-            self.refcount[last] -= 1
-            blocks[idx] = new
-            return new * self.block_size + off, (last, new)
-        return last * self.block_size + off, None
+        held = table[idx]
+        if self.refcount[held] == 1:
+            return held * self.block_size + off, None
+        (copy,) = self.take(1)
+        self.release([held])
+        table[idx] = copy
+        return copy * self.block_size + off, (held, copy)
 
     def move_out(self, seq_id, other):
         """Move seq_id's blocks into the pool managed by `other` (the swap-out
@@ -176,40 +193,17 @@ class BlockManager:
         request's KV blocks are copied to CPU memory and its GPU blocks freed).
         Returns the (block here, block there) pairs to copy. The blocks keep
         their logical order in the sequence's new table."""
-        if any(self.refcount[b] > 1 for b in self.allocated.get(seq_id, [])):
-            raise ValueError("shared blocks stay resident: only a table's private blocks move")
         mine = list(self.allocated.get(seq_id, []))
-        if len(other.free_blocks) < len(mine):
-            raise OutOfBlocks("need %d blocks there, %d free" % (len(mine), len(other.free_blocks)))
-        theirs = [other._pop() for _ in mine]
+        if any(self.refcount[b] > 1 for b in mine):
+            raise ValueError("shared blocks stay resident: only a table's private blocks move")
+        theirs = other.take(len(mine))
         other.allocated[seq_id] = theirs
         self.free(seq_id)
         return list(zip(mine, theirs))
 
     def free(self, seq_id):
-        for b in self.allocated.pop(seq_id, []):
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                del self.refcount[b]
-                self.free_blocks.append(b)
-
-
-class SequenceTable:
-    """One sequence's table that grows by one token at a time."""
-
-    def __init__(self, block_size):
-        self.block_size = int(block_size)
-        self.physical_blocks = []
-        self.num_tokens = 0
-
-    def append_token(self, allocate_block):
-        """Take a new block when the current ones are full; return the slot."""
-        if self.num_tokens % self.block_size == 0:
-            self.physical_blocks.append(int(allocate_block()))
-        blk = self.physical_blocks[self.num_tokens // self.block_size]
-        slot = blk * self.block_size + self.num_tokens % self.block_size
-        self.num_tokens += 1
-        return slot
+        """Let go of seq_id's whole table."""
+        self.release(self.allocated.pop(seq_id, []))
 
 
 def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype_bytes):
@@ -361,35 +355,44 @@ def make_batch(workload, seed=0, lens=None, poison="nan", unallocated="zero"):
     if ctx.max(initial=0) > w.max_blocks_per_seq * BS:
         raise ValueError("context longer than max_blocks_per_seq * block_size")
     # -- block tables --------------------------------------------------------
+    # The pool hands out blocks in the order of a seeded shuffle of its ids.
+    # Every sequence holds its history (positions 0 .. L-2) from earlier
+    # steps: first the shared prefix blocks, if any, then its private
+    # blocks, taken in sequence order. This step's token (position L-1)
+    # takes one more block, after all the histories, when it is the first
+    # token of a block (L-1 a multiple of BS); otherwise it fills the last
+    # history block.
     free = rng.permutation(w.num_blocks)
-    mgr = BlockManager(free, BS)
-    shared = []
-    if w.shared_prefix_tokens:
-        if w.shared_prefix_tokens % BS:
-            raise ValueError("shared prefix must be whole blocks")
-        mgr.allocate("prefix", w.shared_prefix_tokens)
-        shared = list(mgr.allocated["prefix"])
-    tables = []
-    for i in range(B):
-        t = SequenceTable(BS)
-        hist = int(ctx[i]) - 1 if ctx[i] > 0 else 0
-        if shared:
-            mgr.share(i, shared)
-            t.physical_blocks = list(shared)
-            t.num_tokens = w.shared_prefix_tokens
-        mgr.allocate(i, hist)
-        t.physical_blocks = list(mgr.allocated.get(i, []))
-        t.num_tokens = hist
-        tables.append(t)
-    if shared:
-        mgr.free("prefix")  # the prefix stays alive through the sequences' references
-    slots = np.full(B, -1, dtype=np.int64)
-    for i in range(B):
-        if ctx[i] > 0:
-            slots[i] = tables[i].append_token(lambda i=i: _grow(mgr, i))
+    npre = -(-w.shared_prefix_tokens // BS)
+    if w.shared_prefix_tokens % BS:
+        raise ValueError("shared prefix must be whole blocks")
+    hist = np.maximum(ctx - 1, 0)
+    own_hist = -(-np.maximum(hist - w.shared_prefix_tokens, 0) // BS)  # private history blocks
+    opens = (ctx > 0) & (hist % BS == 0) & (hist >= w.shared_prefix_tokens)
+    need = npre + int(own_hist.sum()) + int(opens.sum())
+    if need > w.num_blocks:
+        raise OutOfBlocks("need %d blocks, %d in the pool" % (need, w.num_blocks))
+    shared = [int(b) for b in free[:npre]]
+    hist_start = npre + np.concatenate([[0], np.cumsum(own_hist)[:-1]]).astype(np.int64)
+    new_at = npre + int(own_hist.sum()) + np.cumsum(opens) - 1
     bt = np.full((B, w.max_blocks_per_seq), -1, dtype=np.int32)
-    for i, t in enumerate(tables):
-        bt[i, :len(t.physical_blocks)] = t.physical_blocks
+    slots = np.full(B, -1, dtype=np.int64)
+    # every block in use, the shared ones first, then each sequence's own
+    # in table order (the order their contents are drawn in)
+    order = list(shared)
+    refcount = {b: B for b in shared}
+    tables_blocks = []
+    for i in range(B):
+        own = [int(b) for b in free[hist_start[i]:hist_start[i] + own_hist[i]]]
+        if opens[i]:
+            own.append(int(free[new_at[i]]))
+        row = shared + own
+        bt[i, :len(row)] = row
+        tables_blocks.append(row)
+        if ctx[i] > 0:
+            slots[i] = row[hist[i] // BS] * BS + hist[i] % BS
+        refcount.update((b, 1) for b in own)
+        order += own
     # -- element data (built as uint16 bit patterns) -------------------------
     D, Hq, Hkv = w.head_dim, w.num_heads, w.num_kv_heads
     q = _bits(encode(_normal(seed, STREAM_Q, 0, (B, Hq, D)), w.dtype))
@@ -400,13 +403,6 @@ def make_batch(workload, seed=0, lens=None, poison="nan", unallocated="zero"):
     else:
         key_cache = np.zeros(pool, dtype=np.uint16)
         value_cache = np.zeros(pool, dtype=np.uint16)
-    order = []
-    seen = set()
-    for t in tables:
-        for b in t.physical_blocks:
-            if b not in seen:
-                seen.add(b)
-                order.append(b)
     order = np.asarray(order, dtype=np.int64)
     _fill_blocks(seed, STREAM_K, key_cache, order, w.dtype)
     _fill_blocks(seed, STREAM_V, value_cache, order, w.dtype)
@@ -419,7 +415,7 @@ def make_batch(workload, seed=0, lens=None, poison="nan", unallocated="zero"):
             L = int(ctx[i])
             if L <= 0:
                 continue
-            last = tables[i].physical_blocks[(L - 1) // BS]
+            last = tables_blocks[i][(L - 1) // BS]
             off = (L - 1) % BS
             key_cache[last, off:] = pv
             value_cache[last, off:] = pv
@@ -429,14 +425,7 @@ def make_batch(workload, seed=0, lens=None, poison="nan", unallocated="zero"):
     scale = 1.0 / math.sqrt(D)
     return Batch(w, q, key_cache, value_cache, bt, ctx.astype(np.int32), new_key,
                  new_value, slots, scale, order, np.asarray(shared, dtype=np.int64),
-                 dict(mgr.refcount))
-
-
-def _grow(mgr, seq_id):
-    """Take one block from the free list for seq_id's table."""
-    b = mgr._pop()
-    mgr.allocated.setdefault(seq_id, []).append(b)
-    return b
+                 refcount)
 
 
 # ---------------------------------------------------------------------------

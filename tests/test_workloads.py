@@ -1,9 +1,11 @@
 """Host bookkeeping and the seeded generators (no attention arithmetic).
 
-Pins: the free-list allocator of "vLLM PagedAttention深度解析与工程实践"
-§3.2 (pop front, append back, out-of-memory error), the append rule of
-lqnn.cn/news/170268 §2.2, reference counts of shared prefix blocks, the KV
-byte sizes and the reservation example printed on the pages.
+Pins: the free-list order of "vLLM PagedAttention深度解析与工程实践" §3.2
+(blocks leave from the front, freed blocks return to the back, a request
+that needs more than is free fails), the rule that a token takes a new block
+exactly when it opens one (lqnn.cn/news/170268 §2.2), reference counts of
+shared prefix blocks, the KV byte sizes and the reservation example printed
+on the pages.
 """
 
 import json
@@ -32,19 +34,49 @@ def test_free_list_pops_front_and_frees_to_back():
     m.allocate("b", 1)
     assert m.allocated["b"] == [3]
     m.free("a")
-    assert m.free_blocks == [5, 7, 1, 12]
+    assert list(m.free_blocks) == [5, 7, 1, 12]
     with pytest.raises(W.OutOfBlocks):
         m.allocate("c", 16 * 5)
 
 
-def test_append_token_takes_a_new_block_exactly_at_block_boundaries():
-    pool = iter(range(100, 200))
-    t = W.SequenceTable(4)
-    slots = [t.append_token(lambda: next(pool)) for _ in range(10)]
-    assert t.physical_blocks == [100, 101, 102]
-    assert slots == [400, 401, 402, 403, 404, 405, 406, 407, 408, 409]
-    # the printed 4-slot example: 10 tokens fill 4/4/2
-    assert t.num_tokens == 10 and oracle.unused_slots(10, 4) == 2
+def test_a_token_takes_a_new_block_exactly_at_block_boundaries():
+    # tokens appended one by one at block size 4: positions 0, 4 and 8 open
+    # blocks, the others fill the current one ("vLLM 核心：PagedAttention 与
+    # Continuous Batching" §3: 10 tokens fill 4/4/2)
+    m = W.BlockManager(range(100, 200), 4)
+    got = [m.append_slot("s", pos) for pos in range(10)]
+    assert [slot for slot, _ in got] == list(range(400, 410))
+    assert all(cow is None for _, cow in got)
+    assert m.allocated["s"] == [100, 101, 102]
+    assert oracle.unused_slots(10, 4) == 4 * len(m.allocated["s"]) - 10 == 2
+
+
+def test_batch_tables_follow_the_append_rule():
+    # make_batch builds every table at once; its new token (position L-1)
+    # must sit where growing the table token by token would put it, and it
+    # opens a fresh block exactly when L-1 is a multiple of the block size
+    w = W.custom_workload("grow", num_seqs=40, num_heads=2, num_kv_heads=2, head_dim=64,
+                          block_size=8, num_blocks=512, max_blocks_per_seq=16,
+                          lens="uniform:1:120")
+    b = W.make_batch(w, seed=4)
+    for i in range(w.num_seqs):
+        L = int(b.context_lens[i])
+        nb = oracle.blocks_needed(L, 8)
+        row = [int(x) for x in b.block_tables[i, :nb]]
+        m = W.BlockManager(row, 8)
+        slots = [m.append_slot(i, pos)[0] for pos in range(L)]
+        assert m.allocated[i] == row
+        assert int(b.slot_mapping[i]) == slots[-1]
+    # the history blocks of all sequences come first, then this step's new blocks
+    opened = [i for i in range(w.num_seqs) if (int(b.context_lens[i]) - 1) % 8 == 0]
+    last_new = [int(b.block_tables[i, (int(b.context_lens[i]) - 1) // 8]) for i in opened]
+    hist_blocks = [int(x) for i in range(w.num_seqs) for x in
+                   b.block_tables[i, :oracle.blocks_needed(int(b.context_lens[i]) - 1, 8)]]
+    perm = np.random.default_rng(4)
+    perm.integers(1, 120, endpoint=True, size=w.num_seqs)
+    perm = [int(x) for x in perm.permutation(512)]
+    assert hist_blocks == perm[:len(hist_blocks)]
+    assert last_new == perm[len(hist_blocks):len(hist_blocks) + len(opened)]
 
 
 def test_kv_sizes_printed_on_the_pages():
@@ -181,7 +213,7 @@ def test_swap_out_and_back_keeps_the_table_order():
     before = list(gpu.allocated["a"])
     out = gpu.move_out("a", host)
     assert [g for g, _ in out] == before
-    assert "a" not in gpu.allocated and all(b in gpu.free_blocks[-7:] for b in before)
+    assert "a" not in gpu.allocated and all(b in list(gpu.free_blocks)[-7:] for b in before)
     assert host.allocated["a"] == [h for _, h in out]
     gpu.allocate("c", 16 * 30)                  # someone takes free blocks meanwhile
     back = host.move_out("a", gpu)
