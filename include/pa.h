@@ -200,7 +200,7 @@ size_t pa_decode_split_workspace_bytes(int num_seqs, int num_heads, int head_dim
  *                     workspace must not overlap in time.
  *
  * Two launches on `stream`: pa_decode_partitions, then pa_lse_merge over the
- * workspace (the merge skips sequences with a single partition).
+ * workspace (the merge skips sequences that one workgroup covered whole).
  */
 pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* query,
                           const void* key_cache, const void* value_cache,
@@ -363,11 +363,17 @@ pa_status pa_decode_partitions_append(void* out, pa_dtype out_dtype, const void*
  * Same arguments as pa_decode_split. One workgroup handles one partition of
  * one (sequence, head) - of two adjacent heads when the grid is large
  * compared with the device, and of one (sequence, kv head) when 2..16 query
- * heads share a kv head. A sequence with a single partition (L_i <= partition_size)
- * gets its final output in `out`; for the others each partition p stores its
- * row of the workspace: part_max = the largest scaled logit (natural-log
- * units), part_sum = Σ exp(s - part_max), part_out = the normalised partial
- * output. pa_lse_merge then finishes `out`.
+ * heads share a kv head; a grouped-query workgroup may walk 2 or 4
+ * consecutive partitions when the grid is large. Every partition
+ * p < ceil(L_i / partition_size) of every row gets its workspace row:
+ * part_max = the largest scaled logit (natural-log units), part_sum =
+ * Σ exp(s - part_max), part_out = the normalised partial output, over the
+ * partition's tokens - or over a group of consecutive partitions, whose
+ * first row then holds the group and whose other rows are marked empty
+ * (part_max = -inf, part_sum = 0, part_out not written). A sequence that one
+ * workgroup covered whole (L_i <= partition_size, or within one group) also
+ * gets its final output in `out`. pa_lse_merge over the workspace then
+ * gives `out` for every row.
  */
 pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
                                const void* key_cache, const void* value_cache,
@@ -425,7 +431,8 @@ pa_status pa_decode_split_shared_prefix(void* out, pa_dtype out_dtype, const voi
  *             scaled logit scale·q·k of partition p (natural-log units).
  *   part_sum  float [num_seqs, num_heads, max_partitions]: l_p = Σ exp(s - m_p).
  *   part_out  float [num_seqs, num_heads, max_partitions, head_dim]:
- *             o_p = Σ exp(s - m_p) v / l_p.
+ *             o_p = Σ exp(s - m_p) v / l_p. A partition with m_p = -inf is
+ *             empty: it adds nothing and its o_p is not read.
  *   context_lens  int32 [num_seqs]; sequence i uses partitions
  *             p < ceil(L_i / partition_size).
  *

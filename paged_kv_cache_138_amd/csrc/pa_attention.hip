@@ -36,10 +36,10 @@ struct MergeArgs {
     int num_heads;
     int max_partitions;
     int partition_size;
-    // 0: rows of sequences with at most one partition are skipped (the split
-    // paths, whose partition launch wrote them); 1: every row is written,
-    // a single partition's output copied and an empty context as zeros
-    int complete;
+    // rows of sequences with at most this many partitions are left alone:
+    // the split paths' partition launch wrote their output (one workgroup
+    // covered the whole context); 0 writes every row (pa_lse_merge)
+    int skip_parts;
 };
 
 // A row (one query head of one sequence) with np <= 1 partitions: whether
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     if (L < 0) L = 0;
     int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
     if (np > a.max_partitions) np = a.max_partitions;
-    if (np <= 1 && !a.complete) return;
+    if (a.skip_parts > 0 && np <= a.skip_parts) return;
     const size_t r = (size_t)row * a.max_partitions;
     float o;
     if (!merge_trivial_row(a, np, r, D, d, &o))
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void lse_merge_wave_kernel(MergeArgs a) {
     if (L < 0) L = 0;
     int np = (int)(((int64_t)L + a.partition_size - 1) / a.partition_size);
     if (np > a.max_partitions) np = a.max_partitions;
-    if (np <= 1 && !a.complete) return;
+    if (a.skip_parts > 0 && np <= a.skip_parts) return;
     const size_t r = (size_t)row * a.max_partitions;
 #pragma unroll
     for (int d = lane; d < D; d += 64) {
@@ -134,6 +134,21 @@ int gqa_heads_log2(int num_kv_heads) {
     while ((2 << hl) <= PA_GQA_HEADS && (2 << hl) <= kGqaWaves && num_kv_heads % (2 << hl) == 0)
         ++hl;
     return hl;
+}
+
+// Consecutive partitions one grouped-query workgroup walks (1, 2 or 4).
+// Each workgroup writes one fp32 row per query head to the workspace; such
+// stores, arriving while the device streams the cache at full bandwidth,
+// cost far more time than their share of the bytes (measured on MI355X with
+// 64 q / 8 kv heads, contexts of 1k-8k tokens: 452 / 431 / 416 us per launch
+// for partitions walked in groups of 1 / 2 / 4). Grouping keeps the
+// partition as the unit of the workspace and the merge; it is used while the
+// grid of groups (for the longest table) still holds at least two rounds of
+// the workgroups the device runs at once.
+int gqa_group(int parts, int64_t units, int resident) {
+    for (int k = 4; k > 1; k /= 2)
+        if (parts >= 2 * k && units * ceil_div(parts, k) >= (int64_t)2 * resident) return k;
+    return 1;
 }
 
 // Workgroups of fn that fit on the current device at once (at least 1).
@@ -279,6 +294,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct SplitLayout {
     int np;
     size_t off_max, off_sum, off_out, total;
+    int group;  // partitions one workgroup walked (set by the partition launch)
 };
 
 bool split_layout(int num_seqs, int num_heads, int head_dim, int max_blocks_per_seq,
@@ -290,6 +306,7 @@ bool split_layout(int num_seqs, int num_heads, int head_dim, int max_blocks_per_
     const int np = (int)((lmax + partition_size - 1) / partition_size);
     const size_t rows = (size_t)num_seqs * num_heads * np;
     lay->np = np;
+    lay->group = 1;
     lay->off_max = 0;
     lay->off_sum = lay->off_max + align256(rows * sizeof(float));
     lay->off_out = lay->off_sum + align256(rows * sizeof(float));
@@ -413,7 +430,7 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     int per_seq = 0, threads = 0;
     attn_fn fn = pick_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size, s.num_heads,
                              s.num_kv_heads, 0, &per_seq, &threads);
-    int hl = 0;
+    int hl = 0, group = 1;
     if (fn && !use_gqa(s.num_heads, s.num_kv_heads)) {
         const int64_t rect = (int64_t)s.num_seqs * s.num_heads * (lay.np - prefix_parts);
         hl = mha_heads_log2(s.num_heads, rect, resident_workgroups((const void*)fn, threads),
@@ -422,6 +439,8 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     } else if (fn) {
         hl = gqa_heads_log2(s.num_kv_heads);
         per_seq = s.num_kv_heads >> hl;
+        group = gqa_group(lay.np - prefix_parts, (int64_t)s.num_seqs * per_seq,
+                          resident_workgroups((const void*)fn, threads));
     }
     attn_fn pfn = prefix_tokens > 0 ? pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim,
                                                          s.block_size)
@@ -437,6 +456,8 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     a.max_partitions = lay.np;
     a.prefix_tokens = prefix_tokens;
     a.heads_log2 = hl;
+    a.parts_per_wg = group;
+    lay_out->group = group;
     if (app) {
         a.new_key = (const uint16_t*)app->new_key;
         a.new_value = (const uint16_t*)app->new_value;
@@ -456,7 +477,8 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
         st = check_launch(what);
         if (st != PA_OK) return st;
     }
-    const int64_t grid = (int64_t)s.num_seqs * per_seq * (lay.np - prefix_parts);
+    const int64_t grid =
+        (int64_t)s.num_seqs * per_seq * ceil_div(lay.np - prefix_parts, group);
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     if (grid == 0) return PA_OK;
     a.part_begin = prefix_parts;
@@ -468,11 +490,11 @@ pa_status launch_merge(void* out, pa_dtype out_dtype, const float* part_out,
                        const float* part_max, const float* part_sum,
                        const int32_t* context_lens, int num_seqs, int num_heads, int head_dim,
                        int max_partitions, int partition_size, void* stream, const char* what,
-                       bool complete = false) {
+                       int skip_parts) {
     merge_fn mfn = pick_merge(out_dtype, head_dim);
     PA_REQUIRE(mfn, PA_ERR_UNSUPPORTED, "no merge instance");
     MergeArgs m{out,      part_out,      part_max, part_sum, context_lens, num_seqs,
-                num_heads, max_partitions, partition_size, complete ? 1 : 0};
+                num_heads, max_partitions, partition_size, skip_parts};
     const int64_t rows = (int64_t)num_seqs * num_heads;
     const int64_t rpw = head_dim % 64 == 0 ? 256 / head_dim : 4;  // rows per workgroup
     const int64_t grid = (rows + rpw - 1) / rpw;
@@ -537,7 +559,7 @@ extern "C" pa_status pa_decode_split(void* out, pa_dtype out_dtype, const void* 
     return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
                         (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
                         context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
-                        stream, "pa_decode_split (merge)");
+                        stream, "pa_decode_split (merge)", lay.group);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,7 +642,7 @@ extern "C" pa_status pa_decode_split_noalloc(void* out, pa_dtype out_dtype, cons
     return launch_merge(out, out_dtype, (const float*)(w + lay.off_out),
                         (const float*)(w + lay.off_max), (const float*)(w + lay.off_sum),
                         context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
-                        stream, "pa_decode_split_noalloc (merge)");
+                        stream, "pa_decode_split_noalloc (merge)", lay.group);
 }
 
 namespace {
@@ -693,7 +715,7 @@ extern "C" pa_status pa_decode_split_append(
     return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
                         (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
                         context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
-                        stream, "pa_decode_split_append (merge)");
+                        stream, "pa_decode_split_append (merge)", lay.group);
 }
 
 extern "C" pa_status pa_decode_split_shared_prefix(
@@ -715,7 +737,7 @@ extern "C" pa_status pa_decode_split_shared_prefix(
     return launch_merge(out, out_dtype, (const float*)(ws + lay.off_out),
                         (const float*)(ws + lay.off_max), (const float*)(ws + lay.off_sum),
                         context_lens, num_seqs, num_heads, head_dim, lay.np, partition_size,
-                        stream, "pa_decode_split_shared_prefix (merge)");
+                        stream, "pa_decode_split_shared_prefix (merge)", lay.group);
 }
 
 extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* part_out,
@@ -738,7 +760,7 @@ extern "C" pa_status pa_lse_merge(void* out, pa_dtype out_dtype, const float* pa
                "out and part_out must be 16-byte aligned");
     return launch_merge(out, out_dtype, part_out, part_max, part_sum, context_lens, num_seqs,
                         num_heads, head_dim, max_partitions, partition_size, stream,
-                        "pa_lse_merge", /*complete=*/true);
+                        "pa_lse_merge", /*skip_parts=*/0);
 }
 
 // ---------------------------------------------------------------------------

@@ -24,6 +24,10 @@ struct AttnArgs {
     int partition_size;
     int max_partitions;
     int part_begin;     // first partition index the grid covers
+    // grouped-query decode: consecutive partitions one workgroup walks (1, 2
+    // or 4; 0 counts as 1). Their combined state goes to the first one's
+    // workspace row, and the others' rows are marked empty.
+    int parts_per_wg;
     int prefix_tokens;  // shared-prefix mode: tokens every sequence shares (block_tables row 0)
     int heads_log2;     // MHA kernel: log2 of the query heads one workgroup serves (0, 1, 2)
     float scale_log2;  // scale * log2(e)

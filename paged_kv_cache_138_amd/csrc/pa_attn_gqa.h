@@ -200,6 +200,8 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // rows of every product: row r is query head r_head of sequence r_seq
     const int R = PREFIX ? 16 / G : 1;  // sequences per workgroup
     int seq0, part, Lsrc, nparts = 0;
+    // consecutive partitions this workgroup walks (grouped decode mode)
+    const int K = PREFIX || a.parts_per_wg < 1 ? 1 : a.parts_per_wg;
     const int32_t* bt;
     if constexpr (PREFIX) {
         const int ntiles = (a.num_seqs + R - 1) / R;
@@ -215,7 +217,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         // GQA long-context batch: 457 -> 451 µs; the one-head kernel gained
         // nothing from it)
         const int pslots = (int)(gridDim.x / ((unsigned)ngroups * (unsigned)a.num_seqs));
-        part = pslots - 1 - bid / a.num_seqs + a.part_begin;
+        part = (pslots - 1 - bid / a.num_seqs) * K + a.part_begin;
         Lsrc = ctx_len(seq0);
         nparts = (Lsrc + P - 1) / P;
         if (part > 0 && part >= nparts) return;  // uniform over the workgroup
@@ -233,7 +235,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // stored, by the workgroups of its partition 0, as the scatter would.)
     bool has_new = false, store_new = false;
     if constexpr (MODE == kModeDecode) {
-        if (a.new_key && part == max(nparts, 1) - 1) {
+        if (a.new_key && part + K >= max(nparts, 1)) {  // the group holding position L - 1
             const int64_t slot = a.slot_mapping[seq0];
             const bool slot_ok = slot >= 0 && slot < (int64_t)a.num_blocks * BS;
             has_new = slot_ok && Lsrc > 0;
@@ -250,7 +252,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             }
         }
     }
-    const int end = has_new ? Lsrc - 1 : min(start + P, Lsrc);
+    const int end = has_new ? Lsrc - 1 : min(start + K * P, Lsrc);
     const int nb = (Lsrc + BS - 1) / BS;
     auto row_seq = [&](int r) { return seq0 + r / G; };
     auto row_head = [&](int r) { return kvh * G + r % G; };
@@ -298,7 +300,12 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             const int tok0 = cs + b * RPB;
             const int lb = tok0 / BS;
             const int pid = lb < nb ? bt[lb] : -1;
-            const int rows = min(max(end - tok0, 0), RPB);
+            // the row count is uniform, but min/max compile to a vector
+            // med3; read back as a scalar, the descriptors stay in scalar
+            // registers (a descriptor the compiler takes for per-lane would
+            // wrap every load in a readfirstlane loop)
+            const int rows =
+                __builtin_amdgcn_readfirstlane(min(max(end - tok0, 0), RPB));
             const bool ok = pid >= 0 && pid < a.num_blocks && rows > 0;
             const uint32_t nrec = ok ? (uint32_t)((rows - 1) * row_bytes + D * 2) : 0u;
             const size_t boff =
@@ -513,14 +520,22 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         const float res = tot > 0.f ? o / tot : 0.f;
         const size_t sh = (size_t)row_seq(h) * Hq + (kvh0 + hs) * G + h % G;
         const int np = PREFIX ? (ctx_len(row_seq(h)) + P - 1) / P : nparts;
-        if (np <= 1) {
-            OUT::store(a.out, sh * D + d, res);
-        } else {
+        // a workgroup that covered the whole context writes the output; on
+        // the split path every partition's workspace row is written as well
+        // (this group's state in its first partition's row, the group's
+        // other partitions marked empty), so the rows describe the whole
+        // context whoever merges them
+        if (part == 0 && np <= K) OUT::store(a.out, sh * D + d, res);
+        if (a.part_out) {
             const size_t pidx = sh * a.max_partitions + part;
             a.part_out[pidx * D + d] = res;
             if (d == 0) {
                 a.part_max[pidx] = M * kLn2;
                 a.part_sum[pidx] = tot;
+                for (int q = 1; q < K && part + q < np; ++q) {
+                    a.part_max[pidx + q] = -INFINITY;
+                    a.part_sum[pidx + q] = 0.f;
+                }
             }
         }
     }

@@ -380,13 +380,13 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
         for (int w = 0; w < NW; ++w)
             if (w < nwh) t += wt[w] * sm_acc[w0 + w][d];
         const float o = tot > 0.f ? t / tot : 0.f;
-        if (nparts <= 1) {
-            OUT::store(a.out, sh * D + d, o);
-        } else {
-            a.part_out[pidx * D + d] = o;
-        }
+        // a single partition is the whole context: the output itself; on
+        // the split path the partition's workspace row is written as well,
+        // so the rows describe every context whoever merges them
+        if (nparts <= 1) OUT::store(a.out, sh * D + d, o);
+        if (a.part_out) a.part_out[pidx * D + d] = o;
     }
-    if (nparts > 1 && sub == 0 && lane == 0) {
+    if (a.part_out && sub == 0 && lane == 0) {
         a.part_max[pidx] = M * kLn2;  // natural-log units
         a.part_sum[pidx] = tot;
     }

@@ -627,9 +627,12 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         }
     }
 
-    // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ; in decode
-    // mode with several partitions, the partition's row of the workspace --
-    const bool partial = dec && nparts > 1;
+    // ---- row n's output: O[n][16t + 4g + k] = oacc[t][k] / Σ. In decode
+    // mode on the split path (a workspace is given) the partition's row of
+    // the workspace is written too, and a single partition, which is the
+    // whole context, also gives the output itself --------------------------
+    const bool partial = dec && a.part_out != nullptr;
+    const bool whole = !dec || nparts <= 1;
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
         const float tot = sum_over_groups(lsum[u]);
@@ -643,7 +646,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                     float* po = a.part_out + pidx * D + 16 * t + 4 * g;
                     *(f32x4*)po = f32x4{oacc[u][t][0] * inv, oacc[u][t][1] * inv,
                                         oacc[u][t][2] * inv, oacc[u][t][3] * inv};
-                } else {
+                }
+                if (whole) {
                     const size_t o = orow[u] + 16 * t + 4 * g;
                     OUT::store2(a.out, o, oacc[u][t][0] * inv, oacc[u][t][1] * inv);
                     OUT::store2(a.out, o + 2, oacc[u][t][2] * inv, oacc[u][t][3] * inv);

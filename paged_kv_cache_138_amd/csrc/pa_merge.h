@@ -16,7 +16,8 @@ namespace pa {
 // Merge element d of one workspace row (one query head of one sequence)
 // over its np partitions: first the largest m_p, then the weighted sums.
 // Both loops are free of data-dependent branches, so the loads of successive
-// partitions can be in flight together.
+// partitions can be in flight together. A partition whose m_p is -inf holds
+// no token (its l_p is 0) and its o_p is never used: it may be unwritten.
 __device__ __forceinline__ float merge_row_element(const float* pm, const float* ps,
                                                   const float* po, int np, int D) {
     constexpr int kFew = 16;
@@ -37,9 +38,10 @@ __device__ __forceinline__ float merge_row_element(const float* pm, const float*
         float tot = 0.f, acc = 0.f;
 #pragma unroll
         for (int p = 0; p < kFew; ++p) {
-            const float w = m[p] == -INFINITY ? 0.f : l[p] * fast_exp2((m[p] - M) * kLog2e);
+            const bool live = m[p] != -INFINITY;
+            const float w = live ? l[p] * fast_exp2((m[p] - M) * kLog2e) : 0.f;
             tot += w;
-            acc += w * o[p];
+            acc = live ? fmaf(w, o[p], acc) : acc;
         }
         return tot > 0.f ? acc / tot : 0.f;
     }
@@ -51,9 +53,10 @@ __device__ __forceinline__ float merge_row_element(const float* pm, const float*
 #pragma unroll 8
     for (int p = 0; p < np; ++p) {
         const float mp = pm[p];
-        const float w = mp == -INFINITY ? 0.f : ps[p] * fast_exp2((mp - M) * kLog2e);
+        const bool live = mp != -INFINITY;
+        const float w = live ? ps[p] * fast_exp2((mp - M) * kLog2e) : 0.f;
         tot += w;
-        acc += w * po[(size_t)p * D];
+        acc = live ? fmaf(w, po[(size_t)p * D], acc) : acc;
     }
     return tot > 0.f ? acc / tot : 0.f;
 }

@@ -310,6 +310,58 @@ def test_exported_lse_merge_matches_oracle_merge(D):
     _assert_close(to_host_f64(out16), ref, "f16", "exported merge, fp16 output")
 
 
+PAIR_CASES = [
+    # MHA, partitions of 64: sequences of one partition and of several
+    (dict(num_seqs=6, num_heads=4, num_kv_heads=4, head_dim=128, dtype="f16", block_size=16,
+          num_blocks=200, max_blocks_per_seq=24, lens="uniform:1:380"), 64, False),
+    # grouped queries with a table 16 partitions wide and 128 x 4 workgroups
+    # per partition: workgroups walk partitions in groups
+    (dict(num_seqs=128, num_heads=16, num_kv_heads=8, head_dim=64, dtype="bf16", block_size=16,
+          num_blocks=6144, max_blocks_per_seq=64, lens="uniform:1:1024"), 64, True),
+    (dict(num_seqs=128, num_heads=16, num_kv_heads=8, head_dim=64, dtype="f16", block_size=16,
+          num_blocks=6144, max_blocks_per_seq=64, lens="uniform:1:1024"), 64, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PAIR_CASES)))
+@pytest.mark.parametrize("fused", [False, True])
+def test_partitions_then_exported_merge_give_the_output(case, fused):
+    # pa_decode_partitions (or its fused-append form) then pa_lse_merge over
+    # the same workspace give every row's output, whatever the workspace held
+    # before: every partition row is written (empty ones marked), including
+    # those of sequences one workgroup covered whole
+    kw, P, grouped = PAIR_CASES[case]
+    w = _small("pair%d" % case, **kw)
+    b = W.make_batch(w, seed=400 + case, unallocated="nan")
+    kc, vc, ref = _oracle_step(b)
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=P, fused=fused)
+    if not fused:
+        db.write_cache()
+    db.workspace.fill_(255)  # NaN in every float of the workspace
+    db.out.fill_(float("nan"))
+    db.partitions()
+    out = db.out.clone()
+    db.merge()
+    torch.cuda.synchronize()
+    _assert_close(to_host_f64(db.out), ref, "f32", "partitions + pa_lse_merge")
+    # rows the partition launch finished are the same after the merge
+    B, Hq, D = db.query.shape
+    pm, ps, po = palib.workspace_views(db.workspace, B, Hq, D, db.block_tables.shape[1],
+                                       w.block_size, P)
+    pm = pm.cpu().numpy()
+    L = b.context_lens
+    done = np.isfinite(out.cpu().numpy()).all(axis=(1, 2))
+    assert done[L <= P].all()
+    np.testing.assert_allclose(to_host_f64(db.out)[done], to_host_f64(out)[done], rtol=0,
+                               atol=1e-6)
+    # empty rows mark partitions folded into their group's first row
+    nparts = -(-L.astype(np.int64) // P)
+    live = [(i, p) for i in range(B) for p in range(int(nparts[i]))]
+    empty = sum(1 for i, p in live if np.isneginf(pm[i, :, p]).all())
+    assert (empty > 0) == grouped
+    assert all(not np.isnan(pm[i, :, p]).any() for i, p in live)
+
+
 def test_fused_qkv_strided_cache_write():
     """K/V read straight out of a fused [T, 3, H, D] projection buffer."""
     T, H, D, NB, BS = 9, 4, 64, 8, 16
