@@ -24,8 +24,10 @@
 // kernel: Sᵀ[16 tokens x 16 rows] = K · Qᵀ on v_mfma_f32_16x16x32, the
 // online softmax lane-local per row (lane (g, n) holds row n; the max and
 // sum over a row's four lanes use the gfx950 lane swaps), and
-// Oᵀ[16 d x 16 rows] += Vᵀ · Pᵀ with Vᵀ read by ds_read_b64_tr_b16 and P
-// split into hi + lo 16-bit halves. Each row is masked to positions up to
+// Oᵀ[16 d x 16 rows] += Vᵀ · Pᵀ with Vᵀ read by ds_read_b64_tr_b16; P is
+// one rounded fp16 value per weight for fp16 caches (the softmax
+// denominator sums the rounded weights) and hi + lo halves for bf16 caches,
+// whose 8-bit significand is too coarse alone. Each row is masked to positions up to
 // its own; a wave whose rows all sit before a chunk, or that has no rows,
 // skips its products (it still loads and waits at the barrier).
 //
@@ -90,6 +92,11 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #define PA_PREFILL_MAX_DEPTH 2
 #endif
 
+// fp16 caches: weights as one rounded fp16 value (1) or hi + lo halves (0)
+#ifndef PA_PREFILL_F16_SINGLE_P
+#define PA_PREFILL_F16_SINGLE_P 1
+#endif
+
 // Finds the request of flattened new token tok among requests lo .. hi:
 // the last r in that range with query_start[r] <= tok (requests without
 // new tokens are passed over).
@@ -129,6 +136,12 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     static_assert(BS % RPW == 0, "the rows of one wave's load share a block");
     static_assert(NS == 2, "one p·v contraction (32 tokens) per chunk");
     constexpr int DEPTH = LPC <= 2 ? PA_PREFILL_MAX_DEPTH : 1;
+    // fp16 caches: the weights enter the p·v product as one fp16 value each
+    // (11 significant bits), and the softmax denominator sums those same
+    // rounded weights, so the output is an exact weighted average of the V
+    // rows whose weights differ from the true ones by at most 2^-10
+    // relative; bf16 caches keep hi + lo halves (8 bits would not do)
+    constexpr bool ONE_P = std::is_same<KV, KvF16>::value && PA_PREFILL_F16_SINGLE_P;
 
     __shared__ __attribute__((aligned(16))) char sm_k[2][TILE];
     __shared__ __attribute__((aligned(16))) char sm_v[2][TILE];
@@ -459,14 +472,34 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             float pr[4 * NS];
 #pragma unroll
             for (int e = 0; e < 4 * NS; ++e) pr[e] = fast_exp2(fmaf(sv[e], sl, nm));
-            static_assert(4 * NS == 8, "the sum below adds eight weights");
-            lsum[u] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-            // Pᵀ operand in hi + lo halves
-            uint32_t hw[4], lw[4];
+            static_assert(4 * NS == 8, "the sums below add eight weights");
+            if constexpr (ONE_P) {
+                // Pᵀ operand: the weights rounded to fp16, and the row's sum
+                // of exactly those values (dot2 with (1, 1): each pair
+                // exactly, accumulated in fp32)
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                typedef float f2 __attribute__((ext_vector_type(2)));
+                uint32_t hw[4];
+                float ps = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Mma<KV>::split2(pr[2 * e], pr[2 * e + 1], &hw[e], &lw[e]);
-            phi[u] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-            plo[u] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+                for (int e = 0; e < 4; ++e) {
+                    const h2 h = __builtin_convertvector(f2{pr[2 * e], pr[2 * e + 1]}, h2);
+                    ps = __builtin_amdgcn_fdot2(h, h2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
+                    hw[e] = __builtin_bit_cast(uint32_t, h);
+                }
+                lsum[u] += ps;
+                phi[u] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            } else {
+                lsum[u] +=
+                    ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                // Pᵀ operand in hi + lo halves
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Mma<KV>::split2(pr[2 * e], pr[2 * e + 1], &hw[e], &lw[e]);
+                phi[u] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                plo[u] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            }
         }
         // ---- Oᵀ += Vᵀ · Pᵀ: tokens 4g + e (e < 4) and 16 + 4g + e - 4; each
         // Vᵀ operand serves every tile ------------------------------------
@@ -481,7 +514,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
 #pragma unroll
             for (int u = 0; u < TR; ++u) {
                 oacc[u][t] = Mma<KV>::mma(av, phi[u], oacc[u][t]);
-                oacc[u][t] = Mma<KV>::mma(av, plo[u], oacc[u][t]);
+                if constexpr (!ONE_P) oacc[u][t] = Mma<KV>::mma(av, plo[u], oacc[u][t]);
             }
         }
     };
