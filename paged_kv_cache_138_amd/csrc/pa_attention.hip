@@ -19,6 +19,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 
@@ -111,6 +112,19 @@ bool use_gqa(int num_heads, int num_kv_heads) {
     return g >= 2 && g <= kMaxGroupMfma;
 }
 
+// Adjacent heads (log2, at most max_log2) whose row slices together are a
+// whole number of 128-byte cache lines. A head slice of 160 or 192 bytes
+// (head_dim 80, 96) shares a line with the next head's; workgroups that
+// serve single heads then fetch those lines twice (measured on MI355X:
+// 1.39x the algorithmic bytes at head_dim 80 with two heads per
+// workgroup), while 4 (head_dim 80) or 2 (head_dim 96) heads together start
+// and end on line boundaries.
+int whole_line_heads_log2(int heads, int head_dim, int max_log2) {
+    int hl = 0;
+    while (((head_dim * 2) << hl) % 128 != 0 && hl < max_log2) ++hl;
+    return ((head_dim * 2) << hl) % 128 == 0 && heads % (1 << hl) == 0 ? hl : 0;
+}
+
 // Query heads per workgroup of the MHA kernel on the split path (log2).
 // One head per workgroup gives the finest work units, which matters when
 // the grid is only a few times what the device holds at once (the last,
@@ -120,20 +134,24 @@ bool use_gqa(int num_heads, int num_kv_heads) {
 // workgroup halve the workgroups to dispatch and read each block row's
 // heads side by side. The single-pass path keeps one head per workgroup, so
 // that a sequence's context is spread over all the waves of its workgroup.
-int mha_heads_log2(int num_heads, int64_t rect_workgroups, int resident, bool split) {
+int mha_heads_log2(int num_heads, int64_t rect_workgroups, int resident, bool split,
+                   int head_dim) {
     if (!split || num_heads % 2 != 0) return 0;
-    return rect_workgroups / 2 >= (int64_t)6 * resident ? 1 : 0;
+    const int hl = rect_workgroups / 2 >= (int64_t)6 * resident ? 1 : 0;
+    return std::max(hl, whole_line_heads_log2(num_heads, head_dim, 2));
 }
 
 #ifndef PA_GQA_HEADS
 #define PA_GQA_HEADS 2
 #endif
 // kv heads per workgroup of the grouped-query kernel on the split path (log2)
-int gqa_heads_log2(int num_kv_heads) {
+int gqa_heads_log2(int num_kv_heads, int head_dim) {
     int hl = 0;
     while ((2 << hl) <= PA_GQA_HEADS && (2 << hl) <= kGqaWaves && num_kv_heads % (2 << hl) == 0)
         ++hl;
-    return hl;
+    int max_log2 = 0;
+    while ((2 << max_log2) <= kGqaWaves) ++max_log2;
+    return std::max(hl, whole_line_heads_log2(num_kv_heads, head_dim, max_log2));
 }
 
 // Consecutive partitions one grouped-query workgroup walks (1, 2 or 4).
@@ -434,10 +452,10 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     if (fn && !use_gqa(s.num_heads, s.num_kv_heads)) {
         const int64_t rect = (int64_t)s.num_seqs * s.num_heads * (lay.np - prefix_parts);
         hl = mha_heads_log2(s.num_heads, rect, resident_workgroups((const void*)fn, threads),
-                            true);
+                            true, s.head_dim);
         per_seq = s.num_heads >> hl;
     } else if (fn) {
-        hl = gqa_heads_log2(s.num_kv_heads);
+        hl = gqa_heads_log2(s.num_kv_heads, s.head_dim);
         per_seq = s.num_kv_heads >> hl;
         group = gqa_group(lay.np - prefix_parts, (int64_t)s.num_seqs * per_seq,
                           resident_workgroups((const void*)fn, threads));

@@ -44,7 +44,6 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <class KV>
 struct Mma;
@@ -320,13 +319,16 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // a block longer than a chunk holds a whole number of chunks). Load i of
     // a chunk brings rows vr + RPI*i (the RPI rows of one load share a block).
     const uint32_t voff = vcv ? (uint32_t)(vc * 16) : kNoSlice;
+    // cache policy as in the one-head kernel: head slices that end inside a
+    // cache line keep it in L2 for the neighbouring head's wave
+    constexpr int AUX = (D * 2) % 128 == 0 ? PA_LOAD_AUX : PA_LOAD_AUX_SHARED_LINES;
     auto issue_rows = [&](const __amdgpu_buffer_rsrc_t (&rs)[BPC], u32x4 (&buf)[VL]) {
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
             const int t = vr + RPI * i;
             const int b = (RPI * i) / RPB;
             const int row = t - b * RPB;
-            buf[i] = buffer_load16(rs[b], (uint32_t)(row * row_bytes) + voff);
+            buf[i] = buffer_load16<AUX>(rs[b], (uint32_t)(row * row_bytes) + voff);
         }
     };
     auto issue_k = [&](const ChunkIds& ci, u32x4 (&kb)[VL]) { issue_rows(ci.k, kb); };

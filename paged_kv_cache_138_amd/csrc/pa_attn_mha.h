@@ -194,6 +194,10 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
             }
         }
     };
+    // cache policy: non-temporal for rows of whole lines; a head slice that
+    // ends inside a line (head_dim 80, 96) shares it with the next head,
+    // whose wave reads it soon after from L2 if the line is kept there
+    constexpr int AUX = (D * 2) % 128 == 0 ? PA_LOAD_AUX : PA_LOAD_AUX_SHARED_LINES;
     auto issue = [&](const ChunkIds& ci, auto is_v, u32x4 (&buf)[NI]) {
         // recomputing the IPB offsets here (one add each) keeps them out of
         // the registers that live across the chunk loop
@@ -210,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
                 rs = is_v ? ci.v[b] : ci.k[b];
 #pragma unroll
             for (int j = 0; j < IPB; ++j)
-                buf[b * IPB + j] = buffer_load16(rs, o + (uint32_t)(j * RPI * row_bytes));
+                buf[b * IPB + j] = buffer_load16<AUX>(rs, o + (uint32_t)(j * RPI * row_bytes));
         }
     };
     constexpr std::false_type kK{};

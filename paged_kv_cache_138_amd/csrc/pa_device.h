@@ -10,6 +10,7 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
@@ -180,6 +181,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 // 16-byte streaming read from about 6.2 to about 7.0 TB/s.
 #ifndef PA_LOAD_AUX
 #define PA_LOAD_AUX 2
+#endif
+// the policy for rows whose head slices share cache lines (see the kernels)
+#ifndef PA_LOAD_AUX_SHARED_LINES
+#define PA_LOAD_AUX_SHARED_LINES 0
 #endif
 
 // Added to the in-block offset of a lane whose 16-byte slice of the row
