@@ -39,7 +39,9 @@ struct MergeArgs {
     int partition_size;
     // rows of sequences with at most this many partitions are left alone:
     // the split paths' partition launch wrote their output (one workgroup
-    // covered the whole context); 0 writes every row (pa_lse_merge)
+    // covered the whole context); 0 writes every row (pa_lse_merge). Above
+    // 1, partitions were walked in groups of this size from partition 0,
+    // and only the groups' first rows are read.
     int skip_parts;
 };
 
@@ -71,7 +73,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     const size_t r = (size_t)row * a.max_partitions;
     float o;
     if (!merge_trivial_row(a, np, r, D, d, &o))
-        o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D);
+        o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D,
+                                  a.skip_parts > 1 ? a.skip_parts : 1);
     OUT::store(a.out, (size_t)row * D + d, o);
 }
 
@@ -94,7 +97,8 @@ __global__ __launch_bounds__(256) void lse_merge_wave_kernel(MergeArgs a) {
     for (int d = lane; d < D; d += 64) {
         float o;
         if (!merge_trivial_row(a, np, r, D, d, &o))
-            o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D);
+            o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D,
+                                  a.skip_parts > 1 ? a.skip_parts : 1);
         OUT::store(a.out, (size_t)row * D + d, o);
     }
 }
@@ -457,8 +461,11 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     } else if (fn) {
         hl = gqa_heads_log2(s.num_kv_heads, s.head_dim);
         per_seq = s.num_kv_heads >> hl;
-        group = gqa_group(lay.np - prefix_parts, (int64_t)s.num_seqs * per_seq,
-                          resident_workgroups((const void*)fn, threads));
+        // (not after a shared prefix, whose partitions stay single: the
+        // merge then reads every row)
+        if (prefix_parts == 0)
+            group = gqa_group(lay.np, (int64_t)s.num_seqs * per_seq,
+                              resident_workgroups((const void*)fn, threads));
     }
     attn_fn pfn = prefix_tokens > 0 ? pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim,
                                                          s.block_size)

@@ -150,7 +150,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // LDS bytes per K or V row: a 32-byte pad keeps the 16-byte K reads and
     // the transposed V reads free of bank conflicts (a 16-byte pad left both
     // 2-way on MI355X)
-    constexpr int ROWB = DP * 2 + 32;
+    constexpr int ROWB = DP * 2 + PA_LDS_ROW_PAD;
     constexpr int TILE = CH * ROWB;     // LDS bytes of one chunk's K (then V) rows
     constexpr int OROW = DP + 4;        // floats per row of the wave's partial output
     static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");

@@ -128,7 +128,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // the transposed V reads free of bank conflicts (measured on MI355X,
     // 16 waves on a CU: 4.4 and 2.6 cycles per instruction; a 16-byte pad
     // left both 2-way, 8.1 and 4.1)
-    constexpr int ROWB = DP * 2 + 32;
+    constexpr int ROWB = DP * 2 + PA_LDS_ROW_PAD;
     constexpr int TILE = CH * ROWB;
     constexpr int BSC = BS < CH ? BS : CH;  // tokens of a chunk in one block
     constexpr uint32_t kBlockBits = BSC == 32 ? 0xffffffffu : (1u << BSC) - 1u;

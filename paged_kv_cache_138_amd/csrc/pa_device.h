@@ -182,6 +182,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 #ifndef PA_LOAD_AUX
 #define PA_LOAD_AUX 2
 #endif
+// Bytes of padding after each K/V row in the LDS tiles of the matrix-core
+// kernels. 32 spreads their 16-byte K reads and transposed V reads over the
+// banks; other values build variants for comparison (the rocprofv3
+// SQ_LDS_BANK_CONFLICT counts of both are kept with the profiles).
+#ifndef PA_LDS_ROW_PAD
+#define PA_LDS_ROW_PAD 32
+#endif
+
 // the policy for rows whose head slices share cache lines (see the kernels)
 #ifndef PA_LOAD_AUX_SHARED_LINES
 #define PA_LOAD_AUX_SHARED_LINES 0

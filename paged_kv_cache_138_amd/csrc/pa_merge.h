@@ -14,51 +14,55 @@
 namespace pa {
 
 // Merge element d of one workspace row (one query head of one sequence)
-// over its np partitions: first the largest m_p, then the weighted sums.
-// Both loops are free of data-dependent branches, so the loads of successive
-// partitions can be in flight together. A partition whose m_p is -inf holds
-// no token (its l_p is 0) and its o_p is never used: it may be unwritten.
-__device__ __forceinline__ float merge_row_element(const float* pm, const float* ps,
-                                                  const float* po, int np, int D) {
-    constexpr int kFew = 16;
-    if (np <= kFew) {
-        // up to 16 partitions: every load is issued before any arithmetic
-        float m[kFew], l[kFew], o[kFew];
+// over the partitions p = 0, step, 2*step, ... below np: the largest m_p,
+// then the weighted sums. Partitions walked in groups of `step` keep their
+// state in the group's first row, so the other rows are not read. A
+// partition whose m_p is -inf holds no token (its l_p is 0) and its o_p is
+// never used: it may be unwritten.
+// KB partitions at a time: their loads are free of data-dependent branches
+// and all in flight together; a row of more partitions takes them in blocks
+// of KB, rescaling its running sums to each block's maximum.
+template <int KB>
+__device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, const float* po,
+                                             int np, int D, int step) {
+    float M = -INFINITY, tot = 0.f, acc = 0.f;
+    for (int p0 = 0; p0 < np; p0 += KB * step) {
+        float m[KB], l[KB], o[KB];
 #pragma unroll
-        for (int p = 0; p < kFew; ++p) {
+        for (int q = 0; q < KB; ++q) {
+            const int p = p0 + q * step;
             const bool in = p < np;
-            m[p] = in ? pm[p] : -INFINITY;
-            l[p] = in ? ps[p] : 0.f;
-            o[p] = in ? po[(size_t)p * D] : 0.f;
+            m[q] = in ? pm[p] : -INFINITY;
+            l[q] = in ? ps[p] : 0.f;
+            o[q] = in ? po[(size_t)p * D] : 0.f;
         }
-        float M = -INFINITY;
+        float Mb = M;
 #pragma unroll
-        for (int p = 0; p < kFew; ++p) M = fmaxf(M, m[p]);
-        if (M == -INFINITY) return 0.f;
-        float tot = 0.f, acc = 0.f;
+        for (int q = 0; q < KB; ++q) Mb = fmaxf(Mb, m[q]);
+        if (Mb == -INFINITY) continue;  // nothing yet (uniform over the row)
+        const float r = M == -INFINITY ? 0.f : fast_exp2((M - Mb) * kLog2e);
+        tot *= r;
+        acc *= r;
+        M = Mb;
 #pragma unroll
-        for (int p = 0; p < kFew; ++p) {
-            const bool live = m[p] != -INFINITY;
-            const float w = live ? l[p] * fast_exp2((m[p] - M) * kLog2e) : 0.f;
+        for (int q = 0; q < KB; ++q) {
+            const bool live = m[q] != -INFINITY;
+            const float w = live ? l[q] * fast_exp2((m[q] - M) * kLog2e) : 0.f;
             tot += w;
-            acc = live ? fmaf(w, o[p], acc) : acc;
+            acc = live ? fmaf(w, o[q], acc) : acc;
         }
-        return tot > 0.f ? acc / tot : 0.f;
-    }
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int p = 0; p < np; ++p) M = fmaxf(M, pm[p]);
-    if (M == -INFINITY) return 0.f;
-    float tot = 0.f, acc = 0.f;
-#pragma unroll 8
-    for (int p = 0; p < np; ++p) {
-        const float mp = pm[p];
-        const bool live = mp != -INFINITY;
-        const float w = live ? ps[p] * fast_exp2((mp - M) * kLog2e) : 0.f;
-        tot += w;
-        acc = live ? fmaf(w, po[(size_t)p * D], acc) : acc;
     }
     return tot > 0.f ? acc / tot : 0.f;
+}
+
+// The block width follows the row's partition count (uniform over a wave,
+// which covers part of one row).
+__device__ __forceinline__ float merge_row_element(const float* pm, const float* ps,
+                                                  const float* po, int np, int D, int step) {
+    const int nq = (np + step - 1) / step;
+    if (nq <= 4) return merge_blocks<4>(pm, ps, po, np, D, step);
+    if (nq <= 8) return merge_blocks<8>(pm, ps, po, np, D, step);
+    return merge_blocks<16>(pm, ps, po, np, D, step);
 }
 
 }  // namespace pa
