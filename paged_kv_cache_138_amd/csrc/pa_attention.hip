@@ -55,14 +55,15 @@ __device__ __forceinline__ bool merge_trivial_row(const MergeArgs& a, int np, si
     return true;
 }
 
-// 256 threads merge 256 / head_dim workspace rows (row = one query head of
-// one sequence), one output element per thread.
+// 256 threads merge 1024 / head_dim workspace rows (row = one query head of
+// one sequence), four consecutive output elements per thread, each
+// partition's four read by one 16-byte load.
 template <class OUT, int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-    constexpr int RPW = 256 / D;
-    // a wavefront covers 64 consecutive elements of one row (D >= 64)
-    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * RPW + threadIdx.x / D);
-    const int d = threadIdx.x % D;
+    constexpr int TPR = D / 4;      // threads per row
+    constexpr int RPW = 256 / TPR;  // rows per workgroup
+    const int row = blockIdx.x * RPW + threadIdx.x / TPR;
+    const int d = (threadIdx.x % TPR) * 4;
     if (row >= a.num_seqs * a.num_heads) return;
     const int seq = row / a.num_heads;
     int L = a.context_lens[seq];
@@ -71,11 +72,16 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     if (np > a.max_partitions) np = a.max_partitions;
     if (a.skip_parts > 0 && np <= a.skip_parts) return;
     const size_t r = (size_t)row * a.max_partitions;
-    float o;
-    if (!merge_trivial_row(a, np, r, D, d, &o))
-        o = merge_row_element(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D,
-                                  a.skip_parts > 1 ? a.skip_parts : 1);
-    OUT::store(a.out, (size_t)row * D + d, o);
+    f32x4 o;
+    if (np <= 1) {  // the merge of one partition is its output; of none, zeros
+        o = np == 1 ? *(const f32x4*)(a.part_out + r * D + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        o = merge_row_element4(a.part_max + r, a.part_sum + r, a.part_out + r * D + d, np, D,
+                               a.skip_parts > 1 ? a.skip_parts : 1);
+    }
+    const size_t e = (size_t)row * D + d;
+    OUT::store2(a.out, e, o[0], o[1]);
+    OUT::store2(a.out, e + 2, o[2], o[3]);
 }
 
 // head_dim 80 and 96: one row per wavefront, each lane merging the
@@ -521,7 +527,7 @@ pa_status launch_merge(void* out, pa_dtype out_dtype, const float* part_out,
     MergeArgs m{out,      part_out,      part_max, part_sum, context_lens, num_seqs,
                 num_heads, max_partitions, partition_size, skip_parts};
     const int64_t rows = (int64_t)num_seqs * num_heads;
-    const int64_t rpw = head_dim % 64 == 0 ? 256 / head_dim : 4;  // rows per workgroup
+    const int64_t rpw = head_dim % 64 == 0 ? 1024 / head_dim : 4;  // rows per workgroup
     const int64_t grid = (rows + rpw - 1) / rpw;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     hipLaunchKernelGGL(mfn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, m);

@@ -55,6 +55,51 @@ __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, 
     return tot > 0.f ? acc / tot : 0.f;
 }
 
+// merge_blocks for four consecutive elements of the row at once: one
+// 16-byte load of each partition's output.
+template <int KB>
+__device__ __forceinline__ f32x4 merge_blocks4(const float* pm, const float* ps, const float* po,
+                                              int np, int D, int step) {
+    float M = -INFINITY, tot = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < np; p0 += KB * step) {
+        float m[KB], l[KB];
+        f32x4 o[KB];
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+            const int p = p0 + q * step;
+            const bool in = p < np;
+            m[q] = in ? pm[p] : -INFINITY;
+            l[q] = in ? ps[p] : 0.f;
+            o[q] = in ? *(const f32x4*)(po + (size_t)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        float Mb = M;
+#pragma unroll
+        for (int q = 0; q < KB; ++q) Mb = fmaxf(Mb, m[q]);
+        if (Mb == -INFINITY) continue;
+        const float r = M == -INFINITY ? 0.f : fast_exp2((M - Mb) * kLog2e);
+        tot *= r;
+        acc *= r;
+        M = Mb;
+#pragma unroll
+        for (int q = 0; q < KB; ++q) {
+            const bool live = m[q] != -INFINITY;
+            const float w = live ? l[q] * fast_exp2((m[q] - M) * kLog2e) : 0.f;
+            tot += w;
+            if (live) acc += w * o[q];
+        }
+    }
+    return tot > 0.f ? acc / tot : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ f32x4 merge_row_element4(const float* pm, const float* ps,
+                                                   const float* po, int np, int D, int step) {
+    const int nq = (np + step - 1) / step;
+    if (nq <= 4) return merge_blocks4<4>(pm, ps, po, np, D, step);
+    if (nq <= 8) return merge_blocks4<8>(pm, ps, po, np, D, step);
+    return merge_blocks4<16>(pm, ps, po, np, D, step);
+}
+
 // The block width follows the row's partition count (uniform over a wave,
 // which covers part of one row).
 __device__ __forceinline__ float merge_row_element(const float* pm, const float* ps,
