@@ -273,10 +273,13 @@ def main():
         del base
         torch.cuda.synchronize()
 
-        for k in range(args.warmup):
-            copies[k % R].step()
-        torch.cuda.synchronize()
+        # the streaming-read ceiling is measured first: its saturating reads
+        # (about 8 ms) bring the device out of its idle state, and the
+        # warm-up steps that follow find the batch copies' translations again
+        ceiling = stream_ceiling(args.ceiling_gib) if args.ceiling_gib > 0 else None
         # all copies must agree bit for bit (same logical data, different placement)
+        copies[0].step()
+        torch.cuda.synchronize()
         ref = copies[0].out.clone()
         for c in copies[1:]:
             c.step()
@@ -285,11 +288,10 @@ def main():
             assert torch.equal(c.out.view(torch.int16) if c.out.dtype != torch.float32 else c.out,
                                ref.view(torch.int16) if ref.dtype != torch.float32 else ref), \
                 "rotated copies disagree"
-
-        # the streaming-read ceiling runs here, between the warm-up and the
-        # timed loops: its saturating reads (about 8 ms) also bring the
-        # device out of its idle state before timing starts
-        ceiling = stream_ceiling(args.ceiling_gib) if args.ceiling_gib > 0 else None
+        # the warm-up steps, right before the timed loops
+        for k in range(args.warmup):
+            copies[k % R].step()
+        torch.cuda.synchronize()
         K = args.steps
         split = path.startswith("split")
         loop_ms = []
