@@ -173,8 +173,11 @@ int gqa_heads_log2(int num_kv_heads, int head_dim) {
 // partition as the unit of the workspace and the merge; it is used while the
 // grid of groups (for the longest table) still holds at least two rounds of
 // the workgroups the device runs at once.
+#ifndef PA_GQA_MAX_GROUP
+#define PA_GQA_MAX_GROUP 4
+#endif
 int gqa_group(int parts, int64_t units, int resident) {
-    for (int k = 4; k > 1; k /= 2)
+    for (int k = PA_GQA_MAX_GROUP; k > 1; k /= 2)
         if (parts >= 2 * k && units * ceil_div(parts, k) >= (int64_t)2 * resident) return k;
     return 1;
 }
@@ -886,7 +889,7 @@ extern "C" pa_status pa_prefill_shared_prefix(
                            scale);
     a.query_start = query_start;
     a.prefix_tokens = shared_prefix_tokens;
-    const int rows = waves * (16 / G);  // new tokens per workgroup
+    const int rows = waves * PA_PREFILL_SHARED_TR * (16 / G);  // new tokens per workgroup
     const int64_t grid = (int64_t)ceil_div(num_tokens, rows) * num_kv_heads;
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(waves * 64), 0, (hipStream_t)stream, a);

@@ -7,8 +7,8 @@ namespace pa {
 namespace {
 template <int NW>
 attn_fn pick_cfg(pa_dtype kv, pa_dtype out, int d, int bs) {
-    if (kv == PA_F16) return pick_prefill_out<KvF16, NW, 1, true>(out, kv, d, bs);
-    if (kv == PA_BF16) return pick_prefill_out<KvBF16, NW, 1, true>(out, kv, d, bs);
+    if (kv == PA_F16) return pick_prefill_out<KvF16, NW, PA_PREFILL_SHARED_TR, true>(out, kv, d, bs);
+    if (kv == PA_BF16) return pick_prefill_out<KvBF16, NW, PA_PREFILL_SHARED_TR, true>(out, kv, d, bs);
     return nullptr;
 }
 }  // namespace

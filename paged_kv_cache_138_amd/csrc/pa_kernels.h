@@ -14,6 +14,11 @@
 #define PA_GQA_WAVES 4
 #endif
 
+// 16-row tiles per wave of the prefill kernel in shared-prefix mode
+#ifndef PA_PREFILL_SHARED_TR
+#define PA_PREFILL_SHARED_TR 1
+#endif
+
 namespace pa {
 
 constexpr int kWaves = PA_WAVES;         // wavefronts per workgroup, one-head kernel
