@@ -44,7 +44,13 @@
  *     (PA_F16 or PA_BF16). Outputs may be that type (rounded to nearest
  *     even from fp32) or PA_F32. All accumulation is fp32
  *     (lqnn.cn/news/170268 §6: half-precision accumulation of the scores
- *     degrades long sequences).
+ *     degrades long sequences). The softmax weights enter the p·v
+ *     products on the matrix cores as 16-bit values: for fp16 caches in
+ *     the prefill kernel (pa_prefill, pa_prefill_shared_prefix, and decode
+ *     at head_dim 256) one rounded fp16 value per weight, whose sum is the
+ *     softmax denominator (an exact average of the V rows with weights
+ *     within 2^-10 relative of the true ones); otherwise hi + lo halves,
+ *     about 16 bits of each weight.
  *   - Supported shapes: head_dim in {64, 80, 96, 128, 256}; block_size in
  *     {8, 16, 32, 64}; num_heads a multiple of num_kv_heads (query head h
  *     reads kv head h / (num_heads / num_kv_heads)), at most 16 query heads
