@@ -142,12 +142,22 @@ int whole_line_heads_log2(int heads, int head_dim, int max_log2) {
 // times larger - many sequences or long maximum contexts, where most of the
 // (sequence, partition) rectangle may be empty - two adjacent heads per
 // workgroup halve the workgroups to dispatch and read each block row's
-// heads side by side. The single-pass path keeps one head per workgroup, so
-// that a sequence's context is spread over all the waves of its workgroup.
+// heads side by side. More heads are served when a partition holds fewer
+// chunks than a head would get waves, so that no wave idles. The
+// single-pass path keeps one head per workgroup, so that a sequence's
+// context is spread over all the waves of its workgroup.
+#ifndef PA_MHA_MIN_HEADS_LOG2
+#define PA_MHA_MIN_HEADS_LOG2 0
+#endif
 int mha_heads_log2(int num_heads, int64_t rect_workgroups, int resident, bool split,
-                   int head_dim) {
+                   int head_dim, int block_size, int partition_size) {
     if (!split || num_heads % 2 != 0) return 0;
-    const int hl = rect_workgroups / 2 >= (int64_t)6 * resident ? 1 : 0;
+    int hl = rect_workgroups / 2 >= (int64_t)6 * resident ? 1 : 0;
+    while (hl < PA_MHA_MIN_HEADS_LOG2 && (1 << hl) < kWaves && num_heads % (2 << hl) == 0) ++hl;
+    const int chunk = mha_chunk_tokens(head_dim, block_size);
+    while ((1 << hl) < kWaves && (kWaves >> hl) * chunk > partition_size &&
+           num_heads % (2 << hl) == 0)
+        ++hl;
     return std::max(hl, whole_line_heads_log2(num_heads, head_dim, 2));
 }
 
@@ -465,7 +475,7 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
     if (fn && !use_gqa(s.num_heads, s.num_kv_heads)) {
         const int64_t rect = (int64_t)s.num_seqs * s.num_heads * (lay.np - prefix_parts);
         hl = mha_heads_log2(s.num_heads, rect, resident_workgroups((const void*)fn, threads),
-                            true, s.head_dim);
+                            true, s.head_dim, s.block_size, partition_size);
         per_seq = s.num_heads >> hl;
     } else if (fn) {
         hl = gqa_heads_log2(s.num_kv_heads, s.head_dim);

@@ -5,6 +5,19 @@
 
 namespace pa {
 
+// Tokens per chunk of the one-head decode kernel, from the host's view as
+// well (it sizes the heads per workgroup so that every wave gets a chunk).
+// A lane keeps 16 loads of 16 bytes of K (and as many of V) in flight: 64
+// tokens of 128-element rows (head_dim 80 and 96 are laid out as 128), and
+// 128 tokens of 64-element rows, where each lane then holds two scores. At
+// block size 8 such a chunk would span 16 blocks, whose ids and ranges no
+// longer fit the scalar registers: there it stays at 64 tokens.
+#ifndef PA_MHA_CHUNK_64
+#define PA_MHA_CHUNK_64 128
+#endif
+constexpr int mha_chunk_tokens(int head_dim, int block_size) {
+    return head_dim <= 64 && block_size >= 16 ? PA_MHA_CHUNK_64 : 64;
+}
 
 struct AttnArgs {
     void* out;

@@ -2,16 +2,19 @@
 // grouped-query shapes the matrix-core kernel does not take).
 //
 // Work decomposition (MI355X, 64-lane wavefronts):
-//   * one workgroup = one (sequence, group of 1 or 2 adjacent query heads,
-//     context partition) with NW wavefronts; each head's waves take 64-token
-//     chunks of the partition in turn and their softmax states are merged in
-//     LDS at the end. The single-pass pa_decode is the same kernel with one
-//     head per workgroup and one partition covering the context.
+//   * one workgroup = one (sequence, group of 1, 2 or 4 adjacent query
+//     heads, context partition) with NW wavefronts; each head's waves take
+//     chunks of the partition (64 tokens, 128 at head_dim 64) in turn and
+//     their softmax states are merged in LDS at the end. The single-pass
+//     pa_decode is the same kernel with one head per workgroup and one
+//     partition covering the context.
 //   * inside a chunk, one 16-byte load per lane brings 8 elements of a K (or
 //     V) row: head_dim/8 lanes cover a row, 64 lanes cover 64*8/head_dim
 //     rows of one physical block per load instruction, so each load is a
 //     set of dense head_dim*2-byte row segments and the block's base address
-//     is uniform across the wavefront.
+//     is uniform across the wavefront. A chunk is 16 such loads of K and 16
+//     of V, whatever the row width, so that each wave keeps as many bytes in
+//     flight at head_dim 64 as at 128.
 //   * q·k: fp32 dot2 of packed fp16/bf16 pairs, then a transpose-reduce over
 //     the lanes of a row that leaves lane c of each row group holding the
 //     full score of that group's c-th load; softmax max/sum by wavefront
@@ -25,14 +28,15 @@
 
 namespace pa {
 
-// One transpose-reduce step over groups of lanes: lanes whose index has
-// bit HALF set keep the upper half of their list, the others the lower half,
-// and each adds its partner's copy of the half it keeps.
-template <int HALF, int N>
+// One transpose-reduce step over groups of lanes, on the list pd[OFF ..
+// OFF + 2*HALF - 1]: lanes whose index has bit HALF set keep the upper half
+// of the list, the others the lower half, and each adds its partner's copy
+// of the half it keeps.
+template <int HALF, int OFF, int N>
 __device__ __forceinline__ void tr_step(float (&pd)[N], int c) {
     const bool upper = (c & HALF) != 0;
 #pragma unroll
-    for (int k = 0; k < HALF; ++k) {
+    for (int k = OFF; k < OFF + HALF; ++k) {
         const float send = upper ? pd[k] : pd[k + HALF];
         const float keep = upper ? pd[k + HALF] : pd[k];
         pd[k] = keep + tr_partner<HALF>(send);
@@ -52,8 +56,9 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     constexpr int DP = D <= 64 ? 64 : 128;
     constexpr int LPR = DP / 8;         // lanes per cache row
     constexpr int RPI = 64 / LPR;       // rows per load instruction
-    constexpr int NI = LPR;             // load instructions per chunk
-    constexpr int CHUNK = RPI * NI;     // tokens per chunk (64)
+    constexpr int CHUNK = mha_chunk_tokens(D, BS);  // tokens per chunk
+    constexpr int NI = CHUNK / RPI;     // load instructions per chunk (16)
+    constexpr int SPL = NI / LPR;       // scores per lane (1, or 2 at head_dim 64)
     constexpr int RPB = BS < 32 ? BS : 32;  // rows one load descriptor covers
     constexpr int IPB = RPB / RPI;      // load instructions per descriptor
     constexpr int BPC = CHUNK / RPB;    // descriptors per chunk
@@ -61,7 +66,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     // not fit the scalar registers: keep each block's offset and range and
     // build its descriptor when its loads are issued
     constexpr bool LAZY = BPC > 4;
-    static_assert(CHUNK == 64, "one score per lane per chunk");
+    static_assert(NI % LPR == 0 && SPL >= 1 && SPL <= 2, "whole scores per lane");
     static_assert(RPB % RPI == 0 && CHUNK % BS == 0 && BS % RPB == 0,
                   "blocks tile the chunk, descriptors the block");
     static_assert(LPR == 8 || LPR == 16, "head_dim laid out as 64 or 128");
@@ -78,7 +83,7 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
 
     // the workgroup serves 2^heads_log2 adjacent query heads of one
     // (sequence, partition); each head gets NW / 2^heads_log2 waves, which
-    // take the partition's 64-token chunks in turn. Adjacent heads' rows are
+    // take the partition's chunks in turn. Adjacent heads' rows are
     // adjacent in a cache row, so serving several heads at once reads longer
     // contiguous runs of each block at about the same time.
     constexpr int LOG_NW = NW == 4 ? 2 : (NW == 2 ? 1 : 0);
@@ -219,8 +224,9 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     };
     constexpr std::false_type kK{};
     constexpr std::true_type kV{};
-    // scores of the chunk's 64 tokens, one per lane (log2 units, -inf if absent)
-    auto scores = [&](const u32x4 (&kr)[NI], int cs, const ChunkIds& ci) -> float {
+    // scores of the chunk's tokens, SPL per lane (log2 units, -inf if
+    // absent): slot h of lane (r, c) holds the token of load h*LPR + c, row r
+    auto scores = [&](const u32x4 (&kr)[NI], int cs, const ChunkIds& ci, float (&sc)[SPL]) {
         float pd[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -229,47 +235,62 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
             t = KV::dot2(kr[i].z, q.z, t);
             pd[i] = KV::dot2(kr[i].w, q.w, t);
         }
-        // lane c of each row group ends up with the full score of load c
-        if constexpr (NI >= 16) tr_step<8>(pd, c);
-        tr_step<4>(pd, c);
-        tr_step<2>(pd, c);
-        tr_step<1>(pd, c);
-        const int myb = c / IPB;
-        const int mytok = cs + myb * RPB + (c % IPB) * RPI + r;
-        bool ok;
-        if constexpr (LAZY) {
-            ok = (__builtin_amdgcn_readfirstlane(ci.okm) >> myb) & 1u;
-        } else {
-            ok = ci.ok[0];
+        // per list of LPR loads: lane c of each row group ends up with the
+        // full score of load c of the list
+        static_for<0, SPL>([&](auto H) {
+            constexpr int o = decltype(H)::value * LPR;
+            if constexpr (LPR >= 16) tr_step<8, o>(pd, c);
+            tr_step<4, o>(pd, c);
+            tr_step<2, o>(pd, c);
+            tr_step<1, o>(pd, c);
+        });
 #pragma unroll
-            for (int b = 1; b < BPC; ++b)
-                if (myb == b) ok = ci.ok[b];
+        for (int h = 0; h < SPL; ++h) {
+            const int i = h * LPR + c;
+            const int myb = i / IPB;
+            const int mytok = cs + myb * RPB + (i % IPB) * RPI + r;
+            bool ok;
+            if constexpr (LAZY) {
+                ok = (__builtin_amdgcn_readfirstlane(ci.okm) >> myb) & 1u;
+            } else {
+                ok = ci.ok[0];
+#pragma unroll
+                for (int b = 1; b < BPC; ++b)
+                    if (myb == b) ok = ci.ok[b];
+            }
+            ok = ok && mytok < end_c;
+            sc[h] = ok ? pd[h * LPR] * a.scale_log2 : -INFINITY;
         }
-        ok = ok && mytok < end_c;
-        return ok ? pd[0] * a.scale_log2 : -INFINITY;
     };
-    // online softmax update; returns this lane's weight exp2(s - m)
-    auto update = [&](float s) -> float {
-        const float mn = fmaxf(m, wave_max(s));
-        float alpha, pr;
+    // online softmax update; leaves this lane's weights exp2(s - m) in pr
+    auto update = [&](const float (&sc)[SPL], float (&pr)[SPL]) {
+        float smax = sc[0];
+#pragma unroll
+        for (int h = 1; h < SPL; ++h) smax = fmaxf(smax, sc[h]);
+        const float mn = fmaxf(m, wave_max(smax));
+        float alpha;
         if (mn == -INFINITY) {  // nothing valid yet (uniform)
             alpha = 1.f;
-            pr = 0.f;
+#pragma unroll
+            for (int h = 0; h < SPL; ++h) pr[h] = 0.f;
         } else {
             alpha = fast_exp2(m - mn);
-            pr = fast_exp2(s - mn);
+#pragma unroll
+            for (int h = 0; h < SPL; ++h) pr[h] = fast_exp2(sc[h] - mn);
         }
         m = mn;
-        lsum = lsum * alpha + pr;
+        float psum = pr[0];
+#pragma unroll
+        for (int h = 1; h < SPL; ++h) psum += pr[h];
+        lsum = lsum * alpha + psum;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-        return pr;
     };
     // acc += Σ_rows weight(row) · V(row) for this lane's 8 elements
-    auto pv = [&](const u32x4 (&vr)[NI], float pr) {
+    auto pv = [&](const u32x4 (&vr)[NI], const float (&pr)[SPL]) {
         static_for<0, NI>([&](auto I) {
             constexpr int i = decltype(I)::value;
-            const float pb = group_bcast<LPR, i>(pr);
+            const float pb = group_bcast<LPR, i % LPR>(pr[i / LPR]);
             // tie the row to its weight so its unpacking (explicit shifts for
             // bf16) is not hoisted ahead of the softmax, where all 16 rows'
             // unpacked values would be live at once
@@ -302,7 +323,9 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
             const bool more = nx < end_c;
             ChunkIds nxt;
             if (more) fetch_ids(nx, nxt);
-            const float pr = update(scores(kr, cs, cur));
+            float sc[SPL], pr[SPL];
+            scores(kr, cs, cur, sc);
+            update(sc, pr);
             if (!more) {
                 pv(vr, pr);
                 break;
