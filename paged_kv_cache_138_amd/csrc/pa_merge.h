@@ -1,5 +1,5 @@
-// Log-sum-exp merge of per-partition decode results, shared by the
-// standalone merge kernel and the in-kernel merge of the split path.
+// Log-sum-exp merge of per-partition decode results, shared by the merge
+// kernels (four elements of a row per thread, or one row per wavefront).
 //
 // Partition p of a query head carries m_p (largest scaled logit, natural-log
 // units), l_p = Σ exp(s - m_p) and o_p = Σ exp(s - m_p) v / l_p. With

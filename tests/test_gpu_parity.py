@@ -127,6 +127,32 @@ def test_split_partition_sizes(part):
     _assert_close(to_host_f64(out), ref, "f32", "partition %d" % part)
 
 
+@pytest.mark.parametrize("BS", [8, 16, 32, 64])
+@pytest.mark.parametrize("Hq", [3, 6, 8])
+@pytest.mark.parametrize("path", ["single", "split16", "split64", "split128", "split256",
+                                  "fused512"])
+def test_head_dim_64_chunks_across_partitions(BS, Hq, path):
+    """Multi-head attention at head_dim 64, whose chunk is 128 tokens (64 at
+    block size 8) with two scores per lane: partitions shorter than a chunk,
+    of one chunk and of several, head counts that give one, two or four heads
+    per workgroup, and lengths on both sides of the chunk edges."""
+    lens = [1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 640]
+    need = sum(-(-L // BS) for L in lens)
+    w = _small("d64", num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hq, head_dim=64,
+               dtype="f16" if Hq != 6 else "bf16", block_size=BS, num_blocks=need + 24,
+               max_blocks_per_seq=-(-640 // BS), lens="fixed:1")
+    b = W.make_batch(w, seed=BS + Hq, lens=lens, unallocated="nan")
+    P = None if path == "single" else max(int(path[5:]), BS)  # "split16", "fused512"
+    db = DeviceBatch(b, out_dtype=torch.float32, split=path != "single", partition_size=P,
+                     fused=path.startswith("fused"))
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, "f32", "D=64 BS=%d Hq=%d %s" % (BS, Hq, path))
+
+
 def test_edge_lengths_and_zero_context():
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 511, 512, 513]
     w = _small("edge", num_seqs=len(lens), num_heads=2, num_kv_heads=2, head_dim=128, dtype="f16",
