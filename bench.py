@@ -273,10 +273,6 @@ def main():
         del base
         torch.cuda.synchronize()
 
-        # the streaming-read ceiling is measured first: its saturating reads
-        # (about 8 ms) bring the device out of its idle state, and the
-        # warm-up steps that follow find the batch copies' translations again
-        ceiling = stream_ceiling(args.ceiling_gib) if args.ceiling_gib > 0 else None
         # all copies must agree bit for bit (same logical data, different placement)
         copies[0].step()
         torch.cuda.synchronize()
@@ -288,6 +284,13 @@ def main():
             assert torch.equal(c.out.view(torch.int16) if c.out.dtype != torch.float32 else c.out,
                                ref.view(torch.int16) if ref.dtype != torch.float32 else ref), \
                 "rotated copies disagree"
+        # the streaming-read ceiling is measured right before the warm-up
+        # steps: its saturating reads (about 8 ms) bring the device from the
+        # idle of the host-side checks above to its working clocks, which
+        # otherwise take the first 10 ms or so of steps to reach (those ran
+        # 1.5-2.5% slower); the warm-up steps then find the batch copies'
+        # address translations again
+        ceiling = stream_ceiling(args.ceiling_gib) if args.ceiling_gib > 0 else None
         # the warm-up steps, right before the timed loops
         for k in range(args.warmup):
             copies[k % R].step()
