@@ -186,9 +186,15 @@ int gqa_heads_log2(int num_kv_heads, int head_dim) {
 #ifndef PA_GQA_MAX_GROUP
 #define PA_GQA_MAX_GROUP 4
 #endif
+// rounds of resident workgroups the grid of groups must still hold
+#ifndef PA_GQA_GROUP_ROUNDS
+#define PA_GQA_GROUP_ROUNDS 2
+#endif
 int gqa_group(int parts, int64_t units, int resident) {
     for (int k = PA_GQA_MAX_GROUP; k > 1; k /= 2)
-        if (parts >= 2 * k && units * ceil_div(parts, k) >= (int64_t)2 * resident) return k;
+        if (parts >= 2 * k &&
+            units * ceil_div(parts, k) >= (int64_t)PA_GQA_GROUP_ROUNDS * resident)
+            return k;
     return 1;
 }
 
