@@ -437,6 +437,9 @@ PREFIX_CASES = [
     (16, 2, 64, "f16", 32, 64, 64, [1, 64, 65, 2, 130]),
     (8, 8, 128, "bf16", 32, 128, 256, [1, 300, 5, 128, 129]),
     (16, 1, 128, "f16", 16, 48, 96, [1, 40, 3]),
+    # head_dim 64 multi-head: the suffix partitions run in 128-token chunks
+    (6, 6, 64, "f16", 16, 128, 256, [1, 127, 128, 129, 300, 4, 255, 256, 257]),
+    (4, 4, 64, "bf16", 32, 256, 512, [1, 129, 384, 2, 600]),
 ]
 
 
