@@ -92,6 +92,47 @@ def test_split_rejects_bad_partition_and_workspace(lib):
     assert lib.pa_decode_split(*args, 64, p, 16, None) == 5
 
 
+def test_lse_merge_rejects_bad_arguments(lib):
+    p = 1 << 12
+    # out, out_dtype, part_out, part_max, part_sum, context_lens, B, Hq, D, max_partitions, P
+    ok = [p, 2, p, p, p, p, 2, 8, 128, 4, 512]
+    bad = [
+        (dict(i=8, v=112), 4),     # head_dim outside {64, 80, 96, 128, 256}
+        (dict(i=1, v=7), 3),       # not a pa_dtype
+        (dict(i=9, v=0), 2),       # no partitions
+        (dict(i=10, v=0), 2),      # partition size 0
+        (dict(i=7, v=0), 2),       # no heads
+        (dict(i=6, v=-1), 2),      # negative batch
+        (dict(i=3, v=None), 1),    # null part_max
+        (dict(i=0, v=p + 4), 7),   # out not 16-byte aligned
+        (dict(i=2, v=p + 8), 7),   # part_out not 16-byte aligned
+    ]
+    for kw, status in bad:
+        args = list(ok)
+        args[kw["i"]] = kw["v"]
+        assert lib.pa_lse_merge(*args, None) == status, kw
+        assert lib.pa_last_error() != b""
+    empty = list(ok)
+    empty[6] = 0
+    empty[0] = empty[2] = None
+    assert lib.pa_lse_merge(*empty, None) == 0
+
+
+def test_shared_prefix_decode_rejects_bad_prefix(lib):
+    p = 1 << 12
+    # out, out_dtype, query, K, V, tables, lens, B, Hq, Hkv, D, BS, MB, NB, scale, kv dtype
+    args = [p, 2, p, p, p, p, p, 2, 8, 8, 128, 16, 8, 64, 0.1, 0]
+    ws, nbytes = p, 1 << 20
+    for fn in (lib.pa_decode_split_shared_prefix, lib.pa_decode_partitions_shared_prefix):
+        assert fn(*args, 64, 96, ws, nbytes, None) == 2    # prefix not a multiple of P
+        assert fn(*args, 64, 192, ws, nbytes, None) == 2   # prefix past the tables (128 tokens)
+        assert fn(*args, 64, -64, ws, nbytes, None) == 2
+        g = list(args)
+        g[8], g[9] = 34, 1                                  # 34 query heads on one kv head
+        assert fn(*g, 64, 64, ws, nbytes, None) == 4
+        assert b"shared-prefix" in lib.pa_last_error()
+
+
 def test_noalloc_split_rejects_sizes_beyond_its_scratch_array(lib):
     # pa_decode_split_noalloc checks its workspace need against the scratch
     # array before it touches the device (dummy pointers are never read)
