@@ -337,15 +337,19 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // the row counts cover it.
     // Each select depends on one comparison (the compiler turns a
     // combination of comparisons into lane masks and several instructions).
-    auto issue = [&](int cs, const int32_t* tb, int tnb, int tend, Stage& kr,
-                     Stage& vr) -> uint32_t {
+    // With `full` true the caller knows the whole chunk lies below tend (so
+    // within the table): no clamping, and every load's range is whole.
+    const int full_bytes = RPW * (int)row32 - pad;
+    auto issue = [&](int cs, const int32_t* tb, int tnb, int tend, Stage& kr, Stage& vr,
+                     auto full) -> uint32_t {
+        constexpr bool FULL = decltype(full)::value;
         const uint32_t lb0 = (uint32_t)cs >> LOG_BS;
         const uint32_t last = tnb > 0 ? (uint32_t)tnb - 1 : 0;  // a table entry that exists
         uint32_t pid[NBC];
 #pragma unroll
         for (int b = 0; b < NBC; ++b) {
             const uint32_t lb = lb0 + b;
-            pid[b] = (uint32_t)tb[lb < last ? lb : last];
+            pid[b] = (uint32_t)tb[FULL || lb < last ? lb : last];
         }
         uint32_t okm = 0;
 #pragma unroll
@@ -354,7 +358,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         // (per-request prefill: every row's limit is below tend; not so in
         // decode mode, nor for the shared prefix, which ends where each
         // request's own positions begin)
-        if (dec || SH) okm &= rest >= CH ? 0xffffffffu : (rest > 0 ? (1u << rest) - 1u : 0u);
+        if (!FULL && (dec || SH))
+            okm &= rest >= CH ? 0xffffffffu : (rest > 0 ? (1u << rest) - 1u : 0u);
         const size_t coff = BS > CH ? (size_t)(((uint32_t)cs & (BS - 1)) * row32) : 0;
 #pragma unroll
         for (int j = 0; j < LPC; ++j) {
@@ -374,8 +379,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             // head slice (none: 0, whatever the base)
             // (readfirstlane: the compiler would keep it per lane, and a
             // per-lane range makes it loop over the lanes' values)
-            const int rr = min(rest - (j * RPL + wave * RPW), RPW);
-            const int bytes = max(rr * (int)row32 - pad, 0);
+            const int rr = FULL ? RPW : min(rest - (j * RPL + wave * RPW), RPW);
+            const int bytes = FULL ? full_bytes : max(rr * (int)row32 - pad, 0);
             const uint32_t nrec = __builtin_amdgcn_readfirstlane(p < nblk ? (uint32_t)bytes : 0u);
             const size_t boff = (size_t)p * block32 + coff;
             kr[j] = buffer_load16<PA_PREFILL_LOAD_AUX>(make_rsrc(kb_j[j] + boff, nrec), loff);
@@ -383,6 +388,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         }
         return okm;
     };
+    constexpr std::false_type kPart{};
+    constexpr std::true_type kWhole{};
     auto stash = [&](int buf, const Stage& kr, const Stage& vr) {
 #pragma unroll
         for (int j = 0; j < LPC; ++j) {
@@ -534,12 +541,12 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         const int nch = (max(end - start, 0) + CH - 1) / CH;
         if constexpr (DEPTH == 1) {
             Stage kr, vr;
-            uint32_t okm = issue(start, bt, nb, end, kr, vr);
+            uint32_t okm = issue(start, bt, nb, end, kr, vr, kPart);
             stash(0, kr, vr);
             __syncthreads();
             for (int c = 0; c < nch; ++c) {
                 const int cs = start + c * CH;
-                const uint32_t okm_next = issue(cs + CH, bt, nb, end, kr, vr);
+                const uint32_t okm_next = issue(cs + CH, bt, nb, end, kr, vr, kPart);
                 if (cs < wend) compute(cs, -1, okm, sm_k[c & 1], sm_v[c & 1]);
                 stash((c + 1) & 1, kr, vr);
                 __syncthreads();
@@ -554,14 +561,14 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             // the other buffer; its wait leaves chunk c + 2's loads in
             // flight.
             Stage k0, v0, k1, v1;
-            uint32_t okm0 = issue(start, bt, nb, end, k0, v0);
-            uint32_t okm1 = issue(start + CH, bt, nb, end, k1, v1);
+            uint32_t okm0 = issue(start, bt, nb, end, k0, v0, kPart);
+            uint32_t okm1 = issue(start + CH, bt, nb, end, k1, v1, kPart);
             stash(0, k0, v0);
             __syncthreads();
             for (int c = 0; c < nch; c += 2) {
                 {
                     const int cs = start + c * CH;
-                    const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0);
+                    const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0, kPart);
                     if (cs < wend) compute(cs, -1, okm0, sm_k[0], sm_v[0]);
                     stash(1, k1, v1);
                     __syncthreads();
@@ -570,7 +577,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                 if (c + 1 >= nch) break;
                 {
                     const int cs = start + (c + 1) * CH;
-                    const uint32_t okm3 = issue(cs + 2 * CH, bt, nb, end, k1, v1);
+                    const uint32_t okm3 = issue(cs + 2 * CH, bt, nb, end, k1, v1, kPart);
                     if (cs < wend) compute(cs, -1, okm1, sm_k[1], sm_v[1]);
                     stash(0, k0, v0);
                     __syncthreads();
@@ -618,11 +625,11 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         Cur c1 = next(c0);
         if constexpr (DEPTH == 1) {
             Stage kr, vr;
-            uint32_t okm = issue(c0.cs, c0.tb, c0.nb, c0.end, kr, vr);
+            uint32_t okm = issue(c0.cs, c0.tb, c0.nb, c0.end, kr, vr, kPart);
             stash(0, kr, vr);
             __syncthreads();
             for (int buf = 0; c0.r != kDone; buf ^= 1) {
-                const uint32_t okm_next = issue(c1.cs, c1.tb, c1.nb, c1.end, kr, vr);
+                const uint32_t okm_next = issue(c1.cs, c1.tb, c1.nb, c1.end, kr, vr, kPart);
                 if (wanted(c0)) compute(c0.cs, c0.r, okm, sm_k[buf], sm_v[buf]);
                 stash(buf ^ 1, kr, vr);
                 __syncthreads();
@@ -632,14 +639,37 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             }
         } else {
             Stage k0, v0, k1, v1;
-            uint32_t okm0 = issue(c0.cs, c0.tb, c0.nb, c0.end, k0, v0);
-            uint32_t okm1 = issue(c1.cs, c1.tb, c1.nb, c1.end, k1, v1);
+            uint32_t okm0 = issue(c0.cs, c0.tb, c0.nb, c0.end, k0, v0, kPart);
+            uint32_t okm1 = issue(c1.cs, c1.tb, c1.nb, c1.end, k1, v1, kPart);
             stash(0, k0, v0);
             __syncthreads();
+            // The shared prompt's chunks while the chunks two steps ahead are
+            // still inside it: the cursor is the position alone, and no test
+            // of the rows runs (a chunk that no row attends to would only be
+            // masked out whole).
+            if (c0.r < 0) {
+                const int nb0 = ps / BS;
+                int cs = c0.cs;
+                while (cs + 4 * CH <= ps) {  // chunks cs .. cs + 3 CH whole in the prompt
+                    const uint32_t okm2 = issue(cs + 2 * CH, a.block_tables, nb0, ps, k0, v0, kWhole);
+                    compute(cs, -1, okm0, sm_k[0], sm_v[0]);
+                    stash(1, k1, v1);
+                    __syncthreads();
+                    okm0 = okm2;
+                    const uint32_t okm3 = issue(cs + 3 * CH, a.block_tables, nb0, ps, k1, v1, kWhole);
+                    compute(cs + CH, -1, okm1, sm_k[1], sm_v[1]);
+                    stash(0, k0, v0);
+                    __syncthreads();
+                    okm1 = okm3;
+                    cs += 2 * CH;
+                }
+                c0.cs = cs;
+                c1 = next(c0);
+            }
             while (c0.r != kDone) {
                 const Cur c2 = next(c1);
                 {
-                    const uint32_t okm2 = issue(c2.cs, c2.tb, c2.nb, c2.end, k0, v0);
+                    const uint32_t okm2 = issue(c2.cs, c2.tb, c2.nb, c2.end, k0, v0, kPart);
                     if (wanted(c0)) compute(c0.cs, c0.r, okm0, sm_k[0], sm_v[0]);
                     stash(1, k1, v1);
                     __syncthreads();
@@ -648,7 +678,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                 if (c1.r == kDone) break;
                 const Cur c3 = next(c2);
                 {
-                    const uint32_t okm3 = issue(c3.cs, c3.tb, c3.nb, c3.end, k1, v1);
+                    const uint32_t okm3 = issue(c3.cs, c3.tb, c3.nb, c3.end, k1, v1, kPart);
                     if (wanted(c1)) compute(c1.cs, c1.r, okm1, sm_k[1], sm_v[1]);
                     stash(0, k0, v0);
                     __syncthreads();
