@@ -415,15 +415,20 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         const bool inside = all & (cs + CH - 1 <= first_pos) & (rseg < 0);
         // ---- scores Sᵀ: lane (g, n) gets row n, tokens 16s + 4g + k; each
         // K operand read from LDS serves every tile of the wave ------------
+        // (the sub-blocks' products interleaved: two independent accumulation
+        // chains, so each product's wait for the previous one overlaps)
         f32x4 sc[TR][NS];
+        const char* krow = kt + n * ROWB + 16 * g;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
 #pragma unroll
             for (int u = 0; u < TR; ++u) sc[u][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const char* krow = kt + (16 * s + n) * ROWB + 16 * g;
+        }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const u32x4 kv = *(const u32x4*)(krow + 64 * j);
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 kv = *(const u32x4*)(krow + 16 * s * ROWB + 64 * j);
 #pragma unroll
                 for (int u = 0; u < TR; ++u) sc[u][s] = Mma<KV>::mma(kv, qb[u][j], sc[u][s]);
             }
