@@ -570,7 +570,24 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             uint32_t okm1 = issue(start + CH, bt, nb, end, k1, v1, kPart);
             stash(0, k0, v0);
             __syncthreads();
-            for (int c = 0; c < nch; c += 2) {
+            int c = 0;
+            // while the chunks two steps ahead lie wholly below end, their
+            // loads are whole (no clamped table index, no per-load range)
+            const int nwhole = (end - start) / CH;
+            for (; c + 3 < nwhole; c += 2) {
+                const int cs = start + c * CH;
+                const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0, kWhole);
+                if (cs < wend) compute(cs, -1, okm0, sm_k[0], sm_v[0]);
+                stash(1, k1, v1);
+                __syncthreads();
+                okm0 = okm2;
+                const uint32_t okm3 = issue(cs + 3 * CH, bt, nb, end, k1, v1, kWhole);
+                if (cs + CH < wend) compute(cs + CH, -1, okm1, sm_k[1], sm_v[1]);
+                stash(0, k0, v0);
+                __syncthreads();
+                okm1 = okm3;
+            }
+            for (; c < nch; c += 2) {
                 {
                     const int cs = start + c * CH;
                     const uint32_t okm2 = issue(cs + 2 * CH, bt, nb, end, k0, v0, kPart);
