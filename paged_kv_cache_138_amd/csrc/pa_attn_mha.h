@@ -57,8 +57,8 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     constexpr int LPR = DP / 8;         // lanes per cache row
     constexpr int RPI = 64 / LPR;       // rows per load instruction
     constexpr int CHUNK = mha_chunk_tokens(D, BS);  // tokens per chunk
-    constexpr int NI = CHUNK / RPI;     // load instructions per chunk (16)
-    constexpr int SPL = NI / LPR;       // scores per lane (1, or 2 at head_dim 64)
+    constexpr int NI = CHUNK / RPI;     // load instructions per chunk (16; 8 at 64 / BS 8)
+    constexpr int SPL = NI / LPR;       // scores per lane (2 at head_dim 64 unless BS 8)
     constexpr int RPB = BS < 32 ? BS : 32;  // rows one load descriptor covers
     constexpr int IPB = RPB / RPI;      // load instructions per descriptor
     constexpr int BPC = CHUNK / RPB;    // descriptors per chunk
