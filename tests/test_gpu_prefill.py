@@ -103,6 +103,29 @@ def test_prefill_shared_prefix_matches_oracle(case, share):
     _assert_close(to_host_f64(out), ref, "f32", "case %d shared %d" % (case, ps))
 
 
+@pytest.mark.parametrize("cached", [96, 128, 144, 160, 192, 224])
+@pytest.mark.parametrize("heads", [(8, 8, "f16"), (28, 4, "bf16")])
+def test_prefill_prompt_lengths_around_the_whole_chunk_loops(cached, heads):
+    # Both entries stream the chunks whose successors two steps ahead lie
+    # wholly inside the prompt (shared entry) or below the end (plain entry)
+    # in a loop of their own, then hand over to the general loop: prompts of
+    # 3 to 7 chunks of 32 tokens enter and leave it at every offset.
+    Hq, Hkv, dt = heads
+    lens = [1, 17, 40, 3]
+    b = W.make_prefill_batch(_workload(Hq, Hkv, 128, dt, 16, cached, lens),
+                             seed=900 + cached + Hq, lens=lens)
+    _, _, ref = _oracle(b)
+    for ps in (cached, 0):
+        db = DevicePrefill(b, out_dtype=torch.float32, shared_prefix_tokens=ps)
+        out = db.step()
+        torch.cuda.synchronize()
+        _assert_close(to_host_f64(out), ref, "f32", "prompt %d shared %d" % (cached, ps))
+    db = DevicePrefill(b, out_dtype=torch.float32)  # pa_prefill
+    out = db.step()
+    torch.cuda.synchronize()
+    _assert_close(to_host_f64(out), ref, "f32", "prompt %d plain entry" % cached)
+
+
 def test_prefill_shared_prefix_many_requests_per_workgroup():
     # one or two new tokens per request, requests without new tokens among
     # them: a workgroup's rows span dozens of requests
