@@ -677,6 +677,38 @@ def test_head_dims_80_96_256(D, heads, path):
                       "D=%d heads=%s %s" % (D, HD_HEADS[heads], path))
 
 
+@pytest.mark.parametrize("D", [80, 96])
+@pytest.mark.parametrize("BS", [8, 16, 32, 64])
+@pytest.mark.parametrize("Hq", [1, 3, 4, 8])
+@pytest.mark.parametrize("path", ["single", "split64", "split256", "fused128"])
+def test_head_dims_80_96_one_head_kernel(D, BS, Hq, path):
+    """The one-head kernel at head_dim 80 and 96, whose rows take 10 or 12
+    of the 16 lanes of a 128-wide row (the other lanes read zeros and store
+    nothing): every block size, one, two or four heads per workgroup (the
+    host serves whole cache lines' worth of heads at these widths when it
+    can), partitions shorter and longer than a chunk, the fused new token,
+    both output types."""
+    lens = [1, 2, BS + 1, 63, 64, 65, 129, 300, 513]
+    need = sum(-(-L // BS) for L in lens)
+    dt = "bf16" if (BS + Hq) % 2 else "f16"
+    w = _small("hd%dmha" % D, num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hq, head_dim=D,
+               dtype=dt, block_size=BS, num_blocks=need + 16, max_blocks_per_seq=-(-513 // BS),
+               lens="fixed:1")
+    b = W.make_batch(w, seed=D + BS + Hq, lens=lens, unallocated="nan")
+    split = path != "single"
+    P = int(path[5:]) if path.startswith("split") else (128 if path == "fused128" else None)
+    kc, vc, ref = _oracle_step(b)
+    for od in (torch.float32, None):
+        db = DeviceBatch(b, out_dtype=od, split=split, partition_size=P,
+                         fused=path.startswith("fused"))
+        out = db.step()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+        assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+        _assert_close(to_host_f64(out), ref, "f32" if od is not None else dt,
+                      "D=%d BS=%d Hq=%d %s" % (D, BS, Hq, path))
+
+
 @pytest.mark.parametrize("D", [80, 96, 256])
 def test_head_dims_80_96_256_shared_prefix(D):
     P, prefix, suf = 64, 128, [1, 2, 16, 17, 100, 7]
