@@ -40,8 +40,8 @@ struct MergeArgs {
     // rows of sequences with at most this many partitions are left alone:
     // the split paths' partition launch wrote their output (one workgroup
     // covered the whole context); 0 writes every row (pa_lse_merge). Above
-    // 1, partitions were walked in groups of this size from partition 0,
-    // and only the groups' first rows are read.
+    // 1, partitions were walked in ceil(np / skip_parts) groups of nearly
+    // equal size, and only the groups' first rows are read.
     int skip_parts;
 };
 
@@ -174,8 +174,9 @@ int gqa_heads_log2(int num_kv_heads, int head_dim) {
     return std::max(hl, whole_line_heads_log2(num_kv_heads, head_dim, max_log2));
 }
 
-// Consecutive partitions one grouped-query workgroup walks (1, 2 or 4).
-// Each workgroup writes one fp32 row per query head to the workspace; such
+// Consecutive partitions one grouped-query workgroup walks, at most (1, 2 or
+// 4): a sequence's n partitions form ceil(n / k) groups of nearly equal
+// size. Each workgroup writes one fp32 row per query head to the workspace; such
 // stores, arriving while the device streams the cache at full bandwidth,
 // cost far more time than their share of the bytes (measured on MI355X with
 // 64 q / 8 kv heads, contexts of 1k-8k tokens: 452 / 431 / 416 us per launch

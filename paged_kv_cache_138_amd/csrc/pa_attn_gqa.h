@@ -205,14 +205,15 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     bid /= ngroups;
     // rows of every product: row r is query head r_head of sequence r_seq
     const int R = PREFIX ? 16 / G : 1;  // sequences per workgroup
-    int seq0, part, Lsrc, nparts = 0;
-    // consecutive partitions this workgroup walks (grouped decode mode)
+    int seq0, part, part_end, Lsrc, nparts = 0;
+    // groups of up to K consecutive partitions (grouped decode mode)
     const int K = PREFIX || a.parts_per_wg < 1 ? 1 : a.parts_per_wg;
     const int32_t* bt;
     if constexpr (PREFIX) {
         const int ntiles = (a.num_seqs + R - 1) / R;
         seq0 = (bid % ntiles) * R;
         part = bid / ntiles + a.part_begin;
+        part_end = part + 1;
         Lsrc = a.prefix_tokens;
         bt = a.block_tables;  // the shared prefix, as row 0 lists it
     } else {
@@ -223,10 +224,25 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         // GQA long-context batch: 457 -> 451 µs; the one-head kernel gained
         // nothing from it)
         const int pslots = (int)(gridDim.x / ((unsigned)ngroups * (unsigned)a.num_seqs));
-        part = (pslots - 1 - bid / a.num_seqs) * K + a.part_begin;
+        const int gi = pslots - 1 - bid / a.num_seqs;
         Lsrc = ctx_len(seq0);
         nparts = (Lsrc + P - 1) / P;
-        if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+        if (K == 1) {
+            part = gi + a.part_begin;
+            part_end = part + 1;
+            if (part > 0 && part >= nparts) return;  // uniform over the workgroup
+        } else {
+            // the sequence's partitions (one, if it has none) in
+            // ceil(n / K) groups of nearly equal size: group gi starts at
+            // partition floor(gi * n / groups). Groups of K with a short
+            // last one would leave single-partition workgroups, which
+            // unbalance the launch's end.
+            const int n = max(nparts, 1);
+            const int ng = (n + K - 1) / K;
+            if (gi >= ng) return;  // uniform over the workgroup
+            part = gi * n / ng;
+            part_end = (gi + 1) * n / ng;
+        }
         bt = a.block_tables + (size_t)seq0 * a.max_blocks_per_seq;
     }
     const int start = part * P;
@@ -241,7 +257,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
     // stored, by the workgroups of its partition 0, as the scatter would.)
     bool has_new = false, store_new = false;
     if constexpr (MODE == kModeDecode) {
-        if (a.new_key && part + K >= max(nparts, 1)) {  // the group holding position L - 1
+        if (a.new_key && part_end >= max(nparts, 1)) {  // the group holding position L - 1
             const int64_t slot = a.slot_mapping[seq0];
             const bool slot_ok = slot >= 0 && slot < (int64_t)a.num_blocks * BS;
             has_new = slot_ok && Lsrc > 0;
@@ -258,7 +274,7 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             }
         }
     }
-    const int end = has_new ? Lsrc - 1 : min(start + K * P, Lsrc);
+    const int end = has_new ? Lsrc - 1 : min(part_end * P, Lsrc);
     const int nb = (Lsrc + BS - 1) / BS;
     auto row_seq = [&](int r) { return seq0 + r / G; };
     auto row_head = [&](int r) { return kvh * G + r % G; };
@@ -534,14 +550,14 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         // (this group's state in its first partition's row, the group's
         // other partitions marked empty), so the rows describe the whole
         // context whoever merges them
-        if (part == 0 && np <= K) OUT::store(a.out, sh * D + d, res);
+        if (part == 0 && part_end >= np) OUT::store(a.out, sh * D + d, res);
         if (a.part_out) {
             const size_t pidx = sh * a.max_partitions + part;
             a.part_out[pidx * D + d] = res;
             if (d == 0) {
                 a.part_max[pidx] = M * kLn2;
                 a.part_sum[pidx] = tot;
-                for (int q = 1; q < K && part + q < np; ++q) {
+                for (int q = 1; part + q < part_end && part + q < np; ++q) {
                     a.part_max[pidx + q] = -INFINITY;
                     a.part_sum[pidx + q] = 0.f;
                 }

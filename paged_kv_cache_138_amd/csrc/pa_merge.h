@@ -14,24 +14,31 @@
 namespace pa {
 
 // Merge element d of one workspace row (one query head of one sequence)
-// over the partitions p = 0, step, 2*step, ... below np: the largest m_p,
-// then the weighted sums. Partitions walked in groups of `step` keep their
-// state in the group's first row, so the other rows are not read. A
-// partition whose m_p is -inf holds no token (its l_p is 0) and its o_p is
-// never used: it may be unwritten.
+// over its np partitions: the largest m_p, then the weighted sums.
+// Partitions walked in groups of up to `step` form nq = ceil(np / step)
+// groups of nearly equal size, group i starting at partition
+// floor(i * np / nq), which holds the group's state; the other rows are not
+// read (step 1: every partition is its own group). A partition whose m_p
+// is -inf holds no token (its l_p is 0) and its o_p is never used: it may
+// be unwritten.
 // KB partitions at a time: their loads are free of data-dependent branches
 // and all in flight together; a row of more partitions takes them in blocks
 // of KB, rescaling its running sums to each block's maximum.
+__device__ __forceinline__ int group_row(int i, int np, int nq, int step) {
+    return step == 1 ? i : i * np / nq;
+}
+
 template <int KB>
 __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, const float* po,
                                              int np, int D, int step) {
+    const int nq = (np + step - 1) / step;
     float M = -INFINITY, tot = 0.f, acc = 0.f;
-    for (int p0 = 0; p0 < np; p0 += KB * step) {
+    for (int i0 = 0; i0 < nq; i0 += KB) {
         float m[KB], l[KB], o[KB];
 #pragma unroll
         for (int q = 0; q < KB; ++q) {
-            const int p = p0 + q * step;
-            const bool in = p < np;
+            const bool in = i0 + q < nq;
+            const int p = in ? group_row(i0 + q, np, nq, step) : 0;
             m[q] = in ? pm[p] : -INFINITY;
             l[q] = in ? ps[p] : 0.f;
             o[q] = in ? po[(size_t)p * D] : 0.f;
@@ -60,15 +67,16 @@ __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, 
 template <int KB>
 __device__ __forceinline__ f32x4 merge_blocks4(const float* pm, const float* ps, const float* po,
                                               int np, int D, int step) {
+    const int nq = (np + step - 1) / step;
     float M = -INFINITY, tot = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < np; p0 += KB * step) {
+    for (int i0 = 0; i0 < nq; i0 += KB) {
         float m[KB], l[KB];
         f32x4 o[KB];
 #pragma unroll
         for (int q = 0; q < KB; ++q) {
-            const int p = p0 + q * step;
-            const bool in = p < np;
+            const bool in = i0 + q < nq;
+            const int p = in ? group_row(i0 + q, np, nq, step) : 0;
             m[q] = in ? pm[p] : -INFINITY;
             l[q] = in ? ps[p] : 0.f;
             o[q] = in ? *(const f32x4*)(po + (size_t)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};

@@ -386,6 +386,18 @@ def test_partitions_then_exported_merge_give_the_output(case, fused):
     empty = sum(1 for i, p in live if np.isneginf(pm[i, :, p]).all())
     assert (empty > 0) == grouped
     assert all(not np.isnan(pm[i, :, p]).any() for i, p in live)
+    if grouped:
+        # a sequence's n partitions form ceil(n / k) groups of nearly equal
+        # size (one k for the launch), group j starting at floor(j * n / groups)
+        starts = [[p for p in range(int(nparts[i])) if not np.isneginf(pm[i, :, p]).all()]
+                  for i in range(B)]
+
+        def balanced(n, k):
+            g = -(-n // k)
+            return [j * n // g for j in range(g)]
+
+        assert any(all(starts[i] == balanced(int(nparts[i]), k) for i in range(B))
+                   for k in (2, 4))
 
 
 def test_fused_qkv_strided_cache_write():
