@@ -369,8 +369,10 @@ pa_status pa_decode_partitions_append(void* out, pa_dtype out_dtype, const void*
  * Same arguments as pa_decode_split. One workgroup handles one partition of
  * one (sequence, head) - of two adjacent heads when the grid is large
  * compared with the device, and of one (sequence, kv head) when 2..16 query
- * heads share a kv head; a grouped-query workgroup may walk 2 or 4
- * consecutive partitions when the grid is large. Every partition
+ * heads share a kv head; when the grid is large a grouped-query workgroup
+ * may walk a group of consecutive partitions (a sequence's n partitions
+ * then form ceil(n / k) groups of nearly equal size, k = 2 or 4, group i
+ * starting at partition floor(i * n / groups)). Every partition
  * p < ceil(L_i / partition_size) of every row gets its workspace row:
  * part_max = the largest scaled logit (natural-log units), part_sum =
  * Σ exp(s - part_max), part_out = the normalised partial output, over the
