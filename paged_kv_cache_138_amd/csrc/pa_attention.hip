@@ -199,6 +199,17 @@ int gqa_group(int parts, int64_t units, int resident) {
     return 1;
 }
 
+// Sequence slots of a split-path grid, whose units run (sequence slot, head
+// or kv-head group, partition) with the group fastest. The dispatcher hands
+// workgroup i to XCD i mod 8, so a (sequence, partition) block of, say, 20
+// head groups starts on XCD (20 * block index) mod 8: with one slot per
+// sequence, the sequence's parity alone would pick the XCDs that take each
+// block's 4 extra units, and the even and odd sequences' lengths would load
+// the XCDs unevenly. With slots = 1 (mod 8) the block index mod 8 is
+// (partition + sequence) mod 8, so each sequence's partitions rotate over
+// the XCDs. The padding slots' workgroups return at once.
+int xcd_seq_slots(int num_seqs) { return num_seqs + (9 - num_seqs % 8) % 8; }
+
 // Workgroups of fn that fit on the current device at once (at least 1).
 int resident_workgroups(const void* fn, int threads) {
     static std::mutex mu;
@@ -528,8 +539,9 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
         st = check_launch(what);
         if (st != PA_OK) return st;
     }
+    a.seq_slots = xcd_seq_slots(s.num_seqs);
     const int64_t grid =
-        (int64_t)s.num_seqs * per_seq * ceil_div(lay.np - prefix_parts, group);
+        (int64_t)a.seq_slots * per_seq * ceil_div(lay.np - prefix_parts, group);
     PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
     if (grid == 0) return PA_OK;
     a.part_begin = prefix_parts;

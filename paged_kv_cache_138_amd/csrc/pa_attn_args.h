@@ -37,6 +37,9 @@ struct AttnArgs {
     int partition_size;
     int max_partitions;
     int part_begin;     // first partition index the grid covers
+    // split paths: sequence slots of the grid (>= num_seqs; 0 means
+    // num_seqs); the units of slots past num_seqs return at once
+    int seq_slots;
     // grouped-query decode: consecutive partitions one workgroup walks (1, 2
     // or 4; 0 counts as 1). Their combined state goes to the first one's
     // workspace row, and the others' rows are marked empty.

@@ -217,14 +217,16 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         Lsrc = a.prefix_tokens;
         bt = a.block_tables;  // the shared prefix, as row 0 lists it
     } else {
-        seq0 = bid % a.num_seqs;
+        const int slots = a.seq_slots > 0 ? a.seq_slots : a.num_seqs;
+        seq0 = bid % slots;
+        if (seq0 >= a.num_seqs) return;  // a padding slot (uniform over the workgroup)
         // partitions in descending order: the last workgroups dispatched
         // are partition 0's, one per sequence and mostly full, rather than
         // the few high partitions of the longest sequences (measured on the
         // GQA long-context batch: 457 -> 451 µs; the one-head kernel gained
         // nothing from it)
-        const int pslots = (int)(gridDim.x / ((unsigned)ngroups * (unsigned)a.num_seqs));
-        const int gi = pslots - 1 - bid / a.num_seqs;
+        const int pslots = (int)(gridDim.x / ((unsigned)ngroups * (unsigned)slots));
+        const int gi = pslots - 1 - bid / slots;
         Lsrc = ctx_len(seq0);
         nparts = (Lsrc + P - 1) / P;
         if (K == 1) {

@@ -95,11 +95,13 @@ __attribute__((amdgpu_waves_per_eu(PA_MHA_WAVES_PER_EU))) void attn_partition_ke
     const int Hq = a.num_heads;
     const int ngroups = Hq >> hl;
 
-    int bid = blockIdx.x;  // (sequence, head group, partition), head group fastest
+    int bid = blockIdx.x;  // (sequence slot, head group, partition), head group fastest
     const int head = (bid % ngroups) * (1 << hl) + hslot;
     bid /= ngroups;
-    const int seq = bid % a.num_seqs;
-    const int part = bid / a.num_seqs + a.part_begin;
+    const int slots = a.seq_slots > 0 ? a.seq_slots : a.num_seqs;
+    const int seq = bid % slots;
+    if (seq >= a.num_seqs) return;  // a padding slot (uniform over the workgroup)
+    const int part = bid / slots + a.part_begin;
     const int lane = threadIdx.x & 63;
     const int r = lane / LPR;  // row within a load instruction
     const int c = lane % LPR;  // 8-element slice of the row
