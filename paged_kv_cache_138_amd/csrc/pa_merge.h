@@ -24,21 +24,36 @@ namespace pa {
 // KB partitions at a time: their loads are free of data-dependent branches
 // and all in flight together; a row of more partitions takes them in blocks
 // of KB, rescaling its running sums to each block's maximum.
-__device__ __forceinline__ int group_row(int i, int np, int nq, int step) {
-    return step == 1 ? i : i * np / nq;
-}
+// First rows floor(i * np / nq) of the groups i = 0, 1, ...: with
+// np = q * nq + rem, each step adds q, and one more when the running
+// remainder i * rem mod nq wraps (no division per group).
+struct GroupRows {
+    int q, rem, nq, p = 0, acc = 0;
+    __device__ GroupRows(int np, int nq_) : q(np / nq_), rem(np - (np / nq_) * nq_), nq(nq_) {}
+    __device__ __forceinline__ int next() {
+        const int r = p;
+        p += q;
+        acc += rem;
+        if (acc >= nq) {
+            acc -= nq;
+            ++p;
+        }
+        return r;
+    }
+};
 
 template <int KB>
 __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, const float* po,
                                              int np, int D, int step) {
-    const int nq = (np + step - 1) / step;
+    const int nq = (np + step - 1) / step;  // np >= 1
+    GroupRows rows(np, nq);
     float M = -INFINITY, tot = 0.f, acc = 0.f;
     for (int i0 = 0; i0 < nq; i0 += KB) {
         float m[KB], l[KB], o[KB];
 #pragma unroll
         for (int q = 0; q < KB; ++q) {
             const bool in = i0 + q < nq;
-            const int p = in ? group_row(i0 + q, np, nq, step) : 0;
+            const int p = in ? rows.next() : 0;
             m[q] = in ? pm[p] : -INFINITY;
             l[q] = in ? ps[p] : 0.f;
             o[q] = in ? po[(size_t)p * D] : 0.f;
@@ -67,7 +82,8 @@ __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, 
 template <int KB>
 __device__ __forceinline__ f32x4 merge_blocks4(const float* pm, const float* ps, const float* po,
                                               int np, int D, int step) {
-    const int nq = (np + step - 1) / step;
+    const int nq = (np + step - 1) / step;  // np >= 1
+    GroupRows rows(np, nq);
     float M = -INFINITY, tot = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < nq; i0 += KB) {
@@ -76,7 +92,7 @@ __device__ __forceinline__ f32x4 merge_blocks4(const float* pm, const float* ps,
 #pragma unroll
         for (int q = 0; q < KB; ++q) {
             const bool in = i0 + q < nq;
-            const int p = in ? group_row(i0 + q, np, nq, step) : 0;
+            const int p = in ? rows.next() : 0;
             m[q] = in ? pm[p] : -INFINITY;
             l[q] = in ? ps[p] : 0.f;
             o[q] = in ? *(const f32x4*)(po + (size_t)p * D) : f32x4{0.f, 0.f, 0.f, 0.f};
