@@ -40,9 +40,11 @@ struct AttnArgs {
     // split paths: sequence slots of the grid (>= num_seqs; 0 means
     // num_seqs); the units of slots past num_seqs return at once
     int seq_slots;
-    // grouped-query decode: consecutive partitions one workgroup walks (1, 2
-    // or 4; 0 counts as 1). Their combined state goes to the first one's
-    // workspace row, and the others' rows are marked empty.
+    // grouped-query decode: the most consecutive partitions one workgroup
+    // walks (1, 2 or 4; 0 counts as 1). A sequence's n partitions form
+    // ceil(n / k) groups of nearly equal size; a group's combined state goes
+    // to its first partition's workspace row, and its other rows are marked
+    // empty.
     int parts_per_wg;
     int prefix_tokens;  // shared-prefix mode: tokens every sequence shares (block_tables row 0)
     int heads_log2;     // MHA kernel: log2 of the query heads one workgroup serves (0, 1, 2)

@@ -220,9 +220,9 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
         const int slots = a.seq_slots > 0 ? a.seq_slots : a.num_seqs;
         seq0 = bid % slots;
         if (seq0 >= a.num_seqs) return;  // a padding slot (uniform over the workgroup)
-        // partitions in descending order: the last workgroups dispatched
-        // are partition 0's, one per sequence and mostly full, rather than
-        // the few high partitions of the longest sequences (measured on the
+        // partition groups in descending order: the last workgroups
+        // dispatched are group 0's, one per sequence and mostly full, rather
+        // than the few high groups of the longest sequences (measured on the
         // GQA long-context batch: 457 -> 451 µs; the one-head kernel gained
         // nothing from it)
         const int pslots = (int)(gridDim.x / ((unsigned)ngroups * (unsigned)slots));

@@ -13,17 +13,6 @@
 
 namespace pa {
 
-// Merge element d of one workspace row (one query head of one sequence)
-// over its np partitions: the largest m_p, then the weighted sums.
-// Partitions walked in groups of up to `step` form nq = ceil(np / step)
-// groups of nearly equal size, group i starting at partition
-// floor(i * np / nq), which holds the group's state; the other rows are not
-// read (step 1: every partition is its own group). A partition whose m_p
-// is -inf holds no token (its l_p is 0) and its o_p is never used: it may
-// be unwritten.
-// KB partitions at a time: their loads are free of data-dependent branches
-// and all in flight together; a row of more partitions takes them in blocks
-// of KB, rescaling its running sums to each block's maximum.
 // First rows floor(i * np / nq) of the groups i = 0, 1, ...: with
 // np = q * nq + rem, each step adds q, and one more when the running
 // remainder i * rem mod nq wraps (no division per group).
@@ -42,6 +31,17 @@ struct GroupRows {
     }
 };
 
+// Merge element d of one workspace row (one query head of one sequence)
+// over its np partitions: the largest m_p, then the weighted sums.
+// Partitions walked in groups of up to `step` form nq = ceil(np / step)
+// groups of nearly equal size, group i starting at partition
+// floor(i * np / nq), which holds the group's state; the other rows are not
+// read (step 1: every partition is its own group). A partition whose m_p
+// is -inf holds no token (its l_p is 0) and its o_p is never used: it may
+// be unwritten.
+// KB groups at a time: their loads are free of data-dependent branches and
+// all in flight together; a row of more groups takes them in blocks of KB,
+// rescaling its running sums to each block's maximum.
 template <int KB>
 __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, const float* po,
                                              int np, int D, int step) {
