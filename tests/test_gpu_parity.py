@@ -590,6 +590,35 @@ def test_two_heads_per_workgroup_on_a_sparse_rectangle(fused):
     _assert_close(to_host_f64(out), ref, "f32", "sparse rectangle fused=%s" % fused)
 
 
+@pytest.mark.parametrize("B", [1, 7, 8, 9, 16, 17])
+@pytest.mark.parametrize("heads", [(40, 40), (16, 2), (64, 8)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_split_grid_sequence_slots(B, heads, fused):
+    """The split paths' grids have a number of sequence slots that is 1 mod 8
+    (so that a sequence's partitions rotate over the XCDs); the slots past
+    the batch return at once. Batches on both sides of multiples of 8, on
+    the one-head kernel (40 heads: 20 two-head groups per block) and the
+    grouped-query kernel, with enough partitions that the grouped-query
+    workgroups walk groups of them."""
+    Hq, Hkv = heads
+    lens = [int(x) for x in np.random.default_rng(B + Hq).integers(1, 1500, size=B)]
+    lens[0] = 1500
+    need = sum(-(-L // 16) for L in lens)
+    w = _small("slots", num_seqs=B, num_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+               dtype="bf16" if Hkv == 8 else "f16", block_size=16, num_blocks=need + 8,
+               max_blocks_per_seq=-(-1500 // 16), lens="fixed:1")
+    b = W.make_batch(w, seed=B * 7 + Hq, lens=lens, unallocated="nan")
+    # 16-token partitions: up to 94 per sequence, so that the larger
+    # batches' grouped-query grids hold enough units for groups of them
+    db = DeviceBatch(b, out_dtype=torch.float32, split=True, partition_size=16, fused=fused)
+    out = db.step()
+    torch.cuda.synchronize()
+    kc, vc, ref = _oracle_step(b)
+    assert np.array_equal(to_host_bits(db.key_cache), kc.view(np.uint16))
+    assert np.array_equal(to_host_bits(db.value_cache), vc.view(np.uint16))
+    _assert_close(to_host_f64(out), ref, "f32", "B=%d heads=%s fused=%s" % (B, heads, fused))
+
+
 # ---- block sizes 8 and 64 -----------------------------------------------------
 # An 8-token block puts eight blocks in a 64-token chunk of the one-head
 # kernel and four in a 32-token chunk of the grouped kernel; a 64-token block
