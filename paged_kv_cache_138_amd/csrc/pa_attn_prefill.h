@@ -93,6 +93,9 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #endif
 
 // fp16 caches: weights as one rounded fp16 value (1) or hi + lo halves (0)
+#ifndef PA_PREFILL_V_EARLY
+#define PA_PREFILL_V_EARLY 4
+#endif
 #ifndef PA_PREFILL_F16_SINGLE_P
 #define PA_PREFILL_F16_SINGLE_P 1
 #endif
@@ -433,6 +436,20 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                 for (int u = 0; u < TR; ++u) sc[u][s] = Mma<KV>::mma(kv, qb[u][j], sc[u][s]);
             }
         }
+        // the Vᵀ operands of the first d tiles, read ahead of the softmax:
+        // their LDS latency then overlaps its arithmetic
+        const int e4 = n >> 2, q4 = n & 3;
+        const char* r0 = vt + (4 * g + e4) * ROWB + q4 * 8;
+        const char* r1 = r0 + 16 * ROWB;
+        // (8-wave workgroups only: with 4, the staging registers leave no room)
+        constexpr int VE = NW < 8 ? 0 : (PA_PREFILL_V_EARLY < NT ? PA_PREFILL_V_EARLY : NT);
+        u32x4 ave[VE > 0 ? VE : 1];
+#pragma unroll
+        for (int t = 0; t < VE; ++t) {
+            const u32x2 lo = lds_read_tr16(r0 + 32 * t);
+            const u32x2 hi = lds_read_tr16(r1 + 32 * t);
+            ave[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
         u32x4 phi[TR], plo[TR];
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
@@ -515,14 +532,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         }
         // ---- Oᵀ += Vᵀ · Pᵀ: tokens 4g + e (e < 4) and 16 + 4g + e - 4; each
         // Vᵀ operand serves every tile ------------------------------------
-        const int e4 = n >> 2, q4 = n & 3;
-        const char* r0 = vt + (4 * g + e4) * ROWB + q4 * 8;
-        const char* r1 = r0 + 16 * ROWB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const u32x2 lo = lds_read_tr16(r0 + 32 * t);
-            const u32x2 hi = lds_read_tr16(r1 + 32 * t);
-            const u32x4 av = u32x4{lo.x, lo.y, hi.x, hi.y};
+            u32x4 av;
+            if (t < VE) {
+                av = ave[t < VE ? t : 0];
+            } else {
+                const u32x2 lo = lds_read_tr16(r0 + 32 * t);
+                const u32x2 hi = lds_read_tr16(r1 + 32 * t);
+                av = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
 #pragma unroll
             for (int u = 0; u < TR; ++u) {
                 oacc[u][t] = Mma<KV>::mma(av, phi[u], oacc[u][t]);
