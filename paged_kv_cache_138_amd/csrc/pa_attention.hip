@@ -207,8 +207,14 @@ int gqa_group(int parts, int64_t units, int resident) {
 // block's 4 extra units, and the even and odd sequences' lengths would load
 // the XCDs unevenly. With slots = 1 (mod 8) the block index mod 8 is
 // (partition + sequence) mod 8, so each sequence's partitions rotate over
-// the XCDs. The padding slots' workgroups return at once.
-int xcd_seq_slots(int num_seqs) { return num_seqs + (9 - num_seqs % 8) % 8; }
+// the XCDs. The padding slots' workgroups return at once. (Built with
+// PA_SPLIT_SEQ_SLOTS=0 the grids keep one slot per sequence, for comparison.)
+#ifndef PA_SPLIT_SEQ_SLOTS
+#define PA_SPLIT_SEQ_SLOTS 1
+#endif
+int xcd_seq_slots(int num_seqs) {
+    return PA_SPLIT_SEQ_SLOTS ? num_seqs + (9 - num_seqs % 8) % 8 : num_seqs;
+}
 
 // Workgroups of fn that fit on the current device at once (at least 1).
 int resident_workgroups(const void* fn, int threads) {

@@ -19,6 +19,14 @@ constexpr int mha_chunk_tokens(int head_dim, int block_size) {
     return head_dim <= 64 && block_size >= 16 ? PA_MHA_CHUNK_64 : 64;
 }
 
+// Grouped-query partition groups: a sequence's n partitions in ceil(n / k)
+// groups of nearly equal size (1), or groups of k from partition 0 with a
+// short last one (0, built for comparison). The partition kernel and the
+// merge read the same setting.
+#ifndef PA_GQA_EVEN_GROUPS
+#define PA_GQA_EVEN_GROUPS 1
+#endif
+
 struct AttnArgs {
     void* out;
     const uint16_t* query;

@@ -242,8 +242,8 @@ __attribute__((amdgpu_waves_per_eu(PA_GQA_WAVES_PER_EU))) void attn_gqa_kernel(A
             const int n = max(nparts, 1);
             const int ng = (n + K - 1) / K;
             if (gi >= ng) return;  // uniform over the workgroup
-            part = gi * n / ng;
-            part_end = (gi + 1) * n / ng;
+            part = PA_GQA_EVEN_GROUPS ? gi * n / ng : gi * K;
+            part_end = PA_GQA_EVEN_GROUPS ? (gi + 1) * n / ng : min(part + K, n);
         }
         bt = a.block_tables + (size_t)seq0 * a.max_blocks_per_seq;
     }

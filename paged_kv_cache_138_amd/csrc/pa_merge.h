@@ -9,6 +9,7 @@
 // rule is the textbook one for softmax over a union of disjoint sets).
 #pragma once
 
+#include "pa_attn_args.h"
 #include "pa_device.h"
 
 namespace pa {
@@ -19,6 +20,8 @@ namespace pa {
 struct GroupRows {
     int q, rem, nq, p = 0, acc = 0;
     __device__ GroupRows(int np, int nq_) : q(np / nq_), rem(np - (np / nq_) * nq_), nq(nq_) {}
+    // groups of `step` from partition 0 (PA_GQA_EVEN_GROUPS=0): q = step, no remainder
+    __device__ GroupRows(int step) : q(step), rem(0), nq(1) {}
     __device__ __forceinline__ int next() {
         const int r = p;
         p += q;
@@ -46,7 +49,7 @@ template <int KB>
 __device__ __forceinline__ float merge_blocks(const float* pm, const float* ps, const float* po,
                                              int np, int D, int step) {
     const int nq = (np + step - 1) / step;  // np >= 1
-    GroupRows rows(np, nq);
+    GroupRows rows = PA_GQA_EVEN_GROUPS ? GroupRows(np, nq) : GroupRows(step);
     float M = -INFINITY, tot = 0.f, acc = 0.f;
     for (int i0 = 0; i0 < nq; i0 += KB) {
         float m[KB], l[KB], o[KB];
@@ -83,7 +86,7 @@ template <int KB>
 __device__ __forceinline__ f32x4 merge_blocks4(const float* pm, const float* ps, const float* po,
                                               int np, int D, int step) {
     const int nq = (np + step - 1) / step;  // np >= 1
-    GroupRows rows(np, nq);
+    GroupRows rows = PA_GQA_EVEN_GROUPS ? GroupRows(np, nq) : GroupRows(step);
     float M = -INFINITY, tot = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < nq; i0 += KB) {
