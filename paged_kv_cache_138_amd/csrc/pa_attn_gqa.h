@@ -33,7 +33,10 @@
 // the 16-byte reads of K and the transpose reads of V over the banks. The
 // work decomposition (1 or 2 adjacent kv heads per workgroup), masking by
 // buffer ranges, partitions, the cross-wave merge and the fused append
-// follow the head-per-workgroup kernel.
+// follow the head-per-workgroup kernel. On the split path a workgroup may
+// also walk a group of consecutive partitions of its sequence (a sequence's
+// partitions form groups of nearly equal size), whose combined state is one
+// workspace row.
 #pragma once
 
 #include "pa_attn_args.h"

@@ -92,10 +92,12 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #define PA_PREFILL_MAX_DEPTH 2
 #endif
 
-// fp16 caches: weights as one rounded fp16 value (1) or hi + lo halves (0)
+// Vᵀ operand tiles (of 8) read from LDS ahead of the softmax, in 8-wave
+// workgroups (0: all after it)
 #ifndef PA_PREFILL_V_EARLY
 #define PA_PREFILL_V_EARLY 4
 #endif
+// fp16 caches: weights as one rounded fp16 value (1) or hi + lo halves (0)
 #ifndef PA_PREFILL_F16_SINGLE_P
 #define PA_PREFILL_F16_SINGLE_P 1
 #endif
