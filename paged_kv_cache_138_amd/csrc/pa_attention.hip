@@ -216,6 +216,22 @@ int xcd_seq_slots(int num_seqs) {
     return PA_SPLIT_SEQ_SLOTS ? num_seqs + (9 - num_seqs % 8) % 8 : num_seqs;
 }
 
+// Waves per workgroup of the prefill kernel's shared-prefix mode (16 rows
+// each; every wave reads every chunk from LDS, so more waves fetch each
+// prefix row for more rows)
+#ifndef PA_PREFILL_SHARED_WAVES
+#define PA_PREFILL_SHARED_WAVES 8
+#endif
+int prefill_shared_waves(int head_dim) { return head_dim == 128 ? PA_PREFILL_SHARED_WAVES : 4; }
+
+// The shared-prefix decode's prefix partitions: on the prefill kernel's
+// prefix-only decode mode (1), whose workgroups read each prefix chunk once
+// into LDS for 64 or 128 query rows, or on the grouped-query kernel's
+// prefix mode (0, built for comparison), one 16-row MFMA tile per read.
+#ifndef PA_PREFIX_ON_PREFILL
+#define PA_PREFIX_ON_PREFILL 1
+#endif
+
 // Workgroups of fn that fit on the current device at once (at least 1).
 int resident_workgroups(const void* fn, int threads) {
     static std::mutex mu;
@@ -510,9 +526,22 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
             group = gqa_group(lay.np, (int64_t)s.num_seqs * per_seq,
                               resident_workgroups((const void*)fn, threads));
     }
-    attn_fn pfn = prefix_tokens > 0 ? pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim,
-                                                         s.block_size)
-                                    : nullptr;
+    attn_fn pfn = nullptr;
+    int pthreads = 0, prows = 0;  // prefix launch: threads, sequences per workgroup
+    if (prefix_tokens > 0) {
+        const int G = s.num_heads / s.num_kv_heads;
+        if (PA_PREFIX_ON_PREFILL) {
+            const int waves = prefill_shared_waves(s.head_dim);
+            pfn = pick_prefill_shared_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size,
+                                             waves);
+            pthreads = waves * 64;
+            prows = waves * PA_PREFILL_SHARED_TR * (16 / G);
+        } else {
+            pfn = pick_prefix_kernel(kv_dtype, out_dtype, s.head_dim, s.block_size);
+            pthreads = kGqaWaves * 64;
+            prows = 16 / G;
+        }
+    }
     PA_REQUIRE(fn && (prefix_tokens == 0 || pfn), PA_ERR_UNSUPPORTED,
                "no kernel instance for this dtype/shape");
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,
@@ -534,14 +563,16 @@ pa_status launch_partitions(void* out, pa_dtype out_dtype, const void* query,
         a.new_value_stride = app->value_stride;
     }
     if (prefix_parts > 0) {
-        // shared prefix: 16 / G sequences x G heads per workgroup
-        const int rows = 16 / (s.num_heads / s.num_kv_heads);
-        const int64_t tiles = (s.num_seqs + rows - 1) / rows;
+        // shared prefix: prows sequences x G heads of one kv head per
+        // workgroup, one prefix partition each (the prefill kernel takes a
+        // null query_start for one query row per sequence)
+        const int64_t tiles = (s.num_seqs + prows - 1) / prows;
         const int64_t grid = (int64_t)s.num_kv_heads * tiles * prefix_parts;
         PA_REQUIRE(grid < ((int64_t)1 << 31), PA_ERR_SHAPE, "grid too large");
         a.part_begin = 0;
-        hipLaunchKernelGGL(pfn, dim3((unsigned)grid), dim3(kGqaWaves * 64), 0,
-                           (hipStream_t)stream, a);
+        a.query_start = nullptr;
+        hipLaunchKernelGGL(pfn, dim3((unsigned)grid), dim3(pthreads), 0, (hipStream_t)stream,
+                           a);
         st = check_launch(what);
         if (st != PA_OK) return st;
     }
@@ -886,9 +917,6 @@ extern "C" pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* query
     return check_launch("pa_prefill");
 }
 
-#ifndef PA_PREFILL_SHARED_WAVES
-#define PA_PREFILL_SHARED_WAVES 8
-#endif
 
 extern "C" pa_status pa_prefill_shared_prefix(
     void* out, pa_dtype out_dtype, const void* query, const void* key_cache,
@@ -917,7 +945,7 @@ extern "C" pa_status pa_prefill_shared_prefix(
                "prefill takes at most 16 query heads per kv head (got %d)", G);
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
     PA_REQUIRE(query_start, PA_ERR_NULL, "null query_start");
-    const int waves = head_dim == 128 ? PA_PREFILL_SHARED_WAVES : 4;
+    const int waves = prefill_shared_waves(head_dim);
     attn_fn fn = pick_prefill_shared_kernel(kv_dtype, out_dtype, head_dim, block_size, waves);
     PA_REQUIRE(fn, PA_ERR_UNSUPPORTED, "no kernel instance for this dtype/shape");
     AttnArgs a = make_args(out, query, key_cache, value_cache, block_tables, context_lens, s,

@@ -170,8 +170,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // workspace when a sequence has several; the grid's second coordinate
     // is then the partition instead of the tile of new tokens.
     const bool dec = !SH && a.query_start == nullptr;
+    // Prefix-only decode (shared-prefix mode without query_start): one new
+    // token per sequence, rows indexed by sequence; the workgroup streams
+    // one partition of the shared prefix for all its rows and writes each
+    // row's (max, sum, normalised output) of that partition to the split
+    // workspace. The grid's coordinates are the kv head, the tile of rows
+    // and the prefix partition.
+    const bool pfx = SH && a.query_start == nullptr;
     int kvh, seq = 0, part = 0, qb0 = 0, S = 0, L = 0, start = 0, end = 0, tw, wend = 0,
         first_pos;
+    int pstart = 0, pend = 0;  // shared-prefix mode: the prefix positions streamed
     int nparts = 1;
     bool rowv[TR];
     int lim[TR];  // last position row n of tile u attends to (-1: padding row)
@@ -227,24 +235,35 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         // that request's rows.
         const int32_t* qs = a.query_start;
         const int B = a.num_seqs;
-        const int T = qs[B];
+        const int T = pfx ? B : qs[B];
         kvh = blockIdx.x % Hkv;
-        const int t0 = (blockIdx.x / Hkv) * NW * TR * R;
+        int tile = blockIdx.x / Hkv;
+        const int rows_wg = NW * TR * R;  // new tokens (rows of one head) per workgroup
+        if (pfx) {
+            const int ntl = (T + rows_wg - 1) / rows_wg;
+            part = tile / ntl;
+            tile -= part * ntl;
+        }
+        const int t0 = tile * rows_wg;
         if (t0 >= T) return;  // uniform over the workgroup
         ps = min(a.prefix_tokens, Lmax);
-        r_lo = __builtin_amdgcn_readfirstlane(request_of(qs, 0, B - 1, t0));
-        r_hi = __builtin_amdgcn_readfirstlane(
-            request_of(qs, r_lo, B - 1, min(t0 + NW * TR * R, T) - 1));
+        pstart = pfx ? part * a.partition_size : 0;
+        pend = pfx ? min(pstart + a.partition_size, ps) : ps;
+        r_lo = pfx ? t0 : __builtin_amdgcn_readfirstlane(request_of(qs, 0, B - 1, t0));
+        r_hi = pfx ? min(t0 + rows_wg, T) - 1
+                   : __builtin_amdgcn_readfirstlane(
+                         request_of(qs, r_lo, B - 1, min(t0 + rows_wg, T) - 1));
         tw = t0 + wave * TR * R;
         int lo_pos = 0x7fffffff;
 #pragma unroll
         for (int u = 0; u < TR; ++u) {
             const int tok = tw + u * R + n / G;
             rowv[u] = n < R * G && tok < T;
-            const int r = request_of(qs, r_lo, r_hi, rowv[u] ? tok : t0);  // a short search
+            // (a short search)
+            const int r = pfx ? (rowv[u] ? tok : t0) : request_of(qs, r_lo, r_hi, rowv[u] ? tok : t0);
             int Lr = a.context_lens[r];
             Lr = Lr < 0 ? 0 : (Lr > Lmax ? Lmax : Lr);
-            const int pos = Lr - (qs[r + 1] - qs[r]) + (tok - qs[r]);
+            const int pos = pfx ? Lr - 1 : Lr - (qs[r + 1] - qs[r]) + (tok - qs[r]);
             lim[u] = rowv[u] ? pos : -1;
             rq[u] = r;
             orow[u] = ((size_t)(rowv[u] ? tok : 0) * Hq + kvh * G + n % G) * D;
@@ -280,8 +299,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // the first real score arrives
     float m[TR], lsum[TR];  // lsum: this lane's share of row n's Σ exp2(s - m)
     // how far a chunk's max may pass the reference before it moves (log2
-    // units); 0 in decode mode, whose partitions report their exact max
-    const float thr = dec ? 0.f : 8.f;
+    // units); 0 in the decode modes, whose partitions report their exact max
+    const float thr = dec || pfx ? 0.f : 8.f;
     f32x4 oacc[TR][NT];
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
@@ -642,6 +661,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
         const int32_t* qs = a.query_start;
         // the first stream of request r or a later one of the workgroup
         auto stream_from = [&](int r) -> Cur {
+            if (pfx) r = r_hi + 1;  // the prefix partition is the only stream
             for (; r <= r_hi; ++r) {
                 int Lr = a.context_lens[r];
                 Lr = Lr < 0 ? 0 : (Lr > Lmax ? Lmax : Lr);
@@ -664,7 +684,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                 any |= ((c.r < 0) | (rq[u] == c.r)) & (lim[u] >= c.cs);
             return __builtin_amdgcn_ballot_w64(any) != 0;
         };
-        Cur c0 = ps > 0 ? Cur{-1, 0, ps, ps / BS, a.block_tables} : stream_from(r_lo);
+        Cur c0 = pend > pstart ? Cur{-1, pstart, pend, ps / BS, a.block_tables}
+                               : stream_from(r_lo);
         Cur c1 = next(c0);
         if constexpr (DEPTH == 1) {
             Stage kr, vr;
@@ -693,13 +714,13 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             if (c0.r < 0) {
                 const int nb0 = ps / BS;
                 int cs = c0.cs;
-                while (cs + 4 * CH <= ps) {  // chunks cs .. cs + 3 CH whole in the prompt
-                    const uint32_t okm2 = issue(cs + 2 * CH, a.block_tables, nb0, ps, k0, v0, kWhole);
+                while (cs + 4 * CH <= pend) {  // chunks cs .. cs + 3 CH whole in the prompt
+                    const uint32_t okm2 = issue(cs + 2 * CH, a.block_tables, nb0, pend, k0, v0, kWhole);
                     compute(cs, -1, okm0, sm_k[0], sm_v[0]);
                     stash(1, k1, v1);
                     __syncthreads();
                     okm0 = okm2;
-                    const uint32_t okm3 = issue(cs + 3 * CH, a.block_tables, nb0, ps, k1, v1, kWhole);
+                    const uint32_t okm3 = issue(cs + 3 * CH, a.block_tables, nb0, pend, k1, v1, kWhole);
                     compute(cs + CH, -1, okm1, sm_k[1], sm_v[1]);
                     stash(0, k0, v0);
                     __syncthreads();
@@ -737,14 +758,17 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
     // mode on the split path (a workspace is given) the partition's row of
     // the workspace is written too, and a single partition, which is the
     // whole context, also gives the output itself --------------------------
-    const bool partial = dec && a.part_out != nullptr;
-    const bool whole = !dec || nparts <= 1;
+    // (prefix-only decode: the workspace row of the row's sequence and the
+    // prefix partition, never the output)
+    const bool partial = (dec || pfx) && a.part_out != nullptr;
+    const bool whole = !pfx && (!dec || nparts <= 1);
 #pragma unroll
     for (int u = 0; u < TR; ++u) {
         const float tot = sum_over_groups(lsum[u]);
         if (rowv[u]) {
             const float inv = tot > 0.f ? 1.f / tot : 0.f;
-            const size_t pidx = ((size_t)seq * Hq + head) * a.max_partitions + part;
+            const size_t pidx =
+                ((size_t)(pfx ? rq[u] : seq) * Hq + head) * a.max_partitions + part;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if (16 * t >= D) break;  // columns of the layout only
