@@ -396,11 +396,12 @@ pa_status pa_decode_partitions(void* out, pa_dtype out_dtype, const void* query,
  * same physical blocks - a prompt prefix cached once and referenced by all
  * tables ("vLLM 核心：PagedAttention 与 Continuous Batching" §3 Prefix
  * Caching; lqnn.cn/news/170268 §3.2-§3.4) - the partitions covering that
- * prefix are computed once per 16 query rows: one workgroup takes 16 / G
- * sequences x G query heads of a kv head (G = num_heads / num_kv_heads,
- * at most 16) and reads each prefix block once for all of them on the
- * matrix cores. The remaining partitions, the workspace and the merge are
- * those of pa_decode_split, and the result is the same up to rounding order.
+ * prefix are computed once per 64 or 128 query rows: one workgroup takes
+ * that many sequences x G query heads of a kv head (G = num_heads /
+ * num_kv_heads, at most 16; 128 rows at head_dim 128) and one prefix
+ * partition, and reads each prefix block once for all of them on the matrix
+ * cores. The remaining partitions, the workspace and the merge are those of
+ * pa_decode_split, and the result is the same up to rounding order.
  *
  *   shared_prefix_tokens  tokens every sequence shares; a multiple of
  *                     partition_size (hence of block_size); 0 gives plain

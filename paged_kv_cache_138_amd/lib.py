@@ -377,7 +377,7 @@ def decode_split_shared_prefix(query, key_cache, value_cache, block_tables, cont
                                out_dtype=None):
     """decode_split for a batch whose sequences all begin with the same
     shared_prefix_tokens tokens (the blocks of block_tables row 0); the prefix
-    partitions are computed once per 16 query rows."""
+    partitions are computed once per 64 or 128 query rows."""
     return _split_call("pa_decode_split_shared_prefix", query, key_cache, value_cache, block_tables,
                        context_lens, scale, partition_size, workspace, out, out_dtype,
                        prefix=shared_prefix_tokens)
