@@ -87,11 +87,11 @@ WORKLOADS = {
     "shared_prefix": Workload(
         "shared_prefix", 256, 32, 32, 128, "f16", 32, 16384, 1024,
         "uniform:1:1024", shared_prefix_tokens=2048, long_seqs=4,
-        long_len=32768,
+        long_len=32768, partition_size=1024,
         description="shared prefix: 256 seqs share a 2048-token prefix "
                     "(same physical blocks) then private suffixes U[1,1024]; "
                     "plus 4 seqs of 32768 tokens; 32 heads, head_dim 128, "
-                    "fp16, block 32"),
+                    "fp16, block 32, split-K 1024"),
 }
 
 WORKLOAD_ORDER = ["tiny", "llama13b", "llama7b", "gqa_long", "shared_prefix"]
