@@ -142,7 +142,7 @@ def default_path(workload):
     # measured on MI355X: the split path (partitions of the workload's
     # partition size, then the merge) beats the single launch on every
     # workload: long sequences no longer end the launch alone; a batch whose
-    # sequences share a prefix computes the prefix partitions once per 16 rows
+    # sequences share a prefix computes the prefix partitions once per 128 rows
     return "split_prefix" if workload.shared_prefix_tokens else "split"
 
 
