@@ -452,6 +452,11 @@ PREFIX_CASES = [
     # head_dim 64 multi-head: the suffix partitions run in 128-token chunks
     (6, 6, 64, "f16", 16, 128, 256, [1, 127, 128, 129, 300, 4, 255, 256, 257]),
     (4, 4, 64, "bf16", 32, 256, 512, [1, 129, 384, 2, 600]),
+    # more sequences than one workgroup's rows (the prefix partitions' row
+    # tiles): 32 sequences a tile at G = 4, 8 at G = 16, 64 at head_dim 64
+    (8, 2, 128, "f16", 16, 64, 128, [1 + (i * 37) % 150 for i in range(41)]),
+    (16, 1, 128, "bf16", 32, 64, 64, [1 + (i * 53) % 130 for i in range(19)]),
+    (4, 4, 64, "f16", 16, 64, 128, [1 + (i * 29) % 140 for i in range(70)]),
 ]
 
 
