@@ -97,6 +97,13 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 #ifndef PA_PREFILL_V_EARLY
 #define PA_PREFILL_V_EARLY 4
 #endif
+// Masked scores selected in their own registers (1: a select with a tied
+// operand, so that the unmasked path, taken by most chunks, needs no copy
+// of the scores where the paths join; measured on MI355X about 3% faster
+// for both prefill workloads) or by the compiler's selects (0)
+#ifndef PA_PREFILL_MASK_IN_PLACE
+#define PA_PREFILL_MASK_IN_PLACE 1
+#endif
 // fp16 caches: weights as one rounded fp16 value (1) or hi + lo halves (0)
 #ifndef PA_PREFILL_F16_SINGLE_P
 #define PA_PREFILL_F16_SINGLE_P 1
@@ -484,6 +491,22 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
             if (!inside) {
                 int d = dl[u] - cs;
                 if constexpr (SH) d = ((rseg < 0) | (rq[u] == rseg)) ? d : -1;
+#if PA_PREFILL_MASK_IN_PLACE
+                // v_cndmask writes the score's own register; the nop gives
+                // it the two wait states a lane mask just written by a
+                // vector compare needs before a vector instruction reads it
+                const float ninf = -INFINITY;
+                const uint32_t lm = all ? 0xffffffffu : okm >> (4 * g);
+#pragma unroll
+                for (int e = 0; e < 4 * NS; ++e) {
+                    const int t = (e / 4) * 16 + e % 4;
+                    const bool ok = (((lm >> t) & 1u) != 0u) & (t <= d);
+                    const uint64_t off = __builtin_amdgcn_ballot_w64(!ok);
+                    asm("s_nop 1\n\tv_cndmask_b32_e64 %0, %0, %1, %2"
+                        : "+v"(sv[e])
+                        : "v"(ninf), "s"(off));
+                }
+#else
                 if (all) {  // every block present: the row limit alone
 #pragma unroll
                     for (int e = 0; e < 4 * NS; ++e)
@@ -497,6 +520,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU))) void attn_prefill_
                         sv[e] = ok ? sv[e] : -INFINITY;
                     }
                 }
+#endif
             }
             // ---- online softmax of row n ---------------------------------
             // The reference m moves only when a score of the chunk passes it
